@@ -1,0 +1,317 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself:
+values printed on the source pages (tests/golden), closed forms, brute force on
+tiny inputs, library routines for the textbook special cases, and invariants.
+CPU only."""
+import json
+import math
+import os
+from itertools import combinations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name), encoding="utf-8") as f:
+        return json.load(f)
+
+
+def _case(seed, T=24, d=32, E=6, k=2, F=48, capacity=-1, bias_scale=0.0, x_scale=1.0):
+    return workloads.random_case(seed, T, d, E, k, F, "f32", capacity, bias_scale, x_scale, w_scale=0.2)
+
+
+# ----------------------------------------------------------------- page examples
+def test_renorm_printed_example():
+    g = _golden("renorm_example.json")
+    p = np.array([[0.3, 0.2, 0.15, 0.15, 0.1, 0.1]])
+    ids, w, _ = oracle.topk_route(p, 2)
+    assert ids.tolist() == [[0, 1]]
+    assert p[0, ids[0]].sum() == pytest.approx(g["sum_before"], abs=1e-15)
+    assert w[0].tolist() == pytest.approx(g["renormalised"], abs=1e-15)
+
+
+def test_worked_count_prefill_shape():
+    """Batch 4 x seq 2048 with k=2 routes 16384 pairs; with k=1, 8192."""
+    g = _golden("worked_count.json")
+    inp = workloads.generate("prefill", experts=[])
+    assert inp.X.shape[0] == g["batch"] * g["seq_len"] == g["tokens"]
+    X = oracle.as_f64(inp.X, "bf16")
+    Wg = oracle.as_f64(inp.Wg, "bf16")
+    for k, key in ((2, "pairs_k2"), (1, "pairs_k1")):
+        r = oracle.route(X, Wg, None, k)
+        disp = oracle.dispatch(r.ids, inp.Wg.shape[1])
+        assert int(disp.counts.sum()) == g[key]
+        assert len(disp.perm) == g[key]
+
+
+def test_activation_rate_two_of_64():
+    g = _golden("activation_rate.json")
+    case = _case(7, T=40, d=16, E=g["num_experts"], k=g["num_experts_per_tok"])
+    r = oracle.route(oracle.as_f64(case.X, "f32"), oracle.as_f64(case.Wg, "f32"), None, 2)
+    for t in range(r.ids.shape[0]):
+        assert len(set(r.ids[t].tolist())) == 2
+    frac = r.ids.shape[1] / g["num_experts"]
+    assert round(100 * frac, 1) == g["active_fraction_rounded_pct"]
+
+
+def test_capacity_formula_golden():
+    for c in _golden("capacity_formula.json")["cases"]:
+        assert oracle.expert_capacity_formula(c["T"], c["E"], c["k"]) == c["C"]
+    assert workloads.capacity_of(workloads.WORKLOADS["capacity"]) == 4096
+
+
+def test_capacity_hand_case():
+    g = _golden("capacity_hand_case.json")
+    ids = np.array(g["ids"])
+    d = oracle.dispatch(ids, g["E"], g["capacity"])
+    assert d.keep.tolist() == g["keep"]
+    assert d.counts.tolist() == g["counts"]
+    assert d.offsets.tolist() == g["offsets"]
+    assert d.perm.tolist() == g["perm"]
+    assert d.inv_perm.tolist() == g["inv_perm"]
+
+
+# ----------------------------------------------------------------- GELU
+def test_gelu_matches_torch_tanh_gelu():
+    x = np.linspace(-8, 8, 2001)
+    ref = torch.nn.functional.gelu(torch.tensor(x, dtype=torch.float64), approximate="tanh").numpy()
+    assert np.max(np.abs(oracle.gelu_tanh(x) - ref)) < 1e-14
+
+
+def test_gelu_closed_forms():
+    x = np.linspace(-5, 5, 101)
+    g = oracle.gelu_tanh
+    assert g(np.array([0.0]))[0] == 0.0
+    # 0.5x(1+tanh(u(x))) with u odd  =>  g(x) - g(-x) = x
+    assert np.max(np.abs(g(x) - g(-x) - x)) < 1e-14
+    assert abs(g(np.array([40.0]))[0] - 40.0) < 1e-12
+    assert abs(g(np.array([-40.0]))[0]) < 1e-12
+    # the tanh form stays within 1e-3 of the exact erf GELU
+    exact = 0.5 * x * (1 + np.vectorize(math.erf)(x / math.sqrt(2)))
+    assert np.max(np.abs(g(x) - exact)) < 1e-3
+
+
+# ----------------------------------------------------------------- router
+def test_router_logits_match_bias_free_linear():
+    case = _case(1, E=5, bias_scale=0.7)
+    X = oracle.as_f64(case.X, "f32")
+    Wg = oracle.as_f64(case.Wg, "f32")
+    lin = torch.nn.Linear(X.shape[1], Wg.shape[1], bias=True).double()
+    with torch.no_grad():
+        lin.weight.copy_(torch.tensor(Wg.T))
+        lin.bias.copy_(torch.tensor(case.bias, dtype=torch.float64))
+        ref = lin(torch.tensor(X)).numpy()
+    assert np.max(np.abs(oracle.router_logits(X, Wg, case.bias) - ref)) < 1e-12
+    p = oracle.softmax(ref)
+    ref_p = torch.softmax(torch.tensor(ref), dim=-1).numpy()
+    assert np.max(np.abs(p - ref_p)) < 1e-15
+
+
+@pytest.mark.parametrize("seed,E,k", [(0, 4, 1), (1, 6, 2), (2, 8, 3), (3, 5, 5), (4, 7, 4)])
+def test_topk_is_best_subset(seed, E, k):
+    case = _case(seed, T=20, d=12, E=E, k=k, bias_scale=0.3)
+    r = oracle.route(oracle.as_f64(case.X, "f32"), oracle.as_f64(case.Wg, "f32"), case.bias, k)
+    for t in range(r.ids.shape[0]):
+        best = max(combinations(range(E), k), key=lambda sub: sum(r.probs[t, j] for j in sub))
+        assert set(r.ids[t].tolist()) == set(best)
+        # slots in descending probability
+        assert np.all(np.diff(r.probs[t, r.ids[t]]) <= 0)
+
+
+def test_weights_closed_form_and_sum():
+    case = _case(5, T=50, E=8, k=3, bias_scale=1.0)
+    r = oracle.route(oracle.as_f64(case.X, "f32"), oracle.as_f64(case.Wg, "f32"), case.bias, 3)
+    assert np.max(np.abs(r.weights.sum(1) - 1.0)) < 1e-12
+    # the renormalised weights equal a softmax restricted to the selected logits
+    sel = np.take_along_axis(r.logits, r.ids, 1)
+    ref = np.exp(sel - sel.max(1, keepdims=True))
+    ref /= ref.sum(1, keepdims=True)
+    assert np.max(np.abs(r.weights - ref)) < 1e-14
+
+
+def test_router_shift_invariance_and_huge_bias():
+    case = _case(6, T=30, E=8, k=2)
+    X = oracle.as_f64(case.X, "f32")
+    Wg = oracle.as_f64(case.Wg, "f32")
+    r0 = oracle.route(X, Wg, None, 2)
+    r1 = oracle.route(X, Wg, np.full(8, 3.25), 2)
+    assert (r0.ids == r1.ids).all()
+    assert np.max(np.abs(r0.weights - r1.weights)) < 1e-14
+    b = np.zeros(8)
+    b[5] = 1e3
+    r2 = oracle.route(X, Wg, b, 2)
+    assert (r2.ids[:, 0] == 5).all()
+
+
+def test_router_relabelling_equivariance():
+    case = _case(8, T=30, E=7, k=3)
+    X = oracle.as_f64(case.X, "f32")
+    Wg = oracle.as_f64(case.Wg, "f32")
+    pi = np.array([3, 0, 6, 1, 5, 2, 4])
+    r = oracle.route(X, Wg, None, 3)
+    rp = oracle.route(X, Wg[:, pi], None, 3)
+    # new expert j is old expert pi[j]
+    assert (pi[rp.ids] == r.ids).all()
+
+
+def test_topk_ties_go_to_lower_id_and_margin():
+    p = np.array([[0.25, 0.25, 0.25, 0.25],
+                  [0.1, 0.4, 0.1, 0.4],
+                  [0.5, 0.3, 0.15, 0.05]])
+    ids, w, margin = oracle.topk_route(p, 2)
+    assert ids.tolist() == [[0, 1], [1, 3], [0, 1]]
+    assert margin[0] == 0.0 and margin[1] == 0.0
+    assert margin[2] == pytest.approx(0.15)
+    ids4, _, m4 = oracle.topk_route(p, 4)
+    assert ids4[2].tolist() == [0, 1, 2, 3]
+    assert m4[2] == pytest.approx(0.1)
+
+
+# ----------------------------------------------------------------- dispatch
+@pytest.mark.parametrize("seed,E,k,cap", [(0, 4, 1, -1), (1, 6, 2, -1), (2, 8, 3, 5), (3, 3, 2, 4), (4, 6, 2, 0)])
+def test_dispatch_invariants(seed, E, k, cap):
+    rng = np.random.default_rng(seed)
+    T = 37
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    d = oracle.dispatch(ids, E, cap)
+    assert int(d.counts.sum()) == T * k
+    kept = np.bincount(ids[d.keep], minlength=E)
+    if cap >= 0:
+        assert (kept == np.minimum(d.counts, cap)).all()
+    else:
+        assert d.keep.all()
+    assert (np.diff(d.offsets) == kept).all() and d.offsets[0] == 0
+    N = int(d.offsets[-1])
+    assert len(d.perm) == N == int(d.keep.sum())
+    # bijection between kept pairs and rows
+    assert (d.inv_perm[d.perm] == np.arange(N)).all()
+    assert ((d.inv_perm >= 0) == d.keep.reshape(-1)).all()
+    # rows strictly increasing in (expert, token)
+    t = d.perm // k
+    s = d.perm % k
+    e = ids[t, s]
+    key = e * T + t
+    assert (np.diff(key) > 0).all()
+    for j in range(E):
+        assert (e[d.offsets[j]:d.offsets[j + 1]] == j).all()
+
+
+def test_capacity_bruteforce_and_limits():
+    rng = np.random.default_rng(11)
+    T, E, k = 41, 5, 3
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    for cap in (0, 1, 7, 20, 200):
+        keep = oracle.capacity_keep(ids, E, cap)
+        # brute force: sort all pairs on (expert, slot, token), cut each expert at cap
+        pairs = sorted((int(ids[t, s]), s, t) for t in range(T) for s in range(k))
+        ref = np.zeros((T, k), dtype=bool)
+        n = {}
+        for e, s, t in pairs:
+            n[e] = n.get(e, 0) + 1
+            ref[t, s] = n[e] <= cap
+        assert (keep == ref).all()
+    full = oracle.dispatch(ids, E, -1)
+    big = oracle.dispatch(ids, E, int(full.counts.max()))
+    assert (full.perm == big.perm).all() and (full.inv_perm == big.inv_perm).all()
+
+
+# ----------------------------------------------------------------- expert FFN
+def test_single_expert_is_dense_ffn():
+    """E = 1, k = 1: the layer is the textbook FFN Linear-GELU-Linear."""
+    case = _case(9, T=16, d=20, E=1, k=1, F=36)
+    out, r, _ = oracle.moe_forward(case.X, case.Wg, None, case.W1, case.W2, 1)
+    assert (r.weights == 1.0).all()
+    ffn = torch.nn.Sequential(torch.nn.Linear(20, 36, bias=False), torch.nn.GELU(approximate="tanh"),
+                              torch.nn.Linear(36, 20, bias=False)).double()
+    with torch.no_grad():
+        ffn[0].weight.copy_(torch.tensor(case.W1[0], dtype=torch.float64))
+        ffn[2].weight.copy_(torch.tensor(case.W2[0], dtype=torch.float64))
+        ref = ffn(torch.tensor(case.X, dtype=torch.float64)).numpy()
+    assert np.max(np.abs(out - ref)) < 1e-12
+
+
+def test_linearity_in_w2():
+    case = _case(10, E=4, k=2)
+    o1, _, _ = oracle.moe_forward(case.X, case.Wg, None, case.W1, case.W2, 2)
+    o2, _, _ = oracle.moe_forward(case.X, case.Wg, None, case.W1, case.W2 * np.float32(4.0), 2)
+    assert np.max(np.abs(o2 - 4 * o1)) < 1e-12
+
+
+# ----------------------------------------------------------------- whole layer
+@pytest.mark.parametrize("seed,E,k,cap", [(0, 6, 2, -1), (1, 8, 3, -1), (2, 5, 1, -1),
+                                          (3, 6, 2, 5), (4, 4, 3, 9), (5, 6, 2, 0)])
+def test_sparse_equals_dense_bruteforce(seed, E, k, cap):
+    case = _case(seed, T=24, d=16, E=E, k=k, F=24, bias_scale=0.5)
+    out, r, disp = oracle.moe_forward(case.X, case.Wg, case.bias, case.W1, case.W2, k, cap)
+    ref, ids, w, keep = oracle.dense_bruteforce(case.X, case.Wg, case.bias, case.W1, case.W2, k, cap)
+    assert (r.ids == ids).all()
+    assert np.max(np.abs(r.weights - w)) < 1e-14
+    assert (disp.keep == keep).all()
+    assert np.max(np.abs(out - ref)) < 1e-12
+    if cap == 0:
+        assert (out == 0).all()
+
+
+def test_k_equals_E_is_soft_mixture():
+    """With every expert selected, the layer is the full softmax-weighted mixture."""
+    E = 5
+    case = _case(12, T=18, d=14, E=E, k=E, F=22, bias_scale=0.4)
+    out, r, _ = oracle.moe_forward(case.X, case.Wg, case.bias, case.W1, case.W2, E)
+    X = torch.tensor(case.X, dtype=torch.float64)
+    logits = X @ torch.tensor(case.Wg, dtype=torch.float64) + torch.tensor(case.bias, dtype=torch.float64)
+    p = torch.softmax(logits, -1)
+    ref = torch.zeros_like(X)
+    for e in range(E):
+        h = torch.nn.functional.gelu(X @ torch.tensor(case.W1[e], dtype=torch.float64).T, approximate="tanh")
+        ref += p[:, e:e + 1] * (h @ torch.tensor(case.W2[e], dtype=torch.float64).T)
+    assert np.max(np.abs(out - ref.numpy())) < 1e-12
+
+
+def test_token_permutation_equivariance():
+    case = _case(13, T=30, E=6, k=2)
+    out, _, _ = oracle.moe_forward(case.X, case.Wg, None, case.W1, case.W2, 2)
+    pi = np.random.default_rng(0).permutation(30)
+    outp, _, _ = oracle.moe_forward(case.X[pi], case.Wg, None, case.W1, case.W2, 2)
+    assert np.max(np.abs(outp - out[pi])) < 1e-13
+
+
+def test_token_subset_matches_full():
+    case = _case(14, T=40, E=6, k=2, capacity=9)
+    full, _, _ = oracle.moe_forward(case.X, case.Wg, None, case.W1, case.W2, 2, 9)
+    toks = [3, 17, 39, 0]
+    part, _, _ = oracle.moe_forward(case.X, case.Wg, None, case.W1, case.W2, 2, 9, tokens=toks)
+    assert np.max(np.abs(part - full[toks])) < 1e-13  # BLAS may block rows differently
+
+
+# ----------------------------------------------------------------- inputs
+def test_bf16_rounding_and_widening_match_torch():
+    rng = np.random.default_rng(3)
+    a = (rng.standard_normal(100000) * 3).astype(np.float32)
+    bits = workloads.f32_to_bf16_bits(a)
+    ref = torch.tensor(a).to(torch.bfloat16)
+    assert np.array_equal(bits, ref.view(torch.int16).numpy().view(np.uint16))
+    assert np.array_equal(oracle.as_f64(bits, "bf16"), ref.double().numpy())
+
+
+def test_workload_recipe():
+    w = workloads.WORKLOADS["skewed"]
+    inp = workloads.generate("tiny")
+    a = math.sqrt(6 / (128 + 8))
+    assert np.abs(inp.Wg).max() <= a
+    b = workloads._zipf_pmf_log_bias(w.E)
+    pmf = np.exp(b.astype(np.float64) / 1.5)
+    assert abs(pmf.sum() - 1) < 1e-5
+    assert np.all(np.diff(b) < 0)
+    # expert draws do not depend on which experts are drawn
+    full = workloads.generate("tiny")
+    part = workloads.generate("tiny", experts=[3])
+    assert np.array_equal(full.W1[3], part.W1[3]) and np.array_equal(full.W2[3], part.W2[3])
+    # a smaller T is a prefix of the same stream
+    pre = workloads.generate("tiny", T=10)
+    assert np.array_equal(pre.X, full.X[:10])
