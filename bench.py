@@ -1,0 +1,223 @@
+"""Benchmark of the sparse MoE FFN layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|decode|skewed|capacity|tiny]
+
+A step is one moe_forward (router, dispatch, expert GEMM1+GELU, GEMM2,
+combine) over one batch of seeded synthetic inputs that are resident in HBM
+before the timed region starts.  Prints one JSON line: tokens/s of the whole
+layer, the roofline fraction of the dominant kernel (HIP events over the
+timed region on the stream the kernels run on), per-stage times, and the CPU
+oracle timed on a bounded sample of the same workload (a baseline, not the
+target).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 MFMA/vector
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "MoE-layer tokens/sec at 1 GPU; % bf16 MFMA peak (FFN) / % HBM peak (rest)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill")
+    ap.add_argument("--cpu-sample", type=int, default=None, help="tokens (prefill-like) or steps (decode) for the oracle")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    return ap.parse_args()
+
+
+def to_dev(torch, a, dtype):
+    if a is None:
+        return None
+    if dtype == "bf16" and a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def stage_work(w, N, active, es):
+    """Algorithmic FLOPs and bytes per launch of each stage (N kept pairs, `active` experts with rows)."""
+    T, d, F, E, k = w.T, w.d, w.F, w.E, w.k
+    return {
+        "route": {"flops": 2.0 * T * d * E, "bytes": T * d * es + d * E * es + T * k * 8},
+        "dispatch": {"flops": 0.0, "bytes": T * d * es + N * d * es + T * k * 4 * 3},
+        "expert_up": {"flops": 2.0 * N * d * F, "bytes": active * F * d * es + N * d * es + N * F * es},
+        "expert_down": {"flops": 2.0 * N * F * d, "bytes": active * d * F * es + N * F * es + N * d * es},
+        "combine": {"flops": 0.0, "bytes": N * d * es + T * k * 8 + T * d * es},
+    }
+
+
+def cpu_baseline(w, inp, sample):
+    """The oracle, as it stands, on a bounded sample of the workload."""
+    import oracle
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    if w.steps > 1:
+        n = sample or 4
+        for s in range(n):
+            X = workloads.decode_step_inputs(w, s)
+            oracle.moe_forward(X, inp.Wg, inp.bias, inp.W1, inp.W2, w.k, inp.expert_capacity, w.dtype)
+        toks = n * w.T
+        desc = f"{n} decode steps of {w.T} tokens, full weights"
+    else:
+        n = sample or min(w.T, 1024)
+        cap = (-(-n // w.E) * w.k) if inp.expert_capacity >= 0 else -1
+        oracle.moe_forward(inp.X[:n], inp.Wg, inp.bias, inp.W1, inp.W2, w.k, cap, w.dtype)
+        toks = n
+        desc = f"first {n} of {w.T} tokens as one batch, full weights" + (f", capacity {cap}" if cap >= 0 else "")
+    dt = time.perf_counter() - t0
+    return {"value": toks / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": desc, "seconds": round(dt, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus N>1 is not supported",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import sparse_mixture_experts_04_amd as moe
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    t_gen = time.perf_counter()
+    inp = workloads.generate(w)
+    gen_s = time.perf_counter() - t_gen
+    dt = w.dtype
+    es = 2 if dt == "bf16" else 4
+    cfg = moe.config(w.T, w.d, w.F, w.E, w.k, inp.expert_capacity, dt)
+    Wg, W1, W2 = to_dev(torch, inp.Wg, dt), to_dev(torch, inp.W1, dt), to_dev(torch, inp.W2, dt)
+    bias = to_dev(torch, inp.bias, "f32")
+    if w.steps > 1:
+        xs = [to_dev(torch, workloads.decode_step_inputs(w, s), dt) for s in range(w.steps)]
+    else:
+        xs = [to_dev(torch, inp.X, dt)]
+    layer = moe.MoELayer(cfg, Wg, W1, W2, bias)
+    b = layer.buf
+    stream = torch.cuda.current_stream()
+
+    for i in range(args.warmup):
+        layer.forward(xs[i % len(xs)])
+    torch.cuda.synchronize()
+
+    # ---- headline: K whole-layer steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        layer.forward(xs[i % len(xs)])
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+
+    # ---- per-stage: the same K steps through the stage entry points, events between stages
+    Xp, H, Yp = b.workspace_view(cfg, "Xp"), b.workspace_view(cfg, "H"), b.workspace_view(cfg, "Yp")
+    names = ["route", "dispatch", "expert_up", "expert_down", "combine"]
+    stage_ms = {n: 0.0 for n in names}
+    dws = b.ws  # dispatch scratch sits at the front of the forward workspace
+    dbytes = moe.moe_workspace_size(cfg, moe.MOE_OP_DISPATCH)
+    per_step_active, per_step_N = [], []
+    for i in range(args.steps):
+        X = xs[i % len(xs)]
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+        evs[0].record(stream)
+        moe.moe_route(cfg, X, Wg, bias, b.topk_ids, b.topk_w)
+        evs[1].record(stream)
+        moe.moe_dispatch(cfg, b.topk_ids, X, b.expert_counts, b.expert_offsets, b.perm, b.inv_perm, Xp, dws, dbytes)
+        evs[2].record(stream)
+        moe.moe_expert_up(cfg, Xp, b.expert_offsets, W1, H)
+        evs[3].record(stream)
+        moe.moe_expert_down(cfg, H, b.expert_offsets, W2, Yp)
+        evs[4].record(stream)
+        moe.moe_combine(cfg, Yp, b.inv_perm, b.topk_w, b.out)
+        evs[5].record(stream)
+        torch.cuda.synchronize()
+        for j, n in enumerate(names):
+            stage_ms[n] += evs[j].elapsed_time(evs[j + 1]) / args.steps
+        off = b.expert_offsets.cpu().numpy()
+        per_step_N.append(int(off[-1]))
+        per_step_active.append(int((np.diff(off) > 0).sum()))
+
+    N = float(np.mean(per_step_N))
+    active = float(np.mean(per_step_active))
+    work = stage_work(w, N, active, es)
+    stages = {}
+    for n in names:
+        ms = stage_ms[n]
+        f, by = work[n]["flops"], work[n]["bytes"]
+        stages[n] = {"ms": round(ms, 5), "tflops": round(f / ms / 1e9, 2) if f else 0.0,
+                     "gbs": round(by / ms / 1e6, 1),
+                     "frac_hbm": round(by / ms / 1e6 / PEAK_HBM_GBS, 4)}
+        if n.startswith("expert"):
+            peak = PEAK_BF16_TFLOPS if dt == "bf16" else PEAK_F32_TFLOPS
+            stages[n]["frac_mfma"] = round(f / ms / 1e9 / peak, 4)
+    dom = max(["expert_up", "expert_down"], key=lambda n: stage_ms[n])
+    ms = stage_ms[dom]
+    if w.steps > 1 or N / max(active, 1) < 64:
+        roof = {"bound": "hbm", "achieved": round(work[dom]["bytes"] / ms / 1e6, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    else:
+        peak = PEAK_BF16_TFLOPS if dt == "bf16" else PEAK_F32_TFLOPS
+        roof = {"bound": "mfma", "achieved": round(work[dom]["flops"] / ms / 1e9, 2), "peak": peak,
+                "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = ("grouped_gemm_kernel (GEMM1+GELU)" if dom == "expert_up" else "grouped_gemm_kernel (GEMM2)")
+    roof["ms"] = round(ms, 5)
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(w, inp, args.cpu_sample)
+
+    tok_per_step = w.T
+    line = {
+        "metric": METRIC,
+        "value": round(tok_per_step / (ms_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic (seeded; random-init weights of the stated shapes)",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "k": w.k, "F": w.F,
+                   "expert_capacity": inp.expert_capacity, "bias": w.bias, "seed": w.seed,
+                   "parallelism": "single GPU, all experts resident"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "stages": stages,
+        "kept_pairs": N,
+        "active_experts": active,
+        "wall_s_timed_region": round(wall, 4),
+        "input_gen_s": round(gen_s, 2),
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

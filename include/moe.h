@@ -1,0 +1,160 @@
+/*
+ * moe.h -- C ABI of the sparse Mixture-of-Experts FFN layer forward pass on
+ * one MI355X (gfx950) holding all experts.
+ *
+ * The layer, as the source pages state it:
+ *   router   : logits = X W_g (+ b); softmax over the E experts; top-k; the k
+ *              weights renormalised to sum to 1
+ *              ["Qwen2-MoE代码解析：MoE架构原理、工程实现与部署避坑指南"
+ *               (jsqmd.com/news/1061813) §3.1; Qwen2-MoE walk-through
+ *               (mlqm.cn/news/48291) §3.2, steps 1-2]
+ *   dispatch : (token, slot) pairs grouped by expert; with an expert
+ *              capacity C, pairs beyond C per expert are dropped
+ *              [jsqmd §3.1 detail 3, §3.4; mlqm §2.2 (C = ceil(T/E)*k);
+ *               "GPT-4 activates 2%" article (wmrh.cn/news/106769) §2.2]
+ *   experts  : per expert Linear -> GELU -> Linear [mlqm §2.2; wmrh §2.2]
+ *   combine  : weighted sum of each token's k expert outputs
+ *              [jsqmd §3.1 detail 2]
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers unless stated.  The caller owns every
+ *     buffer; the library never allocates or frees device memory.
+ *   - Row-major layouts.  X, out: [T, d].  W_g: [d, E].  Expert weights use
+ *     the nn.Linear [out, in] layout: W1: [E, F, d], W2: [E, d, F].
+ *     Intermediates Xp, Yp: [T*k, d] (rows past N unused), H: [T*k, F].
+ *   - Element type of X, W_g, W1, W2, Xp, H, Yp and out is cfg->dtype
+ *     (MOE_F32 = float, MOE_BF16 = bfloat16 bit patterns).  gate_bias and
+ *     topk_w are float; ids, counts, offsets, perm and inv_perm are int32.
+ *   - Accumulation is fp32; GELU is the tanh form
+ *     0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))).
+ *   - Every call only enqueues work on `stream` (a hipStream_t; NULL = the
+ *     null stream) and never synchronises or reads results back.  Buffers must
+ *     stay valid until the stream has run the work.
+ *   - Arguments are checked on the host before anything is enqueued; a bad
+ *     argument returns an error and enqueues nothing.  A HIP launch failure
+ *     returns MOE_ERR_HIP (work enqueued before it may have run).
+ *   - Calls that share a workspace or outputs on different streams race.
+ *
+ * Limits: 1 <= E <= 64; 1 <= k <= E; d and F positive multiples of 64;
+ * T >= 0 (T = 0 is a no-op); T*k*max(d, F) < 2^62 elements.
+ * expert_capacity < 0 selects dropless routing; C >= 0 keeps at most C pairs
+ * per expert (C = 0 drops every pair and out is all zeros).
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,        /* null pointer, T < 0, k outside [1, E], bad dtype ... */
+  MOE_ERR_UNSUPPORTED = 2,        /* E > 64, d or F not a multiple of 64 */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+  MOE_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
+} moe_status;
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* The layer's shape.  num_experts / num_experts_per_tok / expert_capacity are
+ * the configuration fields named in jsqmd §2.2 and mlqm §2.2.  Host pointer. */
+typedef struct moe_config {
+  int32_t num_tokens;          /* T = batch * seq, tokens flattened           */
+  int32_t hidden_size;         /* d                                           */
+  int32_t intermediate_size;   /* F, expert FFN inner size                    */
+  int32_t num_experts;         /* E                                           */
+  int32_t num_experts_per_tok; /* k                                           */
+  int32_t expert_capacity;     /* C; < 0: dropless                            */
+  int32_t dtype;               /* moe_dtype of X, weights, out, intermediates */
+} moe_config;
+
+/* Which entry point a workspace is sized for. */
+typedef enum moe_op {
+  MOE_OP_DISPATCH = 0,   /* moe_dispatch                                  */
+  MOE_OP_EXPERT_FFN = 1, /* moe_expert_ffn (holds H)                      */
+  MOE_OP_FORWARD = 2     /* moe_forward (dispatch scratch + Xp + H + Yp)  */
+} moe_op;
+
+/* Human-readable name of a status.  Static string; never NULL. */
+const char* moe_status_string(moe_status status);
+
+/* Library build description (static string). */
+const char* moe_version(void);
+
+/* Bytes of device workspace `op` needs for `cfg` (host only, no HIP call).
+ * *bytes receives the size; 0 is possible.  Errors: INVALID_ARG, UNSUPPORTED. */
+moe_status moe_workspace_size(const moe_config* cfg, int32_t op, size_t* bytes);
+
+/* Router: gate projection, softmax over E, top-k, renormalisation
+ * [jsqmd §3.1; mlqm §3.2 steps 1-2].
+ *   X [T, d], Wg [d, E] (dtype), gate_bias [E] float or NULL (a per-expert
+ *   logit bias, the domain bias of mlqm §6).
+ *   topk_ids [T, k] int32 out: slot 0 holds the most probable expert; slots in
+ *   descending probability; equal logits go to the lower expert id.
+ *   topk_w [T, k] float out: p_s / sum_j p_j over the k selected experts. */
+moe_status moe_route(const moe_config* cfg, const void* X, const void* Wg,
+                     const float* gate_bias, int32_t* topk_ids, float* topk_w,
+                     void* stream);
+
+/* Dispatcher: group the (token, slot) pairs by expert
+ * [jsqmd §3.1 detail 3; wmrh §2.2; capacity: jsqmd §3.4, mlqm §2.2].
+ *   topk_ids [T, k] int32 in; X [T, d] in.
+ *   expert_counts [E] out: pairs routed to each expert (before any drop).
+ *   expert_offsets [E+1] out: exclusive scan of the kept counts; expert e's
+ *     rows are [offsets[e], offsets[e+1]); offsets[E] = N, the kept pairs.
+ *   perm [T*k] out: row r < N holds the pair id t*k+s; rows >= N hold -1.
+ *     Rows are ordered by (expert, token, slot) -- stable by token.
+ *   inv_perm [T*k] out: the row of pair t*k+s, or -1 if the pair was dropped.
+ *   Xp [T*k, d] out: row r = X[perm[r] / k] for r < N; rows >= N untouched.
+ *   Capacity (C >= 0): each expert keeps its pairs in (slot, token) order up
+ *   to C; the rest are dropped.  Ids outside [0, E) are treated as dropped
+ *   and not counted.
+ *   ws / ws_bytes: workspace of moe_workspace_size(cfg, MOE_OP_DISPATCH). */
+moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_ids, const void* X,
+                        int32_t* expert_counts, int32_t* expert_offsets, int32_t* perm,
+                        int32_t* inv_perm, void* Xp, void* ws, size_t ws_bytes, void* stream);
+
+/* Expert up-projection: H[r] = gelu(W1[e] Xp[r]) for every row r of expert
+ * e's segment [offsets[e], offsets[e+1]) (the first Linear and the GELU of
+ * mlqm §2.2).  Xp [T*k, d], W1 [E, F, d] in; H [T*k, F] out (rows >= N
+ * untouched). expert_offsets [E+1] is read on the device. */
+moe_status moe_expert_up(const moe_config* cfg, const void* Xp, const int32_t* expert_offsets,
+                         const void* W1, void* H, void* stream);
+
+/* Expert down-projection: Yp[r] = W2[e] H[r] (the second Linear).
+ * H [T*k, F], W2 [E, d, F] in; Yp [T*k, d] out (rows >= N untouched). */
+moe_status moe_expert_down(const moe_config* cfg, const void* H, const int32_t* expert_offsets,
+                           const void* W2, void* Yp, void* stream);
+
+/* Both expert projections: Yp[r] = W2[e] gelu(W1[e] Xp[r]); H lives in ws
+ * (moe_workspace_size(cfg, MOE_OP_EXPERT_FFN)). */
+moe_status moe_expert_ffn(const moe_config* cfg, const void* Xp, const int32_t* expert_offsets,
+                          const void* W1, const void* W2, void* Yp, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* Combine: out[t] = sum over kept slots s of topk_w[t, s] * Yp[inv_perm[t*k+s]]
+ * [jsqmd §3.1 detail 2], accumulated in fp32, stored in dtype; a token with
+ * no kept slot gets zeros.  Yp [T*k, d], inv_perm [T*k], topk_w [T, k] in;
+ * out [T, d] out. */
+moe_status moe_combine(const moe_config* cfg, const void* Yp, const int32_t* inv_perm,
+                       const float* topk_w, void* out, void* stream);
+
+/* The whole layer [mlqm §3.2 steps 1-5]: route, dispatch, expert FFN,
+ * combine.  The routing and dispatch results are written to the caller's
+ * buffers (same meaning as above) so that every stage can be checked; Xp, H
+ * and Yp live in ws (moe_workspace_size(cfg, MOE_OP_FORWARD)). */
+moe_status moe_forward(const moe_config* cfg, const void* X, const void* Wg,
+                       const float* gate_bias, const void* W1, const void* W2, void* out,
+                       int32_t* topk_ids, float* topk_w, int32_t* expert_counts,
+                       int32_t* expert_offsets, int32_t* perm, int32_t* inv_perm,
+                       void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -1,0 +1,14 @@
+"""Sparse Mixture-of-Experts FFN layer forward on MI355X (gfx950).
+
+The layer -- router, dispatcher, expert Linear-GELU-Linear, weighted combine --
+runs in the HIP kernels of libmoe.so behind the C ABI of include/moe.h.  This
+package is its thin Python binding (ctypes; torch supplies device memory and
+streams) plus buffer plumbing.  Importing it fails loudly when libmoe.so is
+missing: there is no CPU or PyTorch fallback.
+"""
+from ._lib import (MOE_BF16, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED,  # noqa: F401
+                   MOE_ERR_WORKSPACE_TOO_SMALL, MOE_F32, MOE_OK, MOE_OP_DISPATCH, MOE_OP_EXPERT_FFN,
+                   MOE_OP_FORWARD, EXPORTED, LIB, LIB_PATH, MoeConfig, MoeError, config, moe_combine,
+                   moe_dispatch, moe_expert_down, moe_expert_ffn, moe_expert_up, moe_forward, moe_route,
+                   moe_workspace_size, status_string, version)
+from .layer import ForwardBuffers, MoELayer  # noqa: F401

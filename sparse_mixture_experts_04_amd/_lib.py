@@ -1,0 +1,181 @@
+"""ctypes binding of libmoe.so (the C ABI declared in include/moe.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  Tensors are passed as raw device pointers; the stream is torch's
+current HIP stream unless one is given.  There is no fallback: if libmoe.so is
+missing or cannot be loaded, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch  # loads torch's HIP runtime first, so libmoe binds to that same copy
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = 1
+MOE_ERR_UNSUPPORTED = 2
+MOE_ERR_WORKSPACE_TOO_SMALL = 3
+MOE_ERR_HIP = 4
+
+MOE_F32 = 0
+MOE_BF16 = 1
+
+MOE_OP_DISPATCH = 0
+MOE_OP_EXPERT_FFN = 1
+MOE_OP_FORWARD = 2
+
+# Every symbol include/moe.h declares.
+EXPORTED = ("moe_status_string", "moe_version", "moe_workspace_size", "moe_route", "moe_dispatch",
+            "moe_expert_up", "moe_expert_down", "moe_expert_ffn", "moe_combine", "moe_forward")
+
+
+class MoeConfig(ctypes.Structure):
+    _fields_ = [("num_tokens", ctypes.c_int32), ("hidden_size", ctypes.c_int32),
+                ("intermediate_size", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+                ("num_experts_per_tok", ctypes.c_int32), ("expert_capacity", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+    def __repr__(self):
+        return ("MoeConfig(T=%d, d=%d, F=%d, E=%d, k=%d, C=%d, dtype=%s)" %
+                (self.num_tokens, self.hidden_size, self.intermediate_size, self.num_experts,
+                 self.num_experts_per_tok, self.expert_capacity, "bf16" if self.dtype == MOE_BF16 else "f32"))
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)}")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sparse_mixture_experts_04_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    CFG = ctypes.POINTER(MoeConfig)
+    sig = {
+        "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "moe_version": (ctypes.c_char_p, []),
+        "moe_workspace_size": (ctypes.c_int, [CFG, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]),
+        "moe_route": (ctypes.c_int, [CFG, P, P, P, P, P, P]),
+        "moe_dispatch": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "moe_expert_up": (ctypes.c_int, [CFG, P, P, P, P, P]),
+        "moe_expert_down": (ctypes.c_int, [CFG, P, P, P, P, P]),
+        "moe_expert_ffn": (ctypes.c_int, [CFG, P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "moe_combine": (ctypes.c_int, [CFG, P, P, P, P, P]),
+        "moe_forward": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    hip_copies = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    hip_copies.add(line.split()[-1])
+    except OSError:
+        pass
+    if len(hip_copies) > 1:
+        raise ImportError(f"two HIP runtimes are loaded ({sorted(hip_copies)}); libmoe must share torch's")
+    return lib
+
+
+LIB = _load()
+
+
+def status_string(status: int) -> str:
+    return LIB.moe_status_string(int(status)).decode()
+
+
+def version() -> str:
+    return LIB.moe_version().decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != MOE_OK:
+        raise MoeError(fn, status)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        try:
+            return torch.cuda.current_stream().cuda_stream
+        except (RuntimeError, AssertionError):  # no GPU: only argument checks can run
+            return 0
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def config(T: int, d: int, F: int, E: int, k: int, capacity: int = -1, dtype: str = "bf16") -> MoeConfig:
+    """The layer's shape: num_tokens, hidden, intermediate, num_experts,
+    num_experts_per_tok, expert_capacity (< 0: dropless), dtype ("bf16"|"f32")."""
+    return MoeConfig(int(T), int(d), int(F), int(E), int(k), int(capacity),
+                     MOE_BF16 if dtype == "bf16" else MOE_F32)
+
+
+def moe_workspace_size(cfg: MoeConfig, op: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_workspace_size", LIB.moe_workspace_size(ctypes.byref(cfg), int(op), ctypes.byref(n)))
+    return n.value
+
+
+def moe_route(cfg, X, Wg, gate_bias, topk_ids, topk_w, stream=None) -> None:
+    _check("moe_route", LIB.moe_route(ctypes.byref(cfg), _ptr(X), _ptr(Wg), _ptr(gate_bias), _ptr(topk_ids),
+                                      _ptr(topk_w), _stream(stream)))
+
+
+def moe_dispatch(cfg, topk_ids, X, expert_counts, expert_offsets, perm, inv_perm, Xp, ws, ws_bytes=None,
+                 stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check("moe_dispatch", LIB.moe_dispatch(ctypes.byref(cfg), _ptr(topk_ids), _ptr(X), _ptr(expert_counts),
+                                            _ptr(expert_offsets), _ptr(perm), _ptr(inv_perm), _ptr(Xp), _ptr(ws),
+                                            int(ws_bytes), _stream(stream)))
+
+
+def moe_expert_up(cfg, Xp, expert_offsets, W1, H, stream=None) -> None:
+    _check("moe_expert_up", LIB.moe_expert_up(ctypes.byref(cfg), _ptr(Xp), _ptr(expert_offsets), _ptr(W1), _ptr(H),
+                                              _stream(stream)))
+
+
+def moe_expert_down(cfg, H, expert_offsets, W2, Yp, stream=None) -> None:
+    _check("moe_expert_down", LIB.moe_expert_down(ctypes.byref(cfg), _ptr(H), _ptr(expert_offsets), _ptr(W2),
+                                                  _ptr(Yp), _stream(stream)))
+
+
+def moe_expert_ffn(cfg, Xp, expert_offsets, W1, W2, Yp, ws, ws_bytes=None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check("moe_expert_ffn", LIB.moe_expert_ffn(ctypes.byref(cfg), _ptr(Xp), _ptr(expert_offsets), _ptr(W1),
+                                                _ptr(W2), _ptr(Yp), _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def moe_combine(cfg, Yp, inv_perm, topk_w, out, stream=None) -> None:
+    _check("moe_combine", LIB.moe_combine(ctypes.byref(cfg), _ptr(Yp), _ptr(inv_perm), _ptr(topk_w), _ptr(out),
+                                          _stream(stream)))
+
+
+def moe_forward(cfg, X, Wg, gate_bias, W1, W2, out, topk_ids, topk_w, expert_counts, expert_offsets, perm,
+                inv_perm, ws, ws_bytes=None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check("moe_forward", LIB.moe_forward(ctypes.byref(cfg), _ptr(X), _ptr(Wg), _ptr(gate_bias), _ptr(W1), _ptr(W2),
+                                          _ptr(out), _ptr(topk_ids), _ptr(topk_w), _ptr(expert_counts),
+                                          _ptr(expert_offsets), _ptr(perm), _ptr(inv_perm), _ptr(ws), int(ws_bytes),
+                                          _stream(stream)))

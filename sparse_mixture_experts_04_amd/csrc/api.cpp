@@ -1,0 +1,192 @@
+// C ABI of the MoE layer (declared in include/moe.h): argument checks,
+// workspace carving and the launch sequence.  Every check runs on the host
+// before anything is enqueued.
+#include "../../include/moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <limits>
+
+#include "kernels.hpp"
+
+namespace moe {
+
+int device_cu_count() {
+  static std::atomic<int> cache[256];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+}  // namespace moe
+
+namespace {
+
+size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+size_t esize(const moe_config* c) { return c->dtype == MOE_BF16 ? 2 : 4; }
+
+moe_status check_cfg(const moe_config* c) {
+  if (c == nullptr) return MOE_ERR_INVALID_ARG;
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (c->num_tokens < 0 || c->hidden_size <= 0 || c->intermediate_size <= 0) return MOE_ERR_INVALID_ARG;
+  if (c->num_experts < 1 || c->num_experts_per_tok < 1 || c->num_experts_per_tok > c->num_experts)
+    return MOE_ERR_INVALID_ARG;
+  if (c->num_experts > moe::kMaxExpertsAbi) return MOE_ERR_UNSUPPORTED;
+  if (c->hidden_size % 64 != 0 || c->intermediate_size % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  const int64_t pairs = static_cast<int64_t>(c->num_tokens) * c->num_experts_per_tok;
+  if (pairs > std::numeric_limits<int32_t>::max()) return MOE_ERR_UNSUPPORTED;
+  const int64_t widest = c->hidden_size > c->intermediate_size ? c->hidden_size : c->intermediate_size;
+  if (pairs > 0 && widest > (int64_t{1} << 62) / pairs) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+bool capacity_mode(const moe_config* c) { return c->expert_capacity >= 0; }
+
+size_t pairs_of(const moe_config* c) {
+  return static_cast<size_t>(c->num_tokens) * static_cast<size_t>(c->num_experts_per_tok);
+}
+
+size_t dispatch_bytes(const moe_config* c) {
+  return moe::dispatch_scratch_bytes(c->num_tokens, c->num_experts, c->num_experts_per_tok, capacity_mode(c));
+}
+size_t h_bytes(const moe_config* c) { return align256(pairs_of(c) * c->intermediate_size * esize(c)); }
+size_t xp_bytes(const moe_config* c) { return align256(pairs_of(c) * c->hidden_size * esize(c)); }
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape outside the supported limits";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL: workspace smaller than moe_workspace_size";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP runtime call or kernel launch failed";
+  }
+  return "unknown moe_status";
+}
+
+const char* moe_version(void) { return "moe-gfx950 1 (router, dispatch, grouped MFMA GEMM, combine)"; }
+
+moe_status moe_workspace_size(const moe_config* cfg, int32_t op, size_t* bytes) {
+  if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
+  if (moe_status s = check_cfg(cfg); s != MOE_OK) return s;
+  switch (op) {
+    case MOE_OP_DISPATCH: *bytes = dispatch_bytes(cfg); return MOE_OK;
+    case MOE_OP_EXPERT_FFN: *bytes = h_bytes(cfg); return MOE_OK;
+    case MOE_OP_FORWARD: *bytes = align256(dispatch_bytes(cfg)) + 2 * xp_bytes(cfg) + h_bytes(cfg); return MOE_OK;
+    default: return MOE_ERR_INVALID_ARG;
+  }
+}
+
+moe_status moe_route(const moe_config* cfg, const void* X, const void* Wg, const float* gate_bias,
+                     int32_t* topk_ids, float* topk_w, void* stream) {
+  if (moe_status s = check_cfg(cfg); s != MOE_OK) return s;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if (!X || !Wg || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_router(cfg->dtype, X, Wg, gate_bias, cfg->num_tokens, cfg->hidden_size,
+                                       cfg->num_experts, cfg->num_experts_per_tok, topk_ids, topk_w,
+                                       as_stream(stream)));
+}
+
+moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_ids, const void* X, int32_t* expert_counts,
+                        int32_t* expert_offsets, int32_t* perm, int32_t* inv_perm, void* Xp, void* ws,
+                        size_t ws_bytes, void* stream) {
+  if (moe_status s = check_cfg(cfg); s != MOE_OK) return s;
+  if (!expert_counts || !expert_offsets) return MOE_ERR_INVALID_ARG;
+  if (cfg->num_tokens > 0 && (!topk_ids || !X || !perm || !inv_perm || !Xp)) return MOE_ERR_INVALID_ARG;
+  const size_t need = dispatch_bytes(cfg);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (need > 0 && ws == nullptr) return MOE_ERR_INVALID_ARG;
+  const moe::DispatchScratch sc = moe::carve_dispatch_scratch(ws, cfg->num_tokens, cfg->num_experts,
+                                                              cfg->num_experts_per_tok, capacity_mode(cfg));
+  return hip_status(moe::launch_dispatch(cfg->dtype, topk_ids, X, cfg->num_tokens, cfg->hidden_size, cfg->num_experts,
+                                         cfg->num_experts_per_tok, cfg->expert_capacity, expert_counts,
+                                         expert_offsets, perm, inv_perm, Xp, sc, as_stream(stream)));
+}
+
+moe_status moe_expert_up(const moe_config* cfg, const void* Xp, const int32_t* expert_offsets, const void* W1,
+                         void* H, void* stream) {
+  if (moe_status s = check_cfg(cfg); s != MOE_OK) return s;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if (!Xp || !expert_offsets || !W1 || !H) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_grouped_gemm(cfg->dtype, true, Xp, W1, H, expert_offsets, cfg->num_experts,
+                                             cfg->intermediate_size, cfg->hidden_size,
+                                             static_cast<int>(pairs_of(cfg)), as_stream(stream)));
+}
+
+moe_status moe_expert_down(const moe_config* cfg, const void* H, const int32_t* expert_offsets, const void* W2,
+                           void* Yp, void* stream) {
+  if (moe_status s = check_cfg(cfg); s != MOE_OK) return s;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if (!H || !expert_offsets || !W2 || !Yp) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_grouped_gemm(cfg->dtype, false, H, W2, Yp, expert_offsets, cfg->num_experts,
+                                             cfg->hidden_size, cfg->intermediate_size,
+                                             static_cast<int>(pairs_of(cfg)), as_stream(stream)));
+}
+
+moe_status moe_expert_ffn(const moe_config* cfg, const void* Xp, const int32_t* expert_offsets, const void* W1,
+                          const void* W2, void* Yp, void* ws, size_t ws_bytes, void* stream) {
+  if (moe_status s = check_cfg(cfg); s != MOE_OK) return s;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if (!Xp || !expert_offsets || !W1 || !W2 || !Yp) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < h_bytes(cfg)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (ws == nullptr) return MOE_ERR_INVALID_ARG;
+  if (moe_status s = moe_expert_up(cfg, Xp, expert_offsets, W1, ws, stream); s != MOE_OK) return s;
+  return moe_expert_down(cfg, ws, expert_offsets, W2, Yp, stream);
+}
+
+moe_status moe_combine(const moe_config* cfg, const void* Yp, const int32_t* inv_perm, const float* topk_w,
+                       void* out, void* stream) {
+  if (moe_status s = check_cfg(cfg); s != MOE_OK) return s;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if (!Yp || !inv_perm || !topk_w || !out) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_combine(cfg->dtype, Yp, inv_perm, topk_w, out, cfg->num_tokens, cfg->hidden_size,
+                                        cfg->num_experts_per_tok, as_stream(stream)));
+}
+
+moe_status moe_forward(const moe_config* cfg, const void* X, const void* Wg, const float* gate_bias, const void* W1,
+                       const void* W2, void* out, int32_t* topk_ids, float* topk_w, int32_t* expert_counts,
+                       int32_t* expert_offsets, int32_t* perm, int32_t* inv_perm, void* ws, size_t ws_bytes,
+                       void* stream) {
+  if (moe_status s = check_cfg(cfg); s != MOE_OK) return s;
+  if (!expert_counts || !expert_offsets) return MOE_ERR_INVALID_ARG;
+  if (cfg->num_tokens > 0 &&
+      (!X || !Wg || !W1 || !W2 || !out || !topk_ids || !topk_w || !perm || !inv_perm))
+    return MOE_ERR_INVALID_ARG;
+  size_t need = 0;
+  moe_workspace_size(cfg, MOE_OP_FORWARD, &need);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (ws == nullptr) return MOE_ERR_INVALID_ARG;
+  unsigned char* p = static_cast<unsigned char*>(ws);
+  void* dws = p;
+  p += align256(dispatch_bytes(cfg));
+  void* Xp = p;
+  p += xp_bytes(cfg);
+  void* H = p;
+  p += h_bytes(cfg);
+  void* Yp = p;
+  if (moe_status s = moe_route(cfg, X, Wg, gate_bias, topk_ids, topk_w, stream); s != MOE_OK) return s;
+  if (moe_status s = moe_dispatch(cfg, topk_ids, X, expert_counts, expert_offsets, perm, inv_perm, Xp, dws,
+                                  dispatch_bytes(cfg), stream);
+      s != MOE_OK)
+    return s;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if (moe_status s = moe_expert_up(cfg, Xp, expert_offsets, W1, H, stream); s != MOE_OK) return s;
+  if (moe_status s = moe_expert_down(cfg, H, expert_offsets, W2, Yp, stream); s != MOE_OK) return s;
+  return moe_combine(cfg, Yp, inv_perm, topk_w, out, stream);
+}
+
+}  // extern "C"

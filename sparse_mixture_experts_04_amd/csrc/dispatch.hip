@@ -1,0 +1,341 @@
+// Dispatcher kernels: per-chunk expert histogram, exclusive scan, stable
+// scatter of the (token, slot) pairs into expert-contiguous rows, and the
+// capacity cut.
+//
+// Method: the pairs are regrouped by expert id ("Qwen2-MoE代码解析"
+// (jsqmd.com/news/1061813) §3.1 detail 3 sorts them; the "GPT-4 activates 2%"
+// article (wmrh.cn/news/106769) §2.2 gathers each expert's token slices).
+// With an expert capacity C ("Qwen2-MoE代码解析" §3.4; C = ceil(T/E)*k in
+// the Qwen2-MoE walk-through (mlqm.cn/news/48291) §2.2), an expert keeps at
+// most C pairs, taken in (slot rank, token index) order; the others are
+// dropped.
+//
+// The order of the rows is (expert, token, slot), so it is a counting sort:
+//   row(t, s) = offsets[e] + #kept pairs of e in earlier chunks
+//             + #kept pairs of e earlier in the same chunk.
+// A chunk is 64 tokens, one per lane; "earlier in the chunk" is a popcount of
+// a wave ballot that matches expert ids bit by bit (7 ballots per slot).
+// No global atomics, so the result is deterministic.
+//
+// Kernels (dropless): count -> scan -> scatter.
+// Kernels (capacity): count per (slot, expert) -> scan (priority bases and
+// offsets) -> keep -> scan of kept counts -> scatter.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kNone = kMaxExperts;   // id of an invalid, dropped or absent pair (bit 6 set)
+constexpr int kScanThreads = 1024;
+constexpr int kScatterTok = 16;      // tokens per scatter block
+constexpr int kScatterThreads = 256;
+
+struct Ballots {
+  uint64_t b[7];
+};
+
+__device__ __forceinline__ Ballots ballots_of(int e) {
+  Ballots r;
+#pragma unroll
+  for (int i = 0; i < 7; ++i) r.b[i] = __ballot((e >> i) & 1);
+  return r;
+}
+
+// Lanes whose ballot value equals e.
+__device__ __forceinline__ uint64_t match(const Ballots& B, int e) {
+  uint64_t m = ~0ull;
+#pragma unroll
+  for (int i = 0; i < 7; ++i) m &= ((e >> i) & 1) ? B.b[i] : ~B.b[i];
+  return m;
+}
+
+__device__ __forceinline__ int load_id(const int32_t* ids, int t, int T, int k, int s, int E) {
+  if (t >= T) return kNone;
+  const int e = ids[static_cast<int64_t>(t) * k + s];
+  return (e >= 0 && e < E) ? e : kNone;
+}
+
+// Histogram of one chunk: cols = E (dropless, col = e) or k*E (capacity, col = s*E + e).
+__global__ __launch_bounds__(kWave) void dispatch_count_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
+                                                               bool per_slot, int32_t* __restrict__ hist) {
+  extern __shared__ int s_hist[];
+  const int cols = per_slot ? k * E : E;
+  for (int c = threadIdx.x; c < cols; c += kWave) s_hist[c] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * kDispatchChunk + threadIdx.x;
+  for (int s = 0; s < k; ++s) {
+    const int e = load_id(ids, t, T, k, s, E);
+    if (e != kNone) atomicAdd(&s_hist[per_slot ? s * E + e : e], 1);
+  }
+  __syncthreads();
+  int32_t* out = hist + static_cast<int64_t>(blockIdx.x) * cols;
+  for (int c = threadIdx.x; c < cols; c += kWave) out[c] = s_hist[c];
+}
+
+enum ScanMode { kScanDropless = 0, kScanCapacity1 = 1, kScanCapacity2 = 2 };
+
+// One block.  Replaces M[c][col] by its exclusive prefix over chunks c, then
+//   dropless:  counts[e] = total, offsets = exclusive scan of totals;
+//   capacity1: counts[e] = sum over slots, slot_base[s][e] = pairs of e in
+//              slots < s, offsets from min(counts, C);
+//   capacity2: nothing more (offsets were written by capacity1).
+// Then perm rows >= N get -1.
+__global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(int32_t* __restrict__ M, int nrows, int ncols,
+                                                                     int mode, int E, int k, int capacity,
+                                                                     int32_t* __restrict__ counts,
+                                                                     int32_t* __restrict__ offsets,
+                                                                     int32_t* __restrict__ slot_base,
+                                                                     int32_t* __restrict__ perm, int total_pairs) {
+  __shared__ int s_part[kScanThreads];
+  __shared__ int s_tot[kMaxExperts * kMaxExperts];
+  __shared__ int s_N;
+  const int tid = threadIdx.x;
+  for (int col0 = 0; col0 < ncols; col0 += kScanThreads) {
+    const int gcols = min(kScanThreads, ncols - col0);
+    const int P = kScanThreads / gcols;
+    const int ci = tid % gcols;
+    const int p = tid / gcols;
+    const int L = (nrows + P - 1) / P;
+    const int r0 = p * L;
+    const int r1 = min(nrows, r0 + L);
+    int sum = 0;
+    if (p < P)
+      for (int r = r0; r < r1; ++r) sum += M[static_cast<int64_t>(r) * ncols + col0 + ci];
+    s_part[tid] = sum;
+    __syncthreads();
+    if (p < P) {
+      int base = 0;
+      for (int q = 0; q < p; ++q) base += s_part[q * gcols + ci];
+      if (p == P - 1) s_tot[col0 + ci] = base + sum;
+      for (int r = r0; r < r1; ++r) {
+        int32_t* m = &M[static_cast<int64_t>(r) * ncols + col0 + ci];
+        const int v = *m;
+        *m = base;
+        base += v;
+      }
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    if (mode == kScanDropless) {
+      int acc = 0;
+      for (int e = 0; e < E; ++e) {
+        counts[e] = s_tot[e];
+        offsets[e] = acc;
+        acc += s_tot[e];
+      }
+      offsets[E] = acc;
+      s_N = acc;
+    } else if (mode == kScanCapacity1) {
+      int acc = 0;
+      for (int e = 0; e < E; ++e) {
+        int n = 0;
+        for (int s = 0; s < k; ++s) {
+          slot_base[s * E + e] = n;
+          n += s_tot[s * E + e];
+        }
+        counts[e] = n;
+        offsets[e] = acc;
+        acc += min(n, capacity);
+      }
+      offsets[E] = acc;
+      s_N = acc;
+    } else {
+      s_N = offsets[E];
+    }
+  }
+  __syncthreads();
+  if (mode != kScanCapacity1)
+    for (int r = s_N + tid; r < total_pairs; r += kScanThreads) perm[r] = -1;
+}
+
+// Capacity: decide which pairs are kept and count them per chunk and expert.
+// Priority of pair (t, s) with expert e = pairs of e in slots < s (all tokens)
+// + pairs of e in slot s of earlier chunks + earlier tokens of this chunk in
+// slot s with expert e.  Kept iff priority < C.
+__global__ __launch_bounds__(kWave) void dispatch_keep_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
+                                                              int capacity, const int32_t* __restrict__ chunk_base,
+                                                              const int32_t* __restrict__ slot_base,
+                                                              int8_t* __restrict__ keep,
+                                                              int32_t* __restrict__ chunk_kept) {
+  __shared__ int s_kept[kMaxExperts];
+  const int lane = threadIdx.x;
+  if (lane < E) s_kept[lane] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * kDispatchChunk + lane;
+  const uint64_t below = (1ull << lane) - 1ull;
+  const int32_t* cb = chunk_base + static_cast<int64_t>(blockIdx.x) * k * E;
+  for (int s = 0; s < k; ++s) {
+    const int e = load_id(ids, t, T, k, s, E);
+    const Ballots B = ballots_of(e);
+    bool kept = false;
+    if (e != kNone) {
+      const int prio = slot_base[s * E + e] + cb[s * E + e] + __popcll(match(B, e) & below);
+      kept = prio < capacity;
+      if (kept) atomicAdd(&s_kept[e], 1);
+    }
+    if (t < T) keep[static_cast<int64_t>(t) * k + s] = kept ? 1 : 0;
+  }
+  __syncthreads();
+  if (lane < E) chunk_kept[static_cast<int64_t>(blockIdx.x) * E + lane] = s_kept[lane];
+}
+
+// Rows of the pairs of 16 tokens, then the copy of their hidden states.
+// Wave 0 ranks all 64 tokens of the enclosing chunk and keeps its 16.
+template <typename T, int KMAX, bool kCap>
+__global__ __launch_bounds__(kScatterThreads) void dispatch_scatter_kernel(
+    const int32_t* __restrict__ ids, const T* __restrict__ X, int T_tok, int d, int E, int k,
+    const int32_t* __restrict__ chunk_base, const int32_t* __restrict__ offsets, const int8_t* __restrict__ keep,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm, T* __restrict__ Xp) {
+  __shared__ int s_row[kScatterTok][KMAX];
+  const int tok0 = blockIdx.x * kScatterTok;
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    const int chunk = tok0 / kDispatchChunk;
+    const int t = chunk * kDispatchChunk + lane;
+    const uint64_t below = (1ull << lane) - 1ull;
+    int e[KMAX];
+    int cnt[KMAX];
+#pragma unroll
+    for (int s = 0; s < KMAX; ++s) {
+      cnt[s] = 0;
+      e[s] = kNone;
+      if (s < k) {
+        e[s] = load_id(ids, t, T_tok, k, s, E);
+        if (kCap && e[s] != kNone && !keep[static_cast<int64_t>(t) * k + s]) e[s] = kNone;
+      }
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < KMAX; ++s2) {
+      if (s2 < k) {
+        const Ballots B = ballots_of(e[s2]);
+#pragma unroll
+        for (int s = 0; s < KMAX; ++s)
+          if (s < k) cnt[s] += __popcll(match(B, e[s]) & below);
+      }
+    }
+    const bool mine = t >= tok0 && t < tok0 + kScatterTok;
+#pragma unroll
+    for (int s = 0; s < KMAX; ++s) {
+      if (s < k && mine) {
+        int row = -1;
+        if (e[s] != kNone) {
+          int same = 0;  // same expert in an earlier slot of this token (only for repeated ids)
+#pragma unroll
+          for (int s2 = 0; s2 < KMAX; ++s2)
+            if (s2 < s && e[s2] == e[s]) ++same;
+          row = offsets[e[s]] + chunk_base[static_cast<int64_t>(chunk) * E + e[s]] + cnt[s] + same;
+          if (row < 0 || row >= T_tok * k) row = -1;  // unreachable for consistent scratch; keeps stores in bounds
+          if (t < T_tok && row >= 0) perm[row] = t * k + s;
+        }
+        if (t < T_tok) inv_perm[static_cast<int64_t>(t) * k + s] = row;
+        s_row[t - tok0][s] = (t < T_tok) ? row : -1;
+      }
+    }
+  }
+  __syncthreads();
+  const int nvec = d * static_cast<int>(sizeof(T)) / 16;
+  const int ntok = min(kScatterTok, T_tok - tok0);
+  for (int idx = threadIdx.x; idx < ntok * nvec; idx += kScatterThreads) {
+    const int tt = idx / nvec;
+    const int v = idx % nvec;
+    const u32x4_t val = ld16(reinterpret_cast<const unsigned char*>(X + static_cast<int64_t>(tok0 + tt) * d) + v * 16);
+    for (int s = 0; s < k; ++s) {
+      const int row = s_row[tt][s];
+      if (row >= 0) st16(reinterpret_cast<unsigned char*>(Xp + static_cast<int64_t>(row) * d) + v * 16, val);
+    }
+  }
+}
+
+template <typename T, int KMAX>
+hipError_t launch_scatter_k(bool cap, int nblocks, const int32_t* ids, const T* X, int T_tok, int d, int E, int k,
+                            const int32_t* cb, const int32_t* offsets, const int8_t* keep, int32_t* perm,
+                            int32_t* inv_perm, T* Xp, hipStream_t stream) {
+  if (cap)
+    hipLaunchKernelGGL((dispatch_scatter_kernel<T, KMAX, true>), dim3(nblocks), dim3(kScatterThreads), 0, stream, ids,
+                       X, T_tok, d, E, k, cb, offsets, keep, perm, inv_perm, Xp);
+  else
+    hipLaunchKernelGGL((dispatch_scatter_kernel<T, KMAX, false>), dim3(nblocks), dim3(kScatterThreads), 0, stream,
+                       ids, X, T_tok, d, E, k, cb, offsets, keep, perm, inv_perm, Xp);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_scatter(bool cap, int nblocks, const int32_t* ids, const T* X, int T_tok, int d, int E, int k,
+                          const int32_t* cb, const int32_t* offsets, const int8_t* keep, int32_t* perm,
+                          int32_t* inv_perm, T* Xp, hipStream_t stream) {
+  if (k <= 2) return launch_scatter_k<T, 2>(cap, nblocks, ids, X, T_tok, d, E, k, cb, offsets, keep, perm, inv_perm, Xp, stream);
+  if (k <= 4) return launch_scatter_k<T, 4>(cap, nblocks, ids, X, T_tok, d, E, k, cb, offsets, keep, perm, inv_perm, Xp, stream);
+  if (k <= 8) return launch_scatter_k<T, 8>(cap, nblocks, ids, X, T_tok, d, E, k, cb, offsets, keep, perm, inv_perm, Xp, stream);
+  return launch_scatter_k<T, kMaxExperts>(cap, nblocks, ids, X, T_tok, d, E, k, cb, offsets, keep, perm, inv_perm, Xp, stream);
+}
+
+size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+}  // namespace
+
+size_t dispatch_scratch_bytes(int T, int E, int k, bool capacity) {
+  const size_t nchunks = (static_cast<size_t>(T) + kDispatchChunk - 1) / kDispatchChunk;
+  size_t b = align256(nchunks * (capacity ? k * E : E) * sizeof(int32_t));
+  if (capacity) {
+    b += align256(nchunks * E * sizeof(int32_t));
+    b += align256(static_cast<size_t>(k) * E * sizeof(int32_t));
+    b += align256(static_cast<size_t>(T) * k);
+  }
+  return b;
+}
+
+DispatchScratch carve_dispatch_scratch(void* ws, int T, int E, int k, bool capacity) {
+  const size_t nchunks = (static_cast<size_t>(T) + kDispatchChunk - 1) / kDispatchChunk;
+  unsigned char* p = static_cast<unsigned char*>(ws);
+  DispatchScratch s{};
+  s.chunk_base = reinterpret_cast<int32_t*>(p);
+  p += align256(nchunks * (capacity ? k * E : E) * sizeof(int32_t));
+  if (capacity) {
+    s.chunk_kept = reinterpret_cast<int32_t*>(p);
+    p += align256(nchunks * E * sizeof(int32_t));
+    s.slot_base = reinterpret_cast<int32_t*>(p);
+    p += align256(static_cast<size_t>(k) * E * sizeof(int32_t));
+    s.keep = reinterpret_cast<int8_t*>(p);
+  }
+  return s;
+}
+
+hipError_t launch_dispatch(int dtype, const int32_t* ids, const void* X, int T, int d, int E, int k, int capacity,
+                           int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* Xp,
+                           const DispatchScratch& sc, hipStream_t stream) {
+  const bool cap = capacity >= 0;
+  const int nchunks = (T + kDispatchChunk - 1) / kDispatchChunk;
+  const int total_pairs = T * k;
+  if (T <= 0) {
+    // No tokens: every expert is empty.
+    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, sc.chunk_base, 0, E,
+                       static_cast<int>(kScanDropless), E, k, capacity, counts, offsets, sc.slot_base, perm, 0);
+    return hipGetLastError();
+  }
+  const int cols = cap ? k * E : E;
+  hipLaunchKernelGGL(dispatch_count_kernel, dim3(nchunks), dim3(kWave), cols * sizeof(int), stream, ids, T, E, k, cap,
+                     sc.chunk_base);
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, sc.chunk_base, nchunks, cols,
+                     static_cast<int>(cap ? kScanCapacity1 : kScanDropless), E, k, capacity, counts, offsets,
+                     sc.slot_base, perm, total_pairs);
+  const int32_t* row_base = sc.chunk_base;
+  if (cap) {
+    hipLaunchKernelGGL(dispatch_keep_kernel, dim3(nchunks), dim3(kWave), 0, stream, ids, T, E, k, capacity,
+                       sc.chunk_base, sc.slot_base, sc.keep, sc.chunk_kept);
+    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, sc.chunk_kept, nchunks, E,
+                       static_cast<int>(kScanCapacity2), E, k, capacity, counts, offsets, sc.slot_base, perm,
+                       total_pairs);
+    row_base = sc.chunk_kept;
+  }
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  const int nblocks = (T + kScatterTok - 1) / kScatterTok;
+  if (dtype == kDtypeBF16)
+    return launch_scatter<uint16_t>(cap, nblocks, ids, static_cast<const uint16_t*>(X), T, d, E, k, row_base, offsets,
+                                    sc.keep, perm, inv_perm, static_cast<uint16_t*>(Xp), stream);
+  return launch_scatter<float>(cap, nblocks, ids, static_cast<const float*>(X), T, d, E, k, row_base, offsets, sc.keep,
+                               perm, inv_perm, static_cast<float*>(Xp), stream);
+}
+
+}  // namespace moe

@@ -1,0 +1,45 @@
+// Host-side launchers of the gfx950 kernels (internal to libmoe).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kDtypeF32 = 0;
+constexpr int kDtypeBF16 = 1;
+
+// Tokens per dispatch chunk: one wave, one token per lane.
+constexpr int kDispatchChunk = 64;
+constexpr int kMaxExpertsAbi = 64;  // expert ids fit one wave (64 lanes)
+
+// Scratch of the dispatcher, carved from the caller's workspace.
+struct DispatchScratch {
+  int32_t* chunk_base;   // [nchunks][cols]: per-chunk histogram, then its chunk-exclusive prefix
+  int32_t* chunk_kept;   // [nchunks][E]:  kept pairs per chunk, then prefix (capacity only)
+  int32_t* slot_base;    // [k][E]: pairs of expert e in slots < s (capacity only)
+  int8_t* keep;          // [T*k]: keep flag per pair (capacity only)
+};
+
+size_t dispatch_scratch_bytes(int T, int E, int k, bool capacity);
+DispatchScratch carve_dispatch_scratch(void* ws, int T, int E, int k, bool capacity);
+
+hipError_t launch_router(int dtype, const void* X, const void* Wg, const float* bias, int T, int d, int E, int k,
+                         int32_t* ids, float* w, hipStream_t stream);
+
+hipError_t launch_dispatch(int dtype, const int32_t* ids, const void* X, int T, int d, int E, int k, int capacity,
+                           int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* Xp,
+                           const DispatchScratch& scratch, hipStream_t stream);
+
+// C[r, :] = act(A[r, :] . B[e]^T) for the rows r of each expert segment.
+// A: [rows, K]; B: [E, N, K]; C: [rows, N]; rows bounded by max_rows.
+hipError_t launch_grouped_gemm(int dtype, bool gelu, const void* A, const void* B, void* C,
+                               const int32_t* offsets, int E, int N, int K, int max_rows, hipStream_t stream);
+
+hipError_t launch_combine(int dtype, const void* Yp, const int32_t* inv_perm, const float* topk_w, void* out, int T,
+                          int d, int k, hipStream_t stream);
+
+int device_cu_count();
+
+}  // namespace moe
