@@ -78,7 +78,7 @@ def cpu_baseline(w, inp, sample):
         toks = n * w.T
         desc = f"{n} decode steps of {w.T} tokens, full weights"
     else:
-        n = sample or min(w.T, 1024)
+        n = sample or min(w.T, 8192)
         cap = (-(-n // w.E) * w.k) if inp.expert_capacity >= 0 else -1
         oracle.moe_forward(inp.X[:n], inp.Wg, inp.bias, inp.W1, inp.W2, w.k, cap, w.dtype)
         toks = n
