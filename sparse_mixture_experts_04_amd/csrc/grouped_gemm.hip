@@ -222,6 +222,317 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_kernel(const T* 
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 main kernel: 256x256 tiles, 4 waves of 128x128, 32x32x16 MFMAs, and a
+// 4-deep ring of LDS stages fed by direct global->LDS loads.
+//
+// * Stage = 32 K-elements (64 bytes) of 256 token rows and 256 weight rows,
+//   32 KB; four stages = 128 KB of LDS.  Loads run three stages ahead, and the
+//   stream of (tile, stage) pairs is continuous across the persistent block's
+//   tiles, so the next tile's first stages load during this tile's last
+//   stages and epilogue.
+// * LDS layout: two 64-byte rows share a 128-byte line; the eight 16-byte
+//   chunks of a line are XOR-permuted by a per-line key so that the fragment
+//   reads of 8 (or 16) consecutive lanes hit distinct banks.
+// * The weight rows are the MFMA A operand and the token rows the B operand,
+//   so a lane of the 32x32 result holds one token row.  The weight rows of
+//   each 32-row fragment are loaded in the order pi(x) = 16*((x>>2)&1) +
+//   4*(x>>3) + (x&3), which makes a lane's 16 results 16 consecutive output
+//   columns: two 16-byte stores.
+constexpr int kBig = 256;                                 // BM = BN
+constexpr int kBigThreads = 256;                          // 4 waves, 2 x 2
+constexpr int kStageRowBytes = 64;                        // K bytes per row per stage
+constexpr int kOperandBytes = kBig * kStageRowBytes;      // 16 KB
+constexpr int kRingStageBytes = 2 * kOperandBytes;        // tokens + weights
+constexpr int kRing = 4;
+constexpr size_t kBigLds = static_cast<size_t>(kRing) * kRingStageBytes;  // 128 KB
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ int key_x(int line) { return ((line >> 1) & 3) ^ ((line & 1) << 1); }
+__device__ __forceinline__ int key_w(int line) {
+  return (((line >> 1) ^ line) & 1) | ((((line >> 3) ^ line) & 1) << 1);
+}
+// Byte offset of logical chunk c (0..3) of `row` within an operand tile.
+__device__ __forceinline__ int off_x(int row, int c) {
+  const int line = row >> 1;
+  return line * 128 + (((((row & 1) << 2) | c) ^ key_x(line)) << 4);
+}
+__device__ __forceinline__ int off_w(int row, int c) {
+  const int line = row >> 1;
+  return line * 128 + (((((row & 1) << 2) | c) ^ key_w(line)) << 4);
+}
+
+// x * sigmoid(2u) = 0.5 x (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3).
+__device__ __forceinline__ float gelu_tanh_fast(float x) {
+  const float kSqrt2OverPi = 0.7978845608028654f;
+  const float u = kSqrt2OverPi * fmaf(0.044715f * x, x * x, x);
+  return __fdividef(x, 1.0f + __expf(-2.0f * u));
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  // gfx9 s_waitcnt: vmcnt[3:0] and [15:14], expcnt[6:4] (7 = no wait), lgkmcnt[11:8] (15 = no wait)
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+struct TileCoord {
+  int e, m0, n0, seg1;
+};
+
+template <bool kGelu>
+__global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const uint16_t* __restrict__ A,
+                                                                        const uint16_t* __restrict__ B,
+                                                                        uint16_t* __restrict__ C,
+                                                                        const int32_t* __restrict__ offsets, int E,
+                                                                        int N, int K, int max_rows) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ int s_tile_base[kMaxExperts + 1];
+  __shared__ int s_seg0[kMaxExperts];
+  __shared__ int s_seg1[kMaxExperts];
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
+  const int wm = wave >> 1;   // token half of the tile
+  const int wn = wave & 1;    // weight half of the tile
+
+  if (tid < kWave) {
+    const int e = tid;
+    int mt = 0, seg0 = 0, seg1 = 0;
+    if (e < E) {
+      seg0 = min(max(offsets[e], 0), max_rows);
+      seg1 = min(max(offsets[e + 1], seg0), max_rows);
+      mt = (seg1 - seg0 + kBig - 1) / kBig;
+    }
+    int incl = mt;
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) {
+      const int o = __shfl_up(incl, m);
+      if (lane >= m) incl += o;
+    }
+    if (e < E) {
+      s_tile_base[e + 1] = incl;
+      s_seg0[e] = seg0;
+      s_seg1[e] = seg1;
+    }
+    if (e == 0) s_tile_base[0] = 0;
+  }
+  __syncthreads();
+
+  const int n_tiles_n = (N + kBig - 1) / kBig;
+  const int total = s_tile_base[E] * n_tiles_n;
+  const int G = gridDim.x;
+  int first = blockIdx.x;
+  if ((G & 7) == 0) first = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  if (first >= total) return;
+  const int kstages = K * 2 / kStageRowBytes;
+  const int64_t row_stride = static_cast<int64_t>(K) * 2;
+
+  auto coord = [&](int tile) {
+    int e = 0;
+    while (e + 1 < E && s_tile_base[e + 1] * n_tiles_n <= tile) ++e;
+    const int mt_e = s_tile_base[e + 1] - s_tile_base[e];
+    const int local = tile - s_tile_base[e] * n_tiles_n;
+    TileCoord t;
+    t.e = e;
+    t.n0 = (local / mt_e) * kBig;
+    t.m0 = s_seg0[e] + (local % mt_e) * kBig;
+    t.seg1 = s_seg1[e];
+    return t;
+  };
+
+  // ---- producer: direct loads of one stage (4 + 4 instructions of 1 KB per wave)
+  // Instruction t of this wave covers rows wave*64 + t*16 .. +15 = lines L0 .. L0+7,
+  // L0 = wave*32 + t*8; lane p fills line L0 + p/8, physical chunk p%8.
+  const int ld_line_lo = lane >> 3;
+  const int ld_phys = lane & 7;
+  const unsigned char* xsrc[4];
+  const unsigned char* wsrc[4];
+  int p_tile = first, p_ks = 0, p_count = 0;
+  auto producer_setup = [&](int tile) {
+    const TileCoord t = coord(tile);
+    const unsigned char* Ab = reinterpret_cast<const unsigned char*>(A);
+    const unsigned char* Bb = reinterpret_cast<const unsigned char*>(B) + static_cast<int64_t>(t.e) * N * row_stride;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int line = wave * 32 + i * 8 + ld_line_lo;
+      const int qx = ld_phys ^ key_x(line);
+      const int rx = 2 * line + (qx >> 2);
+      xsrc[i] = Ab + min(t.m0 + rx, t.seg1 - 1) * row_stride + (qx & 3) * 16;
+      const int qw = ld_phys ^ key_w(line);
+      const int rw = 2 * line + (qw >> 2);
+      wsrc[i] = Bb + min(t.n0 + rw, N - 1) * row_stride + (qw & 3) * 16;
+    }
+  };
+  // Issue one stage into ring slot p_count % 4.  Past the last tile the
+  // pointers of the last tile are reused (harmless loads into a free slot), so
+  // the issue is branch-free and can be interleaved with the MFMAs.
+  auto produce_issue = [&]() {
+    unsigned char* sx = smem + (p_count & (kRing - 1)) * kRingStageBytes;
+    unsigned char* sw = sx + kOperandBytes;
+    const int64_t koff = static_cast<int64_t>(p_ks) * kStageRowBytes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int run = (wave * 32 + i * 8) * 128;
+      __builtin_amdgcn_global_load_lds(xsrc[i] + koff, (lds_ptr_t)(sx + run), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(wsrc[i] + koff, (lds_ptr_t)(sw + run), 16, 0, 0);
+    }
+  };
+  auto produce_advance = [&]() {
+    ++p_count;
+    if (++p_ks == kstages) {
+      p_ks = 0;
+      p_tile += G;
+      if (p_tile < total) producer_setup(p_tile);
+    }
+  };
+  auto produce = [&]() {
+    produce_issue();
+    produce_advance();
+  };
+
+  producer_setup(p_tile);
+#pragma unroll
+  for (int i = 0; i < kRing - 1; ++i)
+    if (p_tile < total) produce();
+
+  const int frow = lane & 31;
+  const int fhalf = lane >> 5;
+  const int wrow = ((frow >> 2) & 1) * 16 + (frow >> 3) * 4 + (frow & 3);  // pi(frow)
+  int c_count = 0;
+
+  // Fragments of one 16-element k-step: 4 weight and 4 token fragments.
+  u32x4_t wf0[4], xf0[4], wf1[4], xf1[4];
+  auto read_frags = [&](int slot, int kk, u32x4_t (&wf)[4], u32x4_t (&xf)[4]) {
+    const unsigned char* sx = smem + slot * kRingStageBytes;
+    const unsigned char* sw = sx + kOperandBytes;
+    const int c = kk * 2 + fhalf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wf[i] = *reinterpret_cast<const u32x4_t*>(sw + off_w(wn * 128 + i * 32 + wrow, c));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xf[j] = *reinterpret_cast<const u32x4_t*>(sx + off_x(wm * 128 + j * 32 + frow, c));
+  };
+  // Issue the 8 fragment reads of the other k-step among the first 4 of the
+  // 16 MFMAs of a region, so their latency hides behind the MFMA stream.
+  auto interleave_reads = [&]() {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Same, with the 8 global->LDS loads of the next stage spread over the
+  // first 4 MFMAs as well.
+  auto interleave_loads_reads = [&]() {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // 2 global->LDS loads
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  // Stage 0 must be resident before its first fragments are read.
+  wait_vmcnt<0>();
+  barrier();
+  read_frags(0, 0, wf0, xf0);
+  bool after_epilogue = false;
+
+  for (int tile = first; tile < total; tile += G) {
+    const TileCoord tc = coord(tile);
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+    for (int ks = 0; ks < kstages; ++ks) {
+      // k-step 0 of this stage is in wf0/xf0; read k-step 1, then run k-step 0.
+      const int slot = c_count & (kRing - 1);
+      read_frags(slot, 1, wf1, xf1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = GemmMma<uint16_t>::run(wf0[i], xf0[j], acc[i][j]);
+      interleave_reads();
+      // The next stage must have landed (one later stage may stay in flight;
+      // right after an epilogue its stores are outstanding too: drain).
+      ++c_count;
+      const int ahead = p_count - c_count - 1;
+      if (after_epilogue || ahead <= 0) wait_vmcnt<0>();
+      else wait_vmcnt<8>();
+      after_epilogue = false;
+      barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      // Every wave is past the slot of stage c_count - 2 (read last iteration): refill it.
+      produce_issue();
+      // (past the last stage this reads a stale slot whose values go unused)
+      read_frags(c_count & (kRing - 1), 0, wf0, xf0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = GemmMma<uint16_t>::run(wf1[i], xf1[j], acc[i][j]);
+      interleave_loads_reads();
+      produce_advance();
+    }
+    after_epilogue = true;
+
+    // acc[i][j][q]: token row m0 + wm*128 + j*32 + frow, column n0 + wn*128 + i*32 + 16*fhalf + q.
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = tc.m0 + wm * 128 + j * 32 + frow;
+      if (row >= tc.seg1) continue;
+      uint16_t* crow = C + static_cast<int64_t>(row) * N;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int col = tc.n0 + wn * 128 + i * 32 + 16 * fhalf;
+        if (col >= N) continue;
+        float v[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) v[q] = kGelu ? gelu_tanh_fast(acc[i][j][q]) : acc[i][j][q];
+        u32x4_t lo, hi;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          lo[h] = pack_bf16x2(v[2 * h], v[2 * h + 1]);
+          hi[h] = pack_bf16x2(v[8 + 2 * h], v[8 + 2 * h + 1]);
+        }
+        st16(crow + col, lo);
+        st16(crow + col + 8, hi);
+      }
+    }
+  }
+  wait_vmcnt<0>();
+}
+
+template <bool kGelu>
+hipError_t launch_big(const uint16_t* A, const uint16_t* B, uint16_t* C, const int32_t* offsets, int E, int N, int K,
+                      int max_rows, hipStream_t stream) {
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_bf16_256<kGelu>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     static_cast<int>(kBigLds));
+  if (attr != hipSuccess) return attr;
+  const int n_tiles_n = (N + kBig - 1) / kBig;
+  const int64_t upper = (static_cast<int64_t>((max_rows + kBig - 1) / kBig) + E) * n_tiles_n;
+  int64_t grid = device_cu_count();
+  if (upper < grid) grid = upper;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL((grouped_gemm_bf16_256<kGelu>), dim3(static_cast<unsigned>(grid)), dim3(kBigThreads), kBigLds,
+                     stream, A, B, C, offsets, E, N, K, max_rows);
+  return hipGetLastError();
+}
+
 struct GemmShape {
   int BM, BN;
 };
@@ -249,9 +560,13 @@ hipError_t launch_cfg(bool gelu, const T* A, const T* B, T* C, const int32_t* of
 hipError_t launch_grouped_gemm(int dtype, bool gelu, const void* A, const void* B, void* C, const int32_t* offsets,
                                int E, int N, int K, int max_rows, hipStream_t stream) {
   if (max_rows <= 0) return hipSuccess;
-  if (dtype == kDtypeBF16)
-    return launch_cfg<uint16_t, 128, 128, 2, 2>(gelu, static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B),
-                                                static_cast<uint16_t*>(C), offsets, E, N, K, max_rows, stream);
+  if (dtype == kDtypeBF16) {
+    const uint16_t* a = static_cast<const uint16_t*>(A);
+    const uint16_t* b = static_cast<const uint16_t*>(B);
+    uint16_t* c = static_cast<uint16_t*>(C);
+    return gelu ? launch_big<true>(a, b, c, offsets, E, N, K, max_rows, stream)
+                : launch_big<false>(a, b, c, offsets, E, N, K, max_rows, stream);
+  }
   return launch_cfg<float, 64, 64, 2, 2>(gelu, static_cast<const float*>(A), static_cast<const float*>(B),
                                          static_cast<float*>(C), offsets, E, N, K, max_rows, stream);
 }
