@@ -136,14 +136,14 @@ def main():
     Xp, H, Yp = b.workspace_view(cfg, "Xp"), b.workspace_view(cfg, "H"), b.workspace_view(cfg, "Yp")
     names = ["route", "dispatch", "expert_up", "expert_down", "combine"]
     stage_ms = {n: 0.0 for n in names}
-    dws = b.ws  # dispatch scratch sits at the front of the forward workspace
-    dbytes = moe.moe_workspace_size(cfg, moe.MOE_OP_DISPATCH)
+    rws, rbytes = b.scratch_view(cfg, "route"), moe.moe_workspace_size(cfg, moe.MOE_OP_ROUTE)
+    dws, dbytes = b.scratch_view(cfg, "dispatch"), moe.moe_workspace_size(cfg, moe.MOE_OP_DISPATCH)
     per_step_active, per_step_N = [], []
     for i in range(args.steps):
         X = xs[i % len(xs)]
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
         evs[0].record(stream)
-        moe.moe_route(cfg, X, Wg, bias, b.topk_ids, b.topk_w)
+        moe.moe_route(cfg, X, Wg, bias, b.topk_ids, b.topk_w, rws, rbytes)
         evs[1].record(stream)
         moe.moe_dispatch(cfg, b.topk_ids, X, b.expert_counts, b.expert_offsets, b.perm, b.inv_perm, Xp, dws, dbytes)
         evs[2].record(stream)

@@ -76,7 +76,8 @@ typedef struct moe_config {
 typedef enum moe_op {
   MOE_OP_DISPATCH = 0,   /* moe_dispatch                                  */
   MOE_OP_EXPERT_FFN = 1, /* moe_expert_ffn (holds H)                      */
-  MOE_OP_FORWARD = 2     /* moe_forward (dispatch scratch + Xp + H + Yp)  */
+  MOE_OP_FORWARD = 2,    /* moe_forward (all scratch + Xp + H + Yp)       */
+  MOE_OP_ROUTE = 3       /* moe_route (partial logits when K is split)    */
 } moe_op;
 
 /* Human-readable name of a status.  Static string; never NULL. */
@@ -95,10 +96,13 @@ moe_status moe_workspace_size(const moe_config* cfg, int32_t op, size_t* bytes);
  *   logit bias, the domain bias of mlqm §6).
  *   topk_ids [T, k] int32 out: slot 0 holds the most probable expert; slots in
  *   descending probability; equal logits go to the lower expert id.
- *   topk_w [T, k] float out: p_s / sum_j p_j over the k selected experts. */
+ *   topk_w [T, k] float out: p_s / sum_j p_j over the k selected experts.
+ *   ws / ws_bytes: workspace of moe_workspace_size(cfg, MOE_OP_ROUTE) bytes:
+ *   the gate transposed to [16*ceil(E/16), d] and, when T is small (the gate
+ *   projection is then split over K across blocks), the partial logits. */
 moe_status moe_route(const moe_config* cfg, const void* X, const void* Wg,
                      const float* gate_bias, int32_t* topk_ids, float* topk_w,
-                     void* stream);
+                     void* ws, size_t ws_bytes, void* stream);
 
 /* Dispatcher: group the (token, slot) pairs by expert
  * [jsqmd §3.1 detail 3; wmrh §2.2; capacity: jsqmd §3.4, mlqm §2.2].

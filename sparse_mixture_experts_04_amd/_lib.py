@@ -28,6 +28,7 @@ MOE_BF16 = 1
 MOE_OP_DISPATCH = 0
 MOE_OP_EXPERT_FFN = 1
 MOE_OP_FORWARD = 2
+MOE_OP_ROUTE = 3
 
 # Every symbol include/moe.h declares.
 EXPORTED = ("moe_status_string", "moe_version", "moe_workspace_size", "moe_route", "moe_dispatch",
@@ -62,7 +63,7 @@ def _load():
         "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "moe_version": (ctypes.c_char_p, []),
         "moe_workspace_size": (ctypes.c_int, [CFG, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]),
-        "moe_route": (ctypes.c_int, [CFG, P, P, P, P, P, P]),
+        "moe_route": (ctypes.c_int, [CFG, P, P, P, P, P, P, ctypes.c_size_t, P]),
         "moe_dispatch": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
         "moe_expert_up": (ctypes.c_int, [CFG, P, P, P, P, P]),
         "moe_expert_down": (ctypes.c_int, [CFG, P, P, P, P, P]),
@@ -135,9 +136,11 @@ def moe_workspace_size(cfg: MoeConfig, op: int) -> int:
     return n.value
 
 
-def moe_route(cfg, X, Wg, gate_bias, topk_ids, topk_w, stream=None) -> None:
+def moe_route(cfg, X, Wg, gate_bias, topk_ids, topk_w, ws=None, ws_bytes=None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check("moe_route", LIB.moe_route(ctypes.byref(cfg), _ptr(X), _ptr(Wg), _ptr(gate_bias), _ptr(topk_ids),
-                                      _ptr(topk_w), _stream(stream)))
+                                      _ptr(topk_w), _ptr(ws), int(ws_bytes), _stream(stream)))
 
 
 def moe_dispatch(cfg, topk_ids, X, expert_counts, expert_offsets, perm, inv_perm, Xp, ws, ws_bytes=None,

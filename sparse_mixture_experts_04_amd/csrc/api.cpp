@@ -53,11 +53,23 @@ size_t pairs_of(const moe_config* c) {
   return static_cast<size_t>(c->num_tokens) * static_cast<size_t>(c->num_experts_per_tok);
 }
 
+size_t route_bytes(const moe_config* c) {
+  return moe::router_scratch_bytes(c->num_tokens, c->hidden_size, c->num_experts, c->dtype);
+}
 size_t dispatch_bytes(const moe_config* c) {
   return moe::dispatch_scratch_bytes(c->num_tokens, c->num_experts, c->num_experts_per_tok, capacity_mode(c));
 }
 size_t h_bytes(const moe_config* c) { return align256(pairs_of(c) * c->intermediate_size * esize(c)); }
 size_t xp_bytes(const moe_config* c) { return align256(pairs_of(c) * c->hidden_size * esize(c)); }
+
+// Rows one expert can hold: every (token, slot) pair at most (ids given to
+// moe_dispatch may repeat an expert within a token), and at most C under a
+// capacity.
+int rows_per_expert_bound(const moe_config* c) {
+  int b = static_cast<int>(pairs_of(c));
+  if (c->expert_capacity >= 0 && c->expert_capacity < b) b = c->expert_capacity;
+  return b;
+}
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
@@ -84,20 +96,26 @@ moe_status moe_workspace_size(const moe_config* cfg, int32_t op, size_t* bytes) 
   if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
   if (moe_status s = check_cfg(cfg); s != MOE_OK) return s;
   switch (op) {
+    case MOE_OP_ROUTE: *bytes = route_bytes(cfg); return MOE_OK;
     case MOE_OP_DISPATCH: *bytes = dispatch_bytes(cfg); return MOE_OK;
     case MOE_OP_EXPERT_FFN: *bytes = h_bytes(cfg); return MOE_OK;
-    case MOE_OP_FORWARD: *bytes = align256(dispatch_bytes(cfg)) + 2 * xp_bytes(cfg) + h_bytes(cfg); return MOE_OK;
+    case MOE_OP_FORWARD:
+      *bytes = align256(route_bytes(cfg)) + align256(dispatch_bytes(cfg)) + 2 * xp_bytes(cfg) + h_bytes(cfg);
+      return MOE_OK;
     default: return MOE_ERR_INVALID_ARG;
   }
 }
 
 moe_status moe_route(const moe_config* cfg, const void* X, const void* Wg, const float* gate_bias,
-                     int32_t* topk_ids, float* topk_w, void* stream) {
+                     int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes, void* stream) {
   if (moe_status s = check_cfg(cfg); s != MOE_OK) return s;
   if (cfg->num_tokens == 0) return MOE_OK;
   if (!X || !Wg || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+  const size_t need = route_bytes(cfg);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (ws == nullptr) return MOE_ERR_INVALID_ARG;
   return hip_status(moe::launch_router(cfg->dtype, X, Wg, gate_bias, cfg->num_tokens, cfg->hidden_size,
-                                       cfg->num_experts, cfg->num_experts_per_tok, topk_ids, topk_w,
+                                       cfg->num_experts, cfg->num_experts_per_tok, topk_ids, topk_w, ws,
                                        as_stream(stream)));
 }
 
@@ -124,7 +142,8 @@ moe_status moe_expert_up(const moe_config* cfg, const void* Xp, const int32_t* e
   if (!Xp || !expert_offsets || !W1 || !H) return MOE_ERR_INVALID_ARG;
   return hip_status(moe::launch_grouped_gemm(cfg->dtype, true, Xp, W1, H, expert_offsets, cfg->num_experts,
                                              cfg->intermediate_size, cfg->hidden_size,
-                                             static_cast<int>(pairs_of(cfg)), as_stream(stream)));
+                                             static_cast<int>(pairs_of(cfg)), rows_per_expert_bound(cfg),
+                                             as_stream(stream)));
 }
 
 moe_status moe_expert_down(const moe_config* cfg, const void* H, const int32_t* expert_offsets, const void* W2,
@@ -134,7 +153,8 @@ moe_status moe_expert_down(const moe_config* cfg, const void* H, const int32_t* 
   if (!H || !expert_offsets || !W2 || !Yp) return MOE_ERR_INVALID_ARG;
   return hip_status(moe::launch_grouped_gemm(cfg->dtype, false, H, W2, Yp, expert_offsets, cfg->num_experts,
                                              cfg->hidden_size, cfg->intermediate_size,
-                                             static_cast<int>(pairs_of(cfg)), as_stream(stream)));
+                                             static_cast<int>(pairs_of(cfg)), rows_per_expert_bound(cfg),
+                                             as_stream(stream)));
 }
 
 moe_status moe_expert_ffn(const moe_config* cfg, const void* Xp, const int32_t* expert_offsets, const void* W1,
@@ -171,6 +191,8 @@ moe_status moe_forward(const moe_config* cfg, const void* X, const void* Wg, con
   if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
   if (ws == nullptr) return MOE_ERR_INVALID_ARG;
   unsigned char* p = static_cast<unsigned char*>(ws);
+  void* rws = p;
+  p += align256(route_bytes(cfg));
   void* dws = p;
   p += align256(dispatch_bytes(cfg));
   void* Xp = p;
@@ -178,7 +200,8 @@ moe_status moe_forward(const moe_config* cfg, const void* X, const void* Wg, con
   void* H = p;
   p += h_bytes(cfg);
   void* Yp = p;
-  if (moe_status s = moe_route(cfg, X, Wg, gate_bias, topk_ids, topk_w, stream); s != MOE_OK) return s;
+  if (moe_status s = moe_route(cfg, X, Wg, gate_bias, topk_ids, topk_w, rws, route_bytes(cfg), stream); s != MOE_OK)
+    return s;
   if (moe_status s = moe_dispatch(cfg, topk_ids, X, expert_counts, expert_offsets, perm, inv_perm, Xp, dws,
                                   dispatch_bytes(cfg), stream);
       s != MOE_OK)

@@ -25,17 +25,23 @@ struct DispatchScratch {
 size_t dispatch_scratch_bytes(int T, int E, int k, bool capacity);
 DispatchScratch carve_dispatch_scratch(void* ws, int T, int E, int k, bool capacity);
 
+// Router scratch: the transposed gate and, when T is small, the partial
+// logits of the K splits.
+size_t router_scratch_bytes(int T, int d, int E, int dtype);
 hipError_t launch_router(int dtype, const void* X, const void* Wg, const float* bias, int T, int d, int E, int k,
-                         int32_t* ids, float* w, hipStream_t stream);
+                         int32_t* ids, float* w, void* scratch, hipStream_t stream);
 
 hipError_t launch_dispatch(int dtype, const int32_t* ids, const void* X, int T, int d, int E, int k, int capacity,
                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* Xp,
                            const DispatchScratch& scratch, hipStream_t stream);
 
 // C[r, :] = act(A[r, :] . B[e]^T) for the rows r of each expert segment.
-// A: [rows, K]; B: [E, N, K]; C: [rows, N]; rows bounded by max_rows.
+// A: [rows, K]; B: [E, N, K]; C: [rows, N]; rows bounded by max_rows, and
+// no expert holds more than max_tokens_per_expert rows (at most T: a token
+// picks an expert once), which selects the skinny kernel for decode shapes.
 hipError_t launch_grouped_gemm(int dtype, bool gelu, const void* A, const void* B, void* C,
-                               const int32_t* offsets, int E, int N, int K, int max_rows, hipStream_t stream);
+                               const int32_t* offsets, int E, int N, int K, int max_rows,
+                               int max_tokens_per_expert, hipStream_t stream);
 
 hipError_t launch_combine(int dtype, const void* Yp, const int32_t* inv_perm, const float* topk_w, void* out, int T,
                           int d, int k, hipStream_t stream);

@@ -1,4 +1,4 @@
-// Router kernel: gate projection on MFMA, softmax-free top-k selection on the
+// Router kernels: gate projection on MFMA, softmax-free top-k selection on the
 // logits with 16-lane shuffle reductions, and renormalised weights.
 //
 // Method ("Qwen2-MoE代码解析" (jsqmd.com/news/1061813) §3.1; Qwen2-MoE
@@ -9,26 +9,30 @@
 // over the selected logits l_j (l_0 the largest): the full softmax
 // denominator cancels and never has to be formed.
 //
-// Layout of the work: a wave owns 16 tokens and every expert (E <= 64, i.e.
-// up to four 16-column MFMA tiles).  Per stage each lane streams 64 contiguous
-// bytes of its token's row (4 x 16 B), so a row is read front to back by 4
-// lanes.  The stage's slice of W_g ([d, E], experts contiguous) is staged
-// through LDS transposed to [expert][k] so MFMA B fragments are 16-byte reads.
-// The MFMA reduction order over k is a permutation of the plain order, the
-// same one on A and B, so the products are unchanged.
+// Work layout.  W_g ([d, E], experts contiguous) is first transposed into the
+// workspace as WgT [16*ceil(E/16)][d] (rows past E zero), so that MFMA
+// B fragments are 16-byte loads of 8 consecutive k.  A block then owns 32
+// tokens (two 16-row MFMA tiles) and every expert (up to four 16-column
+// tiles) over a range of K; each of its 4 waves streams a quarter of that
+// range straight from global memory (X from HBM, WgT from L2), with no LDS
+// staging and no block-wide sync inside the K loop, and the 4 partial logit
+// tiles are summed in LDS.
+// When there are too few token blocks to fill the GPU (decode), K is split
+// across blocks: each writes partial logits to the workspace and a second
+// kernel sums the splits in a fixed order and selects.  The reduction over K
+// runs in a fixed order, so results are deterministic.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int kRouterWaves = 2;               // waves per block
-constexpr int kRouterThreads = kRouterWaves * kWave;
-constexpr int kTokPerWave = 16;
-constexpr int kStageBytes = 256;              // bytes of one row per stage (16 chunks)
-constexpr int kSwRowBytes = kStageBytes + 16; // padded LDS row of the transposed gate slice
+constexpr int kRouterThreads = 256;               // 4 waves
+constexpr int kRouterTok = 32;                    // tokens per block: 2 row tiles of 16
+constexpr int kRowTiles = kRouterTok / 16;
+constexpr int kChunkBytes = 64;                   // K bytes per MFMA k-step per row (4 lane groups x 16 B)
 
-// One 16-byte chunk of A (token row) and B (gate column) into the 16x16 tile.
+// One 16-byte chunk of A (token row) and B (gate column) into a 16x16 tile.
 template <typename T> struct RouterMma;
 template <> struct RouterMma<uint16_t> {
   static __device__ __forceinline__ f32x4_t run(u32x4_t a, u32x4_t b, f32x4_t c) {
@@ -49,112 +53,16 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
-template <typename T, int NT>
-__global__ __launch_bounds__(kRouterThreads) void router_kernel(
-    const T* __restrict__ X, const T* __restrict__ Wg, const float* __restrict__ bias,
-    int T_tokens, int d, int E, int k, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w) {
-  constexpr int kPer16 = 16 / sizeof(T);             // elements per 16-byte chunk
-  constexpr int kStageElems = kStageBytes / sizeof(T);
-  __shared__ __attribute__((aligned(16))) unsigned char sW[NT * 16 * kSwRowBytes];
-  __shared__ float sel_val[kRouterWaves][kTokPerWave][kMaxExperts];
-  __shared__ int sel_id[kRouterWaves][kTokPerWave][kMaxExperts];
-
+// Top-k + renormalisation for one 16-token row tile held in MFMA C layout:
+// acc[t][i] is the logit of token row (lane>>4)*4+i and expert t*16+(lane&15).
+// sel_val / sel_id: LDS scratch [16][k] of the calling wave.
+template <int NT>
+__device__ __forceinline__ void topk_tile(f32x4_t (&acc)[NT], const float* __restrict__ bias, int E, int k,
+                                          int tok0, int T_tokens, float* sel_val, int* sel_id,
+                                          int32_t* __restrict__ topk_ids, float* __restrict__ topk_w) {
   const int lane = threadIdx.x % kWave;
-  const int wave = threadIdx.x / kWave;
-  const int n = lane & 15;      // MFMA column / A row within the 16-row tile
-  const int grp = lane >> 4;    // 0..3
-  const int tok0 = (blockIdx.x * kRouterWaves + wave) * kTokPerWave;
-
-  // Columns >= E of the staged slice stay zero for the whole kernel.
-  for (int i = threadIdx.x; i < NT * 16 * kSwRowBytes / 4; i += kRouterThreads)
-    reinterpret_cast<uint32_t*>(sW)[i] = 0u;
-
-  const int arow = min(tok0 + n, T_tokens - 1);     // clamp: rows past T are computed and ignored
-  const unsigned char* xrow = reinterpret_cast<const unsigned char*>(X + static_cast<int64_t>(arow) * d);
-  const int row_bytes = d * static_cast<int>(sizeof(T));
-  const int nstages = (row_bytes + kStageBytes - 1) / kStageBytes;
-
-  auto load_x = [&](int st, u32x4_t (&r)[4]) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int off = st * kStageBytes + (grp * 4 + j) * 16;
-      r[j] = off < row_bytes ? ld16(xrow + off) : u32x4_t{0u, 0u, 0u, 0u};
-    }
-  };
-
-  // Gate slice of one stage: kStageElems rows of W_g, each E elements.
-  const bool vec_ok = (E % kPer16) == 0;
-  const int nvec = vec_ok ? kStageElems * (E / kPer16) : kStageElems * E;
-  constexpr int kMaxW = (kStageElems * NT * 16 / kPer16 + kRouterThreads - 1) / kRouterThreads;
-  u32x4_t wreg[kMaxW];
-  auto load_w = [&](int st) {
-    const int k0 = st * kStageElems;
-#pragma unroll
-    for (int i = 0; i < kMaxW; ++i) {
-      const int v = threadIdx.x + i * kRouterThreads;
-      u32x4_t r = {0u, 0u, 0u, 0u};
-      if (vec_ok && v < nvec) {
-        const int vpr = E / kPer16;
-        const int kk = v / vpr;
-        if (k0 + kk < d) r = ld16(Wg + static_cast<int64_t>(k0 + kk) * E + (v % vpr) * kPer16);
-      }
-      wreg[i] = r;
-    }
-  };
-  auto store_w = [&](int st) {
-    const int k0 = st * kStageElems;
-    if (vec_ok) {
-      const int vpr = E / kPer16;
-#pragma unroll
-      for (int i = 0; i < kMaxW; ++i) {
-        const int v = threadIdx.x + i * kRouterThreads;
-        if (v < nvec) {
-          const int kk = v / vpr;
-          const int e0 = (v % vpr) * kPer16;
-          const T* src = reinterpret_cast<const T*>(&wreg[i]);
-#pragma unroll
-          for (int q = 0; q < kPer16; ++q)
-            reinterpret_cast<T*>(sW + (e0 + q) * kSwRowBytes)[kk] = src[q];
-        }
-      }
-    } else {
-      for (int v = threadIdx.x; v < nvec; v += kRouterThreads) {
-        const int kk = v / E;
-        const int e = v % E;
-        T val = (k0 + kk < d) ? Wg[static_cast<int64_t>(k0 + kk) * E + e] : T(0);
-        reinterpret_cast<T*>(sW + e * kSwRowBytes)[kk] = val;
-      }
-    }
-  };
-
-  f32x4_t acc[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  u32x4_t xa[4], xb[4];
-  load_x(0, xa);
-  load_w(0);
-  for (int st = 0; st < nstages; ++st) {
-    __syncthreads();
-    store_w(st);
-    __syncthreads();
-    if (st + 1 < nstages) {
-      load_x(st + 1, xb);
-      load_w(st + 1);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const u32x4_t b = *reinterpret_cast<const u32x4_t*>(sW + (t * 16 + n) * kSwRowBytes + (grp * 4 + j) * 16);
-        acc[t] = RouterMma<T>::run(xa[j], b, acc[t]);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) xa[j] = xb[j];
-  }
-
-  // acc[t][i] is the logit of token row grp*4+i and expert t*16+n.
+  const int n = lane & 15;
+  const int grp = lane >> 4;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int e = t * 16 + n;
@@ -162,7 +70,6 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[t][i] = (e < E) ? acc[t][i] + b : -INFINITY;
   }
-
   for (int s = 0; s < k; ++s) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -183,53 +90,281 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(
           if (t == (bi >> 4)) acc[t][i] = -INFINITY;
       }
       if (n == 0) {
-        sel_val[wave][grp * 4 + i][s] = bv;
-        sel_id[wave][grp * 4 + i][s] = bi;
+        sel_val[(grp * 4 + i) * kMaxExperts + s] = bv;
+        sel_id[(grp * 4 + i) * kMaxExperts + s] = bi;
       }
     }
   }
   __builtin_amdgcn_wave_barrier();
-  __syncthreads();
-
-  for (int idx = lane; idx < kTokPerWave * k; idx += kWave) {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  for (int idx = lane; idx < 16 * k; idx += kWave) {
     const int row = idx / k;
     const int s = idx % k;
     const int tok = tok0 + row;
     if (tok >= T_tokens) continue;
-    const float l0 = sel_val[wave][row][0];
+    const float* v = sel_val + row * kMaxExperts;
+    const float l0 = v[0];
     float den = 0.f;
-    for (int j = 0; j < k; ++j) den += expf(sel_val[wave][row][j] - l0);
+    for (int j = 0; j < k; ++j) den += expf(v[j] - l0);
     const int64_t o = static_cast<int64_t>(tok) * k + s;
-    topk_ids[o] = sel_id[wave][row][s];
-    topk_w[o] = expf(sel_val[wave][row][s] - l0) / den;
+    topk_ids[o] = sel_id[row * kMaxExperts + s];
+    topk_w[o] = expf(v[s] - l0) / den;
   }
 }
 
-template <typename T>
-hipError_t launch_router_t(const T* X, const T* Wg, const float* bias, int T_tokens, int d, int E, int k,
-                           int32_t* ids, float* w, hipStream_t stream) {
-  const int tok_per_block = kRouterWaves * kTokPerWave;
-  const dim3 grid((T_tokens + tok_per_block - 1) / tok_per_block);
-  const int nt = (E + 15) / 16;
-  switch (nt) {
-    case 1: hipLaunchKernelGGL((router_kernel<T, 1>), grid, dim3(kRouterThreads), 0, stream, X, Wg, bias, T_tokens, d, E, k, ids, w); break;
-    case 2: hipLaunchKernelGGL((router_kernel<T, 2>), grid, dim3(kRouterThreads), 0, stream, X, Wg, bias, T_tokens, d, E, k, ids, w); break;
-    case 3: hipLaunchKernelGGL((router_kernel<T, 3>), grid, dim3(kRouterThreads), 0, stream, X, Wg, bias, T_tokens, d, E, k, ids, w); break;
-    default: hipLaunchKernelGGL((router_kernel<T, 4>), grid, dim3(kRouterThreads), 0, stream, X, Wg, bias, T_tokens, d, E, k, ids, w); break;
+// WgT[e][k] = W_g[k][e] for e < E, 0 for E <= e < 16*NT.  One block per 32
+// rows of k: the rows are read with 16-byte loads (a run of 32 rows of W_g is
+// contiguous) and written back as 16-byte runs of 8 (bf16) or 4 (fp32) k.
+template <typename T, int NT>
+__global__ __launch_bounds__(256) void gate_transpose_kernel(const T* __restrict__ Wg, int d, int E,
+                                                             T* __restrict__ WgT) {
+  constexpr int kCols = NT * 16;
+  constexpr int kRows = 32;
+  constexpr int kPer16 = 16 / sizeof(T);
+  __shared__ T tile[kRows][kCols + 2];
+  const int k0 = blockIdx.x * kRows;
+  const T* src = Wg + static_cast<int64_t>(k0) * E;  // kRows * E contiguous elements (d % 64 == 0)
+  if (E % kPer16 == 0) {
+    for (int v = threadIdx.x; v < kRows * E / kPer16; v += 256) {
+      const u32x4_t x = ld16(src + v * kPer16);
+      const T* xe = reinterpret_cast<const T*>(&x);
+      const int flat = v * kPer16;
+#pragma unroll
+      for (int q = 0; q < kPer16; ++q) tile[(flat + q) / E][(flat + q) % E] = xe[q];
+    }
+  } else {
+    for (int i = threadIdx.x; i < kRows * E; i += 256) tile[i / E][i % E] = src[i];
   }
+  for (int i = threadIdx.x; i < kRows * (kCols - E); i += 256) tile[i / (kCols - E)][E + i % (kCols - E)] = T(0);
+  __syncthreads();
+  for (int i = threadIdx.x; i < kCols * (kRows / kPer16); i += 256) {
+    const int e = i / (kRows / kPer16);
+    const int c = i % (kRows / kPer16);
+    u32x4_t v;
+    T* ve = reinterpret_cast<T*>(&v);
+#pragma unroll
+    for (int q = 0; q < kPer16; ++q) ve[q] = tile[c * kPer16 + q][e];
+    st16(WgT + static_cast<int64_t>(e) * d + k0 + c * kPer16, v);
+  }
+}
+
+// Partial (or complete) logits of 32 tokens x all experts over K range
+// [kbeg, kend) of split blockIdx.y.  partial == nullptr: finish with top-k.
+template <typename T, int NT>
+__global__ __launch_bounds__(kRouterThreads) void router_kernel(
+    const T* __restrict__ X, const T* __restrict__ WgT, const float* __restrict__ bias, int T_tokens, int d, int E,
+    int k, int split_len, float* __restrict__ partial, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w) {
+  constexpr int kStepElems = kChunkBytes / sizeof(T);  // K per k-step (32 bf16 / 16 fp32)
+  __shared__ f32x4_t red[4][kRowTiles][NT][kWave];
+  __shared__ float sel_val[2][16 * kMaxExperts];
+  __shared__ int sel_id[2][16 * kMaxExperts];
+
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int n = lane & 15;
+  const int grp = lane >> 4;
+  const int tok0 = blockIdx.x * kRouterTok;
+  const int kbeg = blockIdx.y * split_len;
+  const int kend = min(d, kbeg + split_len);
+
+  // Row pointers of the two row tiles (rows past T repeat the last token; never stored).
+  const unsigned char* xrow[kRowTiles];
+#pragma unroll
+  for (int r = 0; r < kRowTiles; ++r)
+    xrow[r] = reinterpret_cast<const unsigned char*>(X + static_cast<int64_t>(min(tok0 + r * 16 + n, T_tokens - 1)) * d) +
+              grp * 16;
+  const unsigned char* wrow[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    wrow[t] = reinterpret_cast<const unsigned char*>(WgT + static_cast<int64_t>(t * 16 + n) * d) + grp * 16;
+
+  f32x4_t acc[kRowTiles][NT];
+#pragma unroll
+  for (int r = 0; r < kRowTiles; ++r)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // This wave's quarter of [kbeg, kend), in k-steps of kStepElems.
+  const int nsteps = (kend - kbeg) / kStepElems;
+  const int s_lo = wave * nsteps / 4;
+  const int s_hi = (wave + 1) * nsteps / 4;
+  constexpr int kUnroll = NT <= 2 ? 8 : 4;  // 16-byte loads in flight per lane: kUnroll * (2 + NT)
+  int st = s_lo;
+  for (; st + kUnroll <= s_hi; st += kUnroll) {
+    u32x4_t a[kUnroll][kRowTiles], b[kUnroll][NT];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t off = static_cast<int64_t>(kbeg + (st + u) * kStepElems) * sizeof(T);
+#pragma unroll
+      for (int r = 0; r < kRowTiles; ++r) a[u][r] = ld16(xrow[r] + off);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) b[u][t] = ld16(wrow[t] + off);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < kRowTiles; ++r) acc[r][t] = RouterMma<T>::run(a[u][r], b[u][t], acc[r][t]);
+  }
+  for (; st < s_hi; ++st) {
+    const int64_t off = static_cast<int64_t>(kbeg + st * kStepElems) * sizeof(T);
+    u32x4_t a[kRowTiles];
+#pragma unroll
+    for (int r = 0; r < kRowTiles; ++r) a[r] = ld16(xrow[r] + off);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const u32x4_t b = ld16(wrow[t] + off);
+#pragma unroll
+      for (int r = 0; r < kRowTiles; ++r) acc[r][t] = RouterMma<T>::run(a[r], b, acc[r][t]);
+    }
+  }
+
+  // Sum the 4 waves' partial tiles (fixed order: wave 0 + 1 + 2 + 3).
+#pragma unroll
+  for (int r = 0; r < kRowTiles; ++r)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) red[wave][r][t][lane] = acc[r][t];
+  __syncthreads();
+  if (wave >= kRowTiles) return;
+  const int r = wave;  // wave r finishes row tile r
+  f32x4_t sum[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    sum[t] = red[0][r][t][lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) sum[t] += red[w][r][t][lane];
+  }
+  const int rtok0 = tok0 + r * 16;
+  if (partial != nullptr) {
+    // partial[split][token][e]
+    float* out = partial + static_cast<int64_t>(blockIdx.y) * T_tokens * E;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int e = t * 16 + n;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = rtok0 + grp * 4 + i;
+        if (e < E && tok < T_tokens) out[static_cast<int64_t>(tok) * E + e] = sum[t][i];
+      }
+    }
+    return;
+  }
+  topk_tile<NT>(sum, bias, E, k, rtok0, T_tokens, sel_val[r], sel_id[r], topk_ids, topk_w);
+}
+
+// Sum the K-split partial logits in split order, then top-k.  A block of 256
+// threads owns 16 tokens: every thread sums a few (token, expert) entries with
+// independent loads, the sums meet in LDS, and wave 0 selects.
+template <int NT>
+__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ partial, int nsplit,
+                                                          const float* __restrict__ bias, int T_tokens, int E, int k,
+                                                          int32_t* __restrict__ topk_ids,
+                                                          float* __restrict__ topk_w) {
+  __shared__ float logit[16][kMaxExperts];
+  __shared__ float sel_val[16 * kMaxExperts];
+  __shared__ int sel_id[16 * kMaxExperts];
+  const int tok0 = blockIdx.x * 16;
+  for (int p = threadIdx.x; p < 16 * E; p += 256) {
+    const int r = p / E;
+    const int e = p % E;
+    const int tok = tok0 + r;
+    float v = 0.f;
+    if (tok < T_tokens) {
+      const float* src = partial + static_cast<int64_t>(tok) * E + e;
+      const int64_t stride = static_cast<int64_t>(T_tokens) * E;
+      int s = 0;
+      for (; s + 4 <= nsplit; s += 4) {
+        const float a0 = src[(s + 0) * stride], a1 = src[(s + 1) * stride];
+        const float a2 = src[(s + 2) * stride], a3 = src[(s + 3) * stride];
+        v += ((a0 + a1) + (a2 + a3));
+      }
+      for (; s < nsplit; ++s) v += src[s * stride];
+    }
+    logit[r][e] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x >= kWave) return;
+  const int lane = threadIdx.x;
+  const int n = lane & 15;
+  const int grp = lane >> 4;
+  f32x4_t acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int e = t * 16 + n;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[t][i] = (e < E) ? logit[grp * 4 + i][e] : 0.f;
+  }
+  topk_tile<NT>(acc, bias, E, k, tok0, T_tokens, sel_val, sel_id, topk_ids, topk_w);
+}
+
+// K per split: the whole d when there are enough token blocks, else d split
+// into pieces of at least 256 so roughly 256 blocks run.
+int split_len_of(int T_tokens, int d) {
+  const int tok_blocks = (T_tokens + kRouterTok - 1) / kRouterTok;
+  if (tok_blocks >= 128 || d <= 256) return d;
+  int want = (256 + tok_blocks - 1) / tok_blocks;
+  const int max_splits = d / 256;
+  if (want > max_splits) want = max_splits;
+  if (want <= 1) return d;
+  int len = (d + want - 1) / want;
+  len = (len + 127) / 128 * 128;  // whole k-steps for every wave
+  return len;
+}
+
+size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+size_t gate_t_bytes(int d, int E, size_t esize) { return align256(static_cast<size_t>((E + 15) / 16) * 16 * d * esize); }
+
+template <typename T, int NT>
+hipError_t launch_nt(const T* X, const T* Wg, const float* bias, int T_tokens, int d, int E, int k, int32_t* ids,
+                     float* w, unsigned char* scratch, hipStream_t stream) {
+  T* WgT = reinterpret_cast<T*>(scratch);
+  float* partial = reinterpret_cast<float*>(scratch + gate_t_bytes(d, E, sizeof(T)));
+  const int split_len = split_len_of(T_tokens, d);
+  const int nsplit = (d + split_len - 1) / split_len;
+  hipLaunchKernelGGL((gate_transpose_kernel<T, NT>), dim3(d / 32), dim3(256), 0, stream, Wg, d, E, WgT);
+  const dim3 grid((T_tokens + kRouterTok - 1) / kRouterTok, nsplit);
+  hipLaunchKernelGGL((router_kernel<T, NT>), grid, dim3(kRouterThreads), 0, stream, X, WgT, bias, T_tokens, d, E, k,
+                     split_len, nsplit > 1 ? partial : nullptr, ids, w);
+  if (nsplit > 1)
+    hipLaunchKernelGGL((router_topk_kernel<NT>), dim3((T_tokens + 15) / 16), dim3(256), 0, stream, partial, nsplit,
+                       bias, T_tokens, E, k, ids, w);
   return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_t(const T* X, const T* Wg, const float* bias, int T_tokens, int d, int E, int k, int32_t* ids,
+                    float* w, unsigned char* scratch, hipStream_t stream) {
+  switch ((E + 15) / 16) {
+    case 1: return launch_nt<T, 1>(X, Wg, bias, T_tokens, d, E, k, ids, w, scratch, stream);
+    case 2: return launch_nt<T, 2>(X, Wg, bias, T_tokens, d, E, k, ids, w, scratch, stream);
+    case 3: return launch_nt<T, 3>(X, Wg, bias, T_tokens, d, E, k, ids, w, scratch, stream);
+    default: return launch_nt<T, 4>(X, Wg, bias, T_tokens, d, E, k, ids, w, scratch, stream);
+  }
 }
 
 }  // namespace
 
-hipError_t launch_router(int dtype, const void* X, const void* Wg, const float* bias, int T_tokens, int d,
-                         int E, int k, int32_t* ids, float* w, hipStream_t stream) {
+size_t router_scratch_bytes(int T_tokens, int d, int E, int dtype) {
+  if (T_tokens <= 0) return 0;
+  const size_t esize = dtype == kDtypeBF16 ? 2 : 4;
+  const int split_len = split_len_of(T_tokens, d);
+  const int nsplit = (d + split_len - 1) / split_len;
+  size_t b = gate_t_bytes(d, E, esize);
+  if (nsplit > 1) b += static_cast<size_t>(nsplit) * T_tokens * E * sizeof(float);
+  return b;
+}
+
+hipError_t launch_router(int dtype, const void* X, const void* Wg, const float* bias, int T_tokens, int d, int E,
+                         int k, int32_t* ids, float* w, void* scratch, hipStream_t stream) {
   if (T_tokens <= 0) return hipSuccess;
+  unsigned char* sc = static_cast<unsigned char*>(scratch);
   if (dtype == kDtypeBF16)
-    return launch_router_t(static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(Wg), bias, T_tokens, d, E,
-                           k, ids, w, stream);
-  return launch_router_t(static_cast<const float*>(X), static_cast<const float*>(Wg), bias, T_tokens, d, E, k, ids,
-                         w, stream);
+    return launch_t(static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(Wg), bias, T_tokens, d, E, k, ids,
+                    w, sc, stream);
+  return launch_t(static_cast<const float*>(X), static_cast<const float*>(Wg), bias, T_tokens, d, E, k, ids, w, sc,
+                  stream);
 }
 
 }  // namespace moe

@@ -45,13 +45,22 @@ class ForwardBuffers:
                            device=device),
         )
 
+    def scratch_view(self, cfg: _lib.MoeConfig, name: str) -> torch.Tensor:
+        """The router ("route") or dispatcher ("dispatch") scratch inside the forward workspace."""
+        a = lambda b: (b + 255) // 256 * 256  # noqa: E731
+        r = _lib.moe_workspace_size(cfg, _lib.MOE_OP_ROUTE)
+        d = _lib.moe_workspace_size(cfg, _lib.MOE_OP_DISPATCH)
+        if name == "route":
+            return self.ws[:max(r, 1)]
+        return self.ws[a(r):a(r) + max(d, 1)]
+
     def workspace_view(self, cfg: _lib.MoeConfig, name: str) -> torch.Tensor:
         """Xp, H or Yp as a tensor view into the forward workspace (the layout moe_forward uses:
-        dispatch scratch, then Xp, H, Yp, each 256-byte aligned)."""
+        router scratch, dispatch scratch, then Xp, H, Yp, each 256-byte aligned)."""
         T, d, F, k = cfg.num_tokens, cfg.hidden_size, cfg.intermediate_size, cfg.num_experts_per_tok
         es = 2 if cfg.dtype == _lib.MOE_BF16 else 4
         a = lambda b: (b + 255) // 256 * 256  # noqa: E731
-        disp = a(_lib.moe_workspace_size(cfg, _lib.MOE_OP_DISPATCH))
+        disp = a(_lib.moe_workspace_size(cfg, _lib.MOE_OP_ROUTE)) + a(_lib.moe_workspace_size(cfg, _lib.MOE_OP_DISPATCH))
         xp = a(T * k * d * es)
         h = a(T * k * F * es)
         start, cols = {"Xp": (disp, d), "H": (disp + xp, F), "Yp": (disp + xp + h, d)}[name]

@@ -114,6 +114,19 @@ def test_workspace_too_small_rejected():
     assert ei.value.status == moe.MOE_ERR_WORKSPACE_TOO_SMALL
 
 
+def test_route_workspace():
+    # small T with a large hidden size splits the gate projection over K
+    cfg = moe.config(8, 3584, 2560, 64, 2, -1, "bf16")
+    need = moe.moe_workspace_size(cfg, moe.MOE_OP_ROUTE)
+    gate_t = 64 * 3584 * 2
+    assert need > gate_t and (need - gate_t) % (8 * 64 * 4) == 0
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_route(cfg, 1, 1, None, 1, 1, 1, need - 1, stream=0)
+    assert ei.value.status == moe.MOE_ERR_WORKSPACE_TOO_SMALL
+    # plenty of tokens: one pass, only the transposed gate
+    assert moe.moe_workspace_size(moe.config(8192, 2048, 5632, 32, 2), moe.MOE_OP_ROUTE) == 32 * 2048 * 2
+
+
 def test_workspace_sizes():
     T, d, F, E, k = 8192, 2048, 5632, 32, 2
     cfg = moe.config(T, d, F, E, k, -1, "bf16")

@@ -26,6 +26,11 @@ CASES = [
     ("single_token", 1, 128, 8, 2, 128, "bf16", -1, 0.0),
     ("cap_zero", 70, 128, 8, 2, 128, "bf16", 0, 0.0),
     ("cap_tight_f32", 129, 64, 4, 2, 64, "f32", 20, 1.0),
+    ("decode_like_splitk", 8, 1024, 64, 2, 256, "bf16", -1, 0.0),
+    ("splitk_e24_f32", 40, 768, 24, 3, 128, "f32", -1, 0.2),
+    ("skinny_64rows", 64, 256, 2, 1, 192, "bf16", -1, 0.0),
+    ("skinny_33rows", 33, 320, 4, 2, 448, "bf16", -1, 0.3),
+    ("skinny_cap", 60, 128, 8, 3, 128, "bf16", 9, 0.5),
 ]
 IDS = [c[0] for c in CASES]
 
@@ -50,7 +55,8 @@ def test_route(case):
     bias = to_dev(inp.bias, "f32")
     ids = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
     tw = torch.empty((w.T, w.k), dtype=torch.float32, device="cuda")
-    moe.moe_route(cfg, X, Wg, bias, ids, tw)
+    rws = torch.empty(max(1, moe.moe_workspace_size(cfg, moe.MOE_OP_ROUTE)), dtype=torch.uint8, device="cuda")
+    moe.moe_route(cfg, X, Wg, bias, ids, tw, rws)
     torch.cuda.synchronize()
     r = oracle.route(oracle.as_f64(inp.X, w.dtype), oracle.as_f64(inp.Wg, w.dtype), inp.bias, w.k)
     check_routing(ids.cpu().numpy(), tw.cpu().numpy(), r)
