@@ -248,6 +248,161 @@ __global__ __launch_bounds__(kScatterThreads) void dispatch_scatter_kernel(
   }
 }
 
+// Small T (<= 256 tokens, k <= 8): the whole dispatch in one block of 4
+// waves, one 64-token chunk per wave -- histogram, scans, capacity cut,
+// ranks, perm/inv_perm and the row copy -- so decode pays one launch.
+constexpr int kSmallMaxT = 4 * kDispatchChunk;
+constexpr int kSmallMaxK = 8;
+
+template <typename T, bool kCap>
+__global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __restrict__ ids, const T* __restrict__ X,
+                                                             int T_tok, int d, int E, int k, int capacity,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ perm,
+                                                             int32_t* __restrict__ inv_perm, T* __restrict__ Xp) {
+  // per chunk, per (slot, expert): pairs, then exclusive prefix over chunks
+  __shared__ int s_cnt[4][kSmallMaxK * kMaxExperts];
+  __shared__ int s_slot_base[kSmallMaxK * kMaxExperts];  // capacity: pairs of e in slots < s
+  __shared__ int s_kept[4][kMaxExperts];                 // kept pairs per chunk/expert, then prefix
+  __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int s_row[kSmallMaxT][kSmallMaxK];
+  const int lane = threadIdx.x % kWave;
+  const int chunk = threadIdx.x / kWave;
+  const int t = chunk * kDispatchChunk + lane;
+  const uint64_t below = (1ull << lane) - 1ull;
+  const int cols = k * E;
+
+  for (int i = threadIdx.x; i < 4 * kSmallMaxK * kMaxExperts; i += 256) (&s_cnt[0][0])[i] = 0;
+  for (int i = threadIdx.x; i < 4 * kMaxExperts; i += 256) (&s_kept[0][0])[i] = 0;
+  __syncthreads();
+  int e[kSmallMaxK];
+#pragma unroll
+  for (int s = 0; s < kSmallMaxK; ++s) {
+    e[s] = kNone;
+    if (s < k) {
+      e[s] = load_id(ids, t, T_tok, k, s, E);
+      if (e[s] != kNone) atomicAdd(&s_cnt[chunk][s * E + e[s]], 1);
+    }
+  }
+  __syncthreads();
+  // exclusive prefix over the 4 chunks per column; column totals
+  for (int c = threadIdx.x; c < cols; c += 256) {
+    int acc = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int v = s_cnt[q][c];
+      s_cnt[q][c] = acc;
+      acc += v;
+    }
+    s_slot_base[c] = acc;  // column total for now
+  }
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    // per expert: routed count, slot bases (capacity), kept count, offsets (one wave scan)
+    const int ex = lane;
+    int n = 0, kept = 0;
+    if (ex < E) {
+      for (int s = 0; s < k; ++s) {
+        const int tot = s_slot_base[s * E + ex];
+        s_slot_base[s * E + ex] = n;
+        n += tot;
+      }
+      counts[ex] = n;
+      kept = kCap ? min(n, capacity) : n;
+    }
+    int incl = kept;
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) {
+      const int o = __shfl_up(incl, m);
+      if (lane >= m) incl += o;
+    }
+    if (ex < E) s_off[ex] = incl - kept;
+    if (ex == E - 1) s_off[E] = incl;
+  }
+  __syncthreads();
+  if (kCap) {
+    // keep flags by (slot, token) priority; dropped pairs become kNone
+#pragma unroll
+    for (int s = 0; s < kSmallMaxK; ++s) {
+      if (s < k) {
+        const Ballots B = ballots_of(e[s]);
+        if (e[s] != kNone) {
+          const int prio = s_slot_base[s * E + e[s]] + s_cnt[chunk][s * E + e[s]] + __popcll(match(B, e[s]) & below);
+          if (prio < capacity) atomicAdd(&s_kept[chunk][e[s]], 1);
+          else e[s] = kNone;
+        }
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < E) {
+      int acc = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int v = s_kept[q][threadIdx.x];
+        s_kept[q][threadIdx.x] = acc;
+        acc += v;
+      }
+    }
+  } else {
+    // dropless: the chunk base of expert e is the prefix of all slots' counts
+    __syncthreads();
+    if (threadIdx.x < E) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        int acc = 0;
+        for (int s = 0; s < k; ++s) acc += s_cnt[q][s * E + threadIdx.x];
+        s_kept[q][threadIdx.x] = acc;
+      }
+    }
+  }
+  __syncthreads();
+  // ranks within the chunk, in (token, slot) order per expert
+  int cnt[kSmallMaxK];
+#pragma unroll
+  for (int s = 0; s < kSmallMaxK; ++s) cnt[s] = 0;
+#pragma unroll
+  for (int s2 = 0; s2 < kSmallMaxK; ++s2) {
+    if (s2 < k) {
+      const Ballots B = ballots_of(e[s2]);
+#pragma unroll
+      for (int s = 0; s < kSmallMaxK; ++s)
+        if (s < k) cnt[s] += __popcll(match(B, e[s]) & below);
+    }
+  }
+  const int Tk = T_tok * k;
+#pragma unroll
+  for (int s = 0; s < kSmallMaxK; ++s) {
+    if (s < k && t < T_tok) {
+      int row = -1;
+      if (e[s] != kNone) {
+        int same = 0;
+#pragma unroll
+        for (int s2 = 0; s2 < kSmallMaxK; ++s2)
+          if (s2 < s && e[s2] == e[s]) ++same;
+        row = s_off[e[s]] + s_kept[chunk][e[s]] + cnt[s] + same;
+        if (row < 0 || row >= Tk) row = -1;  // unreachable for consistent counts; keeps stores in bounds
+        if (row >= 0) perm[row] = t * k + s;
+      }
+      inv_perm[t * k + s] = row;
+      s_row[t][s] = row;
+    }
+  }
+  if (threadIdx.x <= E) offsets[threadIdx.x] = s_off[threadIdx.x];
+  for (int r = s_off[E] + threadIdx.x; r < Tk; r += 256) perm[r] = -1;
+  __syncthreads();
+  const int nvec = d * static_cast<int>(sizeof(T)) / 16;
+  for (int idx = threadIdx.x; idx < T_tok * nvec; idx += 256) {
+    const int tt = idx / nvec;
+    const int v = idx % nvec;
+    const u32x4_t val = ld16(reinterpret_cast<const unsigned char*>(X + static_cast<int64_t>(tt) * d) + v * 16);
+    for (int s = 0; s < k; ++s) {
+      const int row = s_row[tt][s];
+      if (row >= 0) st16(reinterpret_cast<unsigned char*>(Xp + static_cast<int64_t>(row) * d) + v * 16, val);
+    }
+  }
+}
+
 template <typename T, int KMAX>
 hipError_t launch_scatter_k(bool cap, int nblocks, const int32_t* ids, const T* X, int T_tok, int d, int E, int k,
                             const int32_t* cb, const int32_t* offsets, const int8_t* keep, int32_t* perm,
@@ -308,6 +463,28 @@ hipError_t launch_dispatch(int dtype, const int32_t* ids, const void* X, int T, 
   const bool cap = capacity >= 0;
   const int nchunks = (T + kDispatchChunk - 1) / kDispatchChunk;
   const int total_pairs = T * k;
+  if (T > 0 && T <= kSmallMaxT && k <= kSmallMaxK) {
+    if (dtype == kDtypeBF16) {
+      if (cap)
+        hipLaunchKernelGGL((dispatch_small_kernel<uint16_t, true>), dim3(1), dim3(256), 0, stream, ids,
+                           static_cast<const uint16_t*>(X), T, d, E, k, capacity, counts, offsets, perm, inv_perm,
+                           static_cast<uint16_t*>(Xp));
+      else
+        hipLaunchKernelGGL((dispatch_small_kernel<uint16_t, false>), dim3(1), dim3(256), 0, stream, ids,
+                           static_cast<const uint16_t*>(X), T, d, E, k, capacity, counts, offsets, perm, inv_perm,
+                           static_cast<uint16_t*>(Xp));
+    } else {
+      if (cap)
+        hipLaunchKernelGGL((dispatch_small_kernel<float, true>), dim3(1), dim3(256), 0, stream, ids,
+                           static_cast<const float*>(X), T, d, E, k, capacity, counts, offsets, perm, inv_perm,
+                           static_cast<float*>(Xp));
+      else
+        hipLaunchKernelGGL((dispatch_small_kernel<float, false>), dim3(1), dim3(256), 0, stream, ids,
+                           static_cast<const float*>(X), T, d, E, k, capacity, counts, offsets, perm, inv_perm,
+                           static_cast<float*>(Xp));
+    }
+    return hipGetLastError();
+  }
   if (T <= 0) {
     // No tokens: every expert is empty.
     hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, sc.chunk_base, 0, E,

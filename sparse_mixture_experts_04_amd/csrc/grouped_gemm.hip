@@ -535,30 +535,31 @@ hipError_t launch_big(const uint16_t* A, const uint16_t* B, uint16_t* C, const i
 
 // ---------------------------------------------------------------------------
 // Skinny variant for few rows per expert (decode: a handful of tokens), where
-// the layer is bound by streaming each active expert's weights once.  A wave
-// owns 32 weight rows (two 16-row MFMA A tiles) over the whole K and up to 64
-// of the expert's token rows (up to four 16-column B tiles), so every weight
-// byte is loaded exactly once, by one lane, with 8 k-steps of loads in flight.
-// The result tile is transposed (weights on rows): a lane holds 4 consecutive
-// output columns of one token row.  Waves map to (active expert, 32-row tile)
-// on the device; waves past the end exit.
-constexpr int kSkinnyRows = 32;          // weight rows per wave
+// the layer is bound by streaming each active expert's weights once.  A
+// one-wave block owns 16 weight rows (one 16-row MFMA A tile) over the whole
+// K and up to 64 of the expert's token rows (up to four 16-column B tiles),
+// so every weight byte is loaded exactly once, with 8 k-steps of loads in
+// flight per lane.  Small blocks keep the per-CU work even when the number of
+// (expert, row tile) pairs is not a multiple of the CU count.  The result tile
+// is transposed (weights on rows): a lane holds 4 consecutive output columns
+// of one token row.  Blocks map to (active expert, 16-row tile) on the
+// device; blocks past the end exit.
+constexpr int kSkinnyRows = 16;          // weight rows per wave
 constexpr int kSkinnyMaxTok = 64;        // token rows per expert this kernel handles
 constexpr int kSkinnyUnroll = 8;
 
 template <bool kGelu, int kGroups>
-__global__ __launch_bounds__(256) void grouped_gemm_bf16_skinny(const uint16_t* __restrict__ A,
-                                                                const uint16_t* __restrict__ B,
-                                                                uint16_t* __restrict__ C,
-                                                                const int32_t* __restrict__ offsets, int E, int N,
-                                                                int K, int max_rows) {
+__global__ __launch_bounds__(kWave) void grouped_gemm_bf16_skinny(const uint16_t* __restrict__ A,
+                                                                  const uint16_t* __restrict__ B,
+                                                                  uint16_t* __restrict__ C,
+                                                                  const int32_t* __restrict__ offsets, int E, int N,
+                                                                  int K, int max_rows) {
   __shared__ int s_tile_base[kMaxExperts + 1];
   __shared__ int s_seg0[kMaxExperts];
   __shared__ int s_seg1[kMaxExperts];
-  const int lane = threadIdx.x % kWave;
-  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x;
   const int n_tiles = (N + kSkinnyRows - 1) / kSkinnyRows;
-  if (threadIdx.x < kWave) {
+  {
     const int e = lane;
     int nt = 0, seg0 = 0, seg1 = 0;
     if (e < E) {
@@ -580,7 +581,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_skinny(const uint16_t* 
     if (e == 0) s_tile_base[0] = 0;
   }
   __syncthreads();
-  const int tile = blockIdx.x * 4 + wave;
+  const int tile = blockIdx.x;
   if (tile >= s_tile_base[E]) return;
   int e = 0;
   while (e + 1 < E && s_tile_base[e + 1] <= tile) ++e;
@@ -592,32 +593,26 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_skinny(const uint16_t* 
   const int r16 = lane & 15;
   const int g = lane >> 4;  // 16-byte chunk of a 64-byte k-step
   const int64_t stride = static_cast<int64_t>(K) * 2;
-  const unsigned char* wp[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-    wp[i] = reinterpret_cast<const unsigned char*>(B) + (static_cast<int64_t>(e) * N + min(n0 + i * 16 + r16, N - 1)) * stride +
-            g * 16;
+  const unsigned char* wp = reinterpret_cast<const unsigned char*>(B) +
+                            (static_cast<int64_t>(e) * N + min(n0 + r16, N - 1)) * stride + g * 16;
   const unsigned char* xp[kGroups];
 #pragma unroll
   for (int j = 0; j < kGroups; ++j)
     xp[j] = reinterpret_cast<const unsigned char*>(A) + static_cast<int64_t>(seg0 + min(j * 16 + r16, rows - 1)) * stride +
             g * 16;
 
-  f32x4_t acc[2][kGroups];
+  f32x4_t acc[kGroups];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < kGroups; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < kGroups; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int steps = K / 32;  // 64 bytes of K per step
   int st = 0;
   for (; st + kSkinnyUnroll <= steps; st += kSkinnyUnroll) {
-    u32x4_t wa[kSkinnyUnroll][2], xb[kSkinnyUnroll][kGroups];
+    u32x4_t wa[kSkinnyUnroll], xb[kSkinnyUnroll][kGroups];
 #pragma unroll
     for (int u = 0; u < kSkinnyUnroll; ++u) {
       const int64_t off = static_cast<int64_t>(st + u) * 64;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) wa[u][i] = ld16(wp[i] + off);
+      wa[u] = ld16(wp + off);
 #pragma unroll
       for (int j = 0; j < kGroups; ++j)
         if (j < groups) xb[u][j] = ld16(xp[j] + off);
@@ -626,43 +621,33 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_skinny(const uint16_t* 
     for (int u = 0; u < kSkinnyUnroll; ++u)
 #pragma unroll
       for (int j = 0; j < kGroups; ++j)
-        if (j < groups) {
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wa[u][i]),
-                                                                __builtin_bit_cast(bf16x8_t, xb[u][j]), acc[i][j], 0, 0, 0);
-        }
+        if (j < groups)
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wa[u]),
+                                                           __builtin_bit_cast(bf16x8_t, xb[u][j]), acc[j], 0, 0, 0);
   }
   for (; st < steps; ++st) {
     const int64_t off = static_cast<int64_t>(st) * 64;
-    u32x4_t wa[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) wa[i] = ld16(wp[i] + off);
+    const u32x4_t wa = ld16(wp + off);
 #pragma unroll
     for (int j = 0; j < kGroups; ++j)
       if (j < groups) {
         const u32x4_t xb = ld16(xp[j] + off);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wa[i]),
-                                                              __builtin_bit_cast(bf16x8_t, xb), acc[i][j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wa),
+                                                         __builtin_bit_cast(bf16x8_t, xb), acc[j], 0, 0, 0);
       }
   }
-  // acc[i][j][q]: weight row n0 + i*16 + g*4 + q, token row j*16 + r16.
+  // acc[j][q]: weight row n0 + g*4 + q, token row j*16 + r16.
 #pragma unroll
   for (int j = 0; j < kGroups; ++j) {
     const int tok = j * 16 + r16;
     if (j >= groups || tok >= rows) continue;
-    uint16_t* crow = C + static_cast<int64_t>(seg0 + tok) * N;
+    const int col = n0 + g * 4;
+    if (col >= N) continue;
+    float v[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int col = n0 + i * 16 + g * 4;
-      if (col >= N) continue;
-      float v[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] = kGelu ? gelu_tanh_fast(acc[i][j][q]) : acc[i][j][q];
-      *reinterpret_cast<uint2*>(crow + col) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-    }
+    for (int q = 0; q < 4; ++q) v[q] = kGelu ? gelu_tanh_fast(acc[j][q]) : acc[j][q];
+    *reinterpret_cast<uint2*>(C + static_cast<int64_t>(seg0 + tok) * N + col) =
+        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
   }
 }
 
@@ -671,10 +656,9 @@ hipError_t launch_skinny(const uint16_t* A, const uint16_t* B, uint16_t* C, cons
                          int K, int max_rows, hipStream_t stream) {
   // at most min(E, max_rows) experts have rows
   const int active = max_rows < E ? max_rows : E;
-  const int64_t waves = static_cast<int64_t>(active) * ((N + kSkinnyRows - 1) / kSkinnyRows);
-  const int64_t blocks = (waves + 3) / 4;
-  hipLaunchKernelGGL((grouped_gemm_bf16_skinny<kGelu, kGroups>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, A,
-                     B, C, offsets, E, N, K, max_rows);
+  const int64_t blocks = static_cast<int64_t>(active) * ((N + kSkinnyRows - 1) / kSkinnyRows);
+  hipLaunchKernelGGL((grouped_gemm_bf16_skinny<kGelu, kGroups>), dim3(static_cast<unsigned>(blocks)), dim3(kWave), 0,
+                     stream, A, B, C, offsets, E, N, K, max_rows);
   return hipGetLastError();
 }
 

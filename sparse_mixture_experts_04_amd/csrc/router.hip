@@ -148,12 +148,27 @@ __global__ __launch_bounds__(256) void gate_transpose_kernel(const T* __restrict
   }
 }
 
+// B fragment of k-step `kstep` read straight from W_g [d, E]: lane (n, grp)
+// gathers the kPer16 consecutive k of column col (used when only a few
+// blocks run, so the transpose launch would cost more than the gathers).
+template <typename T>
+__device__ __forceinline__ u32x4_t gather_b(const T* __restrict__ Wg, int E, int col, int k0) {
+  constexpr int kPer16 = 16 / sizeof(T);
+  u32x4_t r;
+  T* re = reinterpret_cast<T*>(&r);
+#pragma unroll
+  for (int q = 0; q < kPer16; ++q) re[q] = col < E ? Wg[static_cast<int64_t>(k0 + q) * E + col] : T(0);
+  return r;
+}
+
 // Partial (or complete) logits of 32 tokens x all experts over K range
 // [kbeg, kend) of split blockIdx.y.  partial == nullptr: finish with top-k.
-template <typename T, int NT>
+// kDirect: B fragments gathered from W_g itself (WgT unused).
+template <typename T, int NT, bool kDirect>
 __global__ __launch_bounds__(kRouterThreads) void router_kernel(
-    const T* __restrict__ X, const T* __restrict__ WgT, const float* __restrict__ bias, int T_tokens, int d, int E,
-    int k, int split_len, float* __restrict__ partial, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w) {
+    const T* __restrict__ X, const T* __restrict__ WgT, const T* __restrict__ Wg, const float* __restrict__ bias,
+    int T_tokens, int d, int E, int k, int split_len, float* __restrict__ partial, int32_t* __restrict__ topk_ids,
+    float* __restrict__ topk_w) {
   constexpr int kStepElems = kChunkBytes / sizeof(T);  // K per k-step (32 bf16 / 16 fp32)
   __shared__ f32x4_t red[4][kRowTiles][NT][kWave];
   __shared__ float sel_val[2][16 * kMaxExperts];
@@ -176,7 +191,8 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(
   const unsigned char* wrow[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
-    wrow[t] = reinterpret_cast<const unsigned char*>(WgT + static_cast<int64_t>(t * 16 + n) * d) + grp * 16;
+    wrow[t] = kDirect ? nullptr
+                      : reinterpret_cast<const unsigned char*>(WgT + static_cast<int64_t>(t * 16 + n) * d) + grp * 16;
 
   f32x4_t acc[kRowTiles][NT];
 #pragma unroll
@@ -198,7 +214,9 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(
 #pragma unroll
       for (int r = 0; r < kRowTiles; ++r) a[u][r] = ld16(xrow[r] + off);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) b[u][t] = ld16(wrow[t] + off);
+      for (int t = 0; t < NT; ++t)
+        b[u][t] = kDirect ? gather_b(Wg, E, t * 16 + n, kbeg + (st + u) * kStepElems + grp * (16 / sizeof(T)))
+                          : ld16(wrow[t] + off);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
@@ -214,7 +232,8 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(
     for (int r = 0; r < kRowTiles; ++r) a[r] = ld16(xrow[r] + off);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const u32x4_t b = ld16(wrow[t] + off);
+      const u32x4_t b = kDirect ? gather_b(Wg, E, t * 16 + n, kbeg + st * kStepElems + grp * (16 / sizeof(T)))
+                                : ld16(wrow[t] + off);
 #pragma unroll
       for (int r = 0; r < kRowTiles; ++r) acc[r][t] = RouterMma<T>::run(a[r], b, acc[r][t]);
     }
@@ -323,10 +342,16 @@ hipError_t launch_nt(const T* X, const T* Wg, const float* bias, int T_tokens, i
   float* partial = reinterpret_cast<float*>(scratch + gate_t_bytes(d, E, sizeof(T)));
   const int split_len = split_len_of(T_tokens, d);
   const int nsplit = (d + split_len - 1) / split_len;
-  hipLaunchKernelGGL((gate_transpose_kernel<T, NT>), dim3(d / 32), dim3(256), 0, stream, Wg, d, E, WgT);
   const dim3 grid((T_tokens + kRouterTok - 1) / kRouterTok, nsplit);
-  hipLaunchKernelGGL((router_kernel<T, NT>), grid, dim3(kRouterThreads), 0, stream, X, WgT, bias, T_tokens, d, E, k,
-                     split_len, nsplit > 1 ? partial : nullptr, ids, w);
+  if (nsplit > 1) {
+    // few token blocks: gather from W_g directly, no transpose launch
+    hipLaunchKernelGGL((router_kernel<T, NT, true>), grid, dim3(kRouterThreads), 0, stream, X, WgT, Wg, bias, T_tokens,
+                       d, E, k, split_len, partial, ids, w);
+  } else {
+    hipLaunchKernelGGL((gate_transpose_kernel<T, NT>), dim3(d / 32), dim3(256), 0, stream, Wg, d, E, WgT);
+    hipLaunchKernelGGL((router_kernel<T, NT, false>), grid, dim3(kRouterThreads), 0, stream, X, WgT, Wg, bias,
+                       T_tokens, d, E, k, split_len, nullptr, ids, w);
+  }
   if (nsplit > 1)
     hipLaunchKernelGGL((router_topk_kernel<NT>), dim3((T_tokens + 15) / 16), dim3(256), 0, stream, partial, nsplit,
                        bias, T_tokens, E, k, ids, w);
