@@ -263,11 +263,14 @@ __device__ __forceinline__ int off_w(int row, int c) {
   return line * 128 + (((((row & 1) << 2) | c) ^ key_w(line)) << 4);
 }
 
-// x * sigmoid(2u) = 0.5 x (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3).
+// x * sigmoid(2u) = 0.5 x (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3),
+// with the hardware exp2 and reciprocal (about 1 ulp each).  Large |x|
+// saturates correctly: exp2 -> inf gives -0, exp2 -> 0 gives x.
 __device__ __forceinline__ float gelu_tanh_fast(float x) {
   const float kSqrt2OverPi = 0.7978845608028654f;
+  const float kMinus2Log2e = -2.0f * 1.4426950408889634f;
   const float u = kSqrt2OverPi * fmaf(0.044715f * x, x * x, x);
-  return __fdividef(x, 1.0f + __expf(-2.0f * u));
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(kMinus2Log2e * u));
 }
 
 template <int N>
@@ -490,15 +493,16 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
     after_epilogue = true;
 
     // acc[i][j][q]: token row m0 + wm*128 + j*32 + frow, column n0 + wn*128 + i*32 + 16*fhalf + q.
+    // Branch-free per group (only the stores are predicated) so the 16
+    // accumulators of one group are read, converted and stored before the next.
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = tc.m0 + wm * 128 + j * 32 + frow;
-      if (row >= tc.seg1) continue;
-      uint16_t* crow = C + static_cast<int64_t>(row) * N;
+      const bool row_ok = row < tc.seg1;
+      uint16_t* crow = C + static_cast<int64_t>(row_ok ? row : tc.m0) * N;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int col = tc.n0 + wn * 128 + i * 32 + 16 * fhalf;
-        if (col >= N) continue;
         float v[16];
 #pragma unroll
         for (int q = 0; q < 16; ++q) v[q] = kGelu ? gelu_tanh_fast(acc[i][j][q]) : acc[i][j][q];
@@ -508,8 +512,11 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
           lo[h] = pack_bf16x2(v[2 * h], v[2 * h + 1]);
           hi[h] = pack_bf16x2(v[8 + 2 * h], v[8 + 2 * h + 1]);
         }
-        st16(crow + col, lo);
-        st16(crow + col + 8, hi);
+        if (row_ok && col < N) {
+          st16(crow + col, lo);
+          st16(crow + col + 8, hi);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
