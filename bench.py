@@ -28,6 +28,34 @@ PEAK_F32_TFLOPS = 157.3     # MI355X fp32 MFMA/vector
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "MoE-layer tokens/sec at 1 GPU; % bf16 MFMA peak (FFN) / % HBM peak (rest)"
 
+# HBM bytes per launch of the expert GEMMs from rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE (KiB per dispatch), scaled by what the same counters read for a
+# plain 1 GiB device copy (FETCH_SIZE x2.0, WRITE_SIZE x1.0); valid only for
+# the GEMM source they were taken on (sha1 prefix), else reported as null.
+TRAFFIC_SOURCE_SHA1 = "a4b2dbc6bb48"
+TRAFFIC_BYTES = {  # (workload, stage) -> (fetch KiB, write KiB) per dispatch, raw counter values
+    ("prefill", "expert_up"): (540435.8, 193243.2),
+    ("prefill", "expert_down"): (711703.8, 65562.2),
+    ("capacity", "expert_up"): (891743.6, 301959.9),
+    ("capacity", "expert_down"): (752908.2, 417563.5),
+    ("skewed", "expert_up"): (9385058.7, 976436.1),
+    ("skewed", "expert_down"): (9011081.1, 262520.5),
+    ("decode", "expert_up"): (123405.9, 80.0),
+    ("decode", "expert_down"): (123581.7, 112.0),
+}
+FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
+
+
+def gemm_traffic(workload, stage):
+    import hashlib
+    src = os.path.join(ROOT, "sparse_mixture_experts_04_amd", "csrc", "grouped_gemm.hip")
+    with open(src, "rb") as f:
+        sha = hashlib.sha1(f.read()).hexdigest()[:12]
+    if sha != TRAFFIC_SOURCE_SHA1 or (workload, stage) not in TRAFFIC_BYTES:
+        return None
+    fetch, write = TRAFFIC_BYTES[(workload, stage)]
+    return round((fetch * FETCH_SCALE + write * WRITE_SCALE) * 1024)
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -39,6 +67,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of one HIP-graph replay of the K steps")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -71,20 +101,33 @@ def cpu_baseline(w, inp, sample):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
+    # Repeat the sample until at least 10 s of CPU work (at most 30 s) is timed.
     t0 = time.perf_counter()
+    toks, reps = 0, 0
     if w.steps > 1:
         n = sample or 4
-        for s in range(n):
-            X = workloads.decode_step_inputs(w, s)
-            oracle.moe_forward(X, inp.Wg, inp.bias, inp.W1, inp.W2, w.k, inp.expert_capacity, w.dtype)
-        toks = n * w.T
-        desc = f"{n} decode steps of {w.T} tokens, full weights"
+        while True:
+            for s in range(n):
+                X = workloads.decode_step_inputs(w, s)
+                oracle.moe_forward(X, inp.Wg, inp.bias, inp.W1, inp.W2, w.k, inp.expert_capacity, w.dtype)
+            toks += n * w.T
+            reps += 1
+            elapsed = time.perf_counter() - t0
+            if elapsed >= 10.0 or elapsed + elapsed / reps > 30.0:
+                break
+        desc = f"{reps} x {n} decode steps of {w.T} tokens, full weights"
     else:
         n = sample or min(w.T, 8192)
         cap = (-(-n // w.E) * w.k) if inp.expert_capacity >= 0 else -1
-        oracle.moe_forward(inp.X[:n], inp.Wg, inp.bias, inp.W1, inp.W2, w.k, cap, w.dtype)
-        toks = n
-        desc = f"first {n} of {w.T} tokens as one batch, full weights" + (f", capacity {cap}" if cap >= 0 else "")
+        while True:
+            oracle.moe_forward(inp.X[:n], inp.Wg, inp.bias, inp.W1, inp.W2, w.k, cap, w.dtype)
+            toks += n
+            reps += 1
+            elapsed = time.perf_counter() - t0
+            if elapsed >= 10.0 or elapsed + elapsed / reps > 30.0:
+                break
+        desc = (f"{reps} x first {n} of {w.T} tokens as one batch, full weights"
+                + (f", capacity {cap}" if cap >= 0 else ""))
     dt = time.perf_counter() - t0
     return {"value": toks / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": desc, "seconds": round(dt, 2)}
@@ -92,6 +135,15 @@ def cpu_baseline(w, inp, sample):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        import torch
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": src.numel() * 4, "copies": 5}))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus N>1 is not supported",
                           "n_gpus": args.gpus}))
@@ -203,7 +255,8 @@ def main():
         roof = {"bound": "mfma", "achieved": round(work[dom]["flops"] / ms / 1e9, 2), "peak": peak,
                 "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["traffic"] = gemm_traffic(w.name, dom)
+    roof["algorithmic_bytes"] = round(work[dom]["bytes"])
     roof["kernel"] = ("grouped_gemm_kernel (GEMM1+GELU)" if dom == "expert_up" else "grouped_gemm_kernel (GEMM2)")
     roof["ms"] = round(ms, 5)
 

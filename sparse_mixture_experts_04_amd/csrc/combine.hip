@@ -2,7 +2,7 @@
 // accumulated in fp32 ("Qwen2-MoE代码解析" (jsqmd.com/news/1061813) §3.1
 // detail 2: the renormalised routing weights weight the experts' outputs).
 // A dropped slot (inv_perm = -1) adds nothing; a token with no kept slot is 0.
-// Each thread owns one 16-byte chunk of the output row, so every row of Yp is
+// Each thread owns one 16-byte chunk of one output row, so every row of Yp is
 // read with full 16-byte vector loads and each output row is written once;
 // no atomics, so the sum order (slot 0 first) is fixed.
 #include "common.hpp"
@@ -12,56 +12,62 @@ namespace moe {
 namespace {
 
 constexpr int kCombineThreads = 256;
-constexpr int kCombineTok = 8;
 
+// One token per blockIdx.x; each thread owns one 16-byte chunk of the output
+// row (blockIdx.y covers rows longer than 256 chunks) and issues the k slot
+// loads together, so a step costs one memory round trip.
 template <typename T>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const T* __restrict__ Yp,
                                                                   const int32_t* __restrict__ inv_perm,
                                                                   const float* __restrict__ topk_w,
                                                                   T* __restrict__ out, int T_tok, int d, int k) {
   constexpr int kPer = Elem<T>::kPer16B;
-  extern __shared__ int s_dyn[];
-  int* s_row = s_dyn;                                              // [kCombineTok][k]
-  float* s_w = reinterpret_cast<float*>(s_dyn + kCombineTok * k);  // [kCombineTok][k]
-  const int tok0 = blockIdx.x * kCombineTok;
-  const int ntok = min(kCombineTok, T_tok - tok0);
-  for (int i = threadIdx.x; i < ntok * k; i += kCombineThreads) {
-    const int64_t p = static_cast<int64_t>(tok0) * k + i;
-    s_row[i] = inv_perm[p];
-    s_w[i] = topk_w[p];
-  }
-  __syncthreads();
+  constexpr int kMaxSlots = 8;  // slots whose loads are issued together; more are handled in rounds
+  const int t = blockIdx.x;
+  const int v = blockIdx.y * kCombineThreads + threadIdx.x;
   const int nvec = d / kPer;
-  for (int idx = threadIdx.x; idx < ntok * nvec; idx += kCombineThreads) {
-    const int tt = idx / nvec;
-    const int v = idx % nvec;
-    float acc[kPer];
+  if (v >= nvec) return;
+  const int64_t p0 = static_cast<int64_t>(t) * k;
+  const int Tk = T_tok * k;
+  float acc[kPer];
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) acc[q] = 0.f;
-    for (int s = 0; s < k; ++s) {
-      const int row = s_row[tt * k + s];
-      if (row < 0 || row >= T_tok * k) continue;  // dropped (or an invalid row index)
-      const float w = s_w[tt * k + s];
-      const u32x4_t y = ld16(Yp + static_cast<int64_t>(row) * d + v * kPer);
-      const T* ye = reinterpret_cast<const T*>(&y);
+  for (int q = 0; q < kPer; ++q) acc[q] = 0.f;
+  for (int s0 = 0; s0 < k; s0 += kMaxSlots) {
+    u32x4_t y[kMaxSlots];
+    float w[kMaxSlots];
 #pragma unroll
-      for (int q = 0; q < kPer; ++q) acc[q] += w * Elem<T>::to_f32(ye[q]);
+    for (int j = 0; j < kMaxSlots; ++j) {
+      const int s = s0 + j;
+      w[j] = 0.f;
+      y[j] = u32x4_t{0u, 0u, 0u, 0u};
+      if (s < k) {
+        const int row = inv_perm[p0 + s];
+        if (row >= 0 && row < Tk) {  // dropped (or an invalid row index) adds nothing
+          w[j] = topk_w[p0 + s];
+          y[j] = ld16(Yp + static_cast<int64_t>(row) * d + v * kPer);
+        }
+      }
     }
-    u32x4_t o;
-    T* oe = reinterpret_cast<T*>(&o);
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) oe[q] = Elem<T>::from_f32(acc[q]);
-    st16(out + static_cast<int64_t>(tok0 + tt) * d + v * kPer, o);
+    for (int j = 0; j < kMaxSlots; ++j) {
+      const T* ye = reinterpret_cast<const T*>(&y[j]);
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) acc[q] += w[j] * Elem<T>::to_f32(ye[q]);
+    }
   }
+  u32x4_t o;
+  T* oe = reinterpret_cast<T*>(&o);
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) oe[q] = Elem<T>::from_f32(acc[q]);
+  st16(out + static_cast<int64_t>(t) * d + v * kPer, o);
 }
 
 template <typename T>
 hipError_t launch_t(const T* Yp, const int32_t* inv_perm, const float* w, T* out, int T_tok, int d, int k,
                     hipStream_t stream) {
-  const int nblocks = (T_tok + kCombineTok - 1) / kCombineTok;
-  const size_t shm = static_cast<size_t>(kCombineTok) * k * (sizeof(int) + sizeof(float));
-  hipLaunchKernelGGL(combine_kernel<T>, dim3(nblocks), dim3(kCombineThreads), shm, stream, Yp, inv_perm, w, out,
-                     T_tok, d, k);
+  const int nvec = d / Elem<T>::kPer16B;
+  const dim3 grid(T_tok, (nvec + kCombineThreads - 1) / kCombineThreads);
+  hipLaunchKernelGGL(combine_kernel<T>, grid, dim3(kCombineThreads), 0, stream, Yp, inv_perm, w, out, T_tok, d, k);
   return hipGetLastError();
 }
 

@@ -50,6 +50,41 @@ __device__ __forceinline__ uint64_t match(const Ballots& B, int e) {
   return m;
 }
 
+// Copy hidden-state rows tok0 .. tok0+ntok-1 of X to their dispatched rows
+// (row_of[t * row_stride + s], -1 = none).  Each thread issues 8 16-byte loads
+// before their stores, so the copy is not one memory round trip per chunk.
+template <int kThreads, typename T>
+__device__ __forceinline__ void copy_rows(const T* __restrict__ X, T* __restrict__ Xp, int d, int k, int tok0,
+                                          int ntok, const int* row_of, int row_stride) {
+  constexpr int kBatch = 8;
+  const int nvec = d * static_cast<int>(sizeof(T)) / 16;
+  const int total = ntok * nvec;
+  for (int base = threadIdx.x; base < total; base += kThreads * kBatch) {
+    u32x4_t val[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int idx = base + j * kThreads;
+      if (idx < total) {
+        const int tt = idx / nvec;
+        const int v = idx % nvec;
+        val[j] = ld16(reinterpret_cast<const unsigned char*>(X + static_cast<int64_t>(tok0 + tt) * d) + v * 16);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int idx = base + j * kThreads;
+      if (idx < total) {
+        const int tt = idx / nvec;
+        const int v = idx % nvec;
+        for (int s = 0; s < k; ++s) {
+          const int row = row_of[tt * row_stride + s];
+          if (row >= 0) st16(reinterpret_cast<unsigned char*>(Xp + static_cast<int64_t>(row) * d) + v * 16, val[j]);
+        }
+      }
+    }
+  }
+}
+
 __device__ __forceinline__ int load_id(const int32_t* ids, int t, int T, int k, int s, int E) {
   if (t >= T) return kNone;
   const int e = ids[static_cast<int64_t>(t) * k + s];
@@ -235,17 +270,7 @@ __global__ __launch_bounds__(kScatterThreads) void dispatch_scatter_kernel(
     }
   }
   __syncthreads();
-  const int nvec = d * static_cast<int>(sizeof(T)) / 16;
-  const int ntok = min(kScatterTok, T_tok - tok0);
-  for (int idx = threadIdx.x; idx < ntok * nvec; idx += kScatterThreads) {
-    const int tt = idx / nvec;
-    const int v = idx % nvec;
-    const u32x4_t val = ld16(reinterpret_cast<const unsigned char*>(X + static_cast<int64_t>(tok0 + tt) * d) + v * 16);
-    for (int s = 0; s < k; ++s) {
-      const int row = s_row[tt][s];
-      if (row >= 0) st16(reinterpret_cast<unsigned char*>(Xp + static_cast<int64_t>(row) * d) + v * 16, val);
-    }
-  }
+  copy_rows<kScatterThreads>(X, Xp, d, k, tok0, min(kScatterTok, T_tok - tok0), &s_row[0][0], KMAX);
 }
 
 // Small T (<= 256 tokens, k <= 8): the whole dispatch in one block of 4
@@ -391,16 +416,7 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __re
   if (threadIdx.x <= E) offsets[threadIdx.x] = s_off[threadIdx.x];
   for (int r = s_off[E] + threadIdx.x; r < Tk; r += 256) perm[r] = -1;
   __syncthreads();
-  const int nvec = d * static_cast<int>(sizeof(T)) / 16;
-  for (int idx = threadIdx.x; idx < T_tok * nvec; idx += 256) {
-    const int tt = idx / nvec;
-    const int v = idx % nvec;
-    const u32x4_t val = ld16(reinterpret_cast<const unsigned char*>(X + static_cast<int64_t>(tt) * d) + v * 16);
-    for (int s = 0; s < k; ++s) {
-      const int row = s_row[tt][s];
-      if (row >= 0) st16(reinterpret_cast<unsigned char*>(Xp + static_cast<int64_t>(row) * d) + v * 16, val);
-    }
-  }
+  copy_rows<256>(X, Xp, d, k, 0, T_tok, &s_row[0][0], kSmallMaxK);
 }
 
 template <typename T, int KMAX>

@@ -272,33 +272,33 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(
   topk_tile<NT>(sum, bias, E, k, rtok0, T_tokens, sel_val[r], sel_id[r], topk_ids, topk_w);
 }
 
-// Sum the K-split partial logits in split order, then top-k.  A block of 256
-// threads owns 16 tokens: every thread sums a few (token, expert) entries with
-// independent loads, the sums meet in LDS, and wave 0 selects.
+// Sum the K-split partial logits in split order, then top-k.  A block of 1024
+// threads owns 16 tokens: one thread per (token, expert) entry sums the splits
+// with 8 loads in flight, the sums meet in LDS, and wave 0 selects.
 template <int NT>
-__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ partial, int nsplit,
-                                                          const float* __restrict__ bias, int T_tokens, int E, int k,
-                                                          int32_t* __restrict__ topk_ids,
-                                                          float* __restrict__ topk_w) {
+__global__ __launch_bounds__(1024) void router_topk_kernel(const float* __restrict__ partial, int nsplit,
+                                                           const float* __restrict__ bias, int T_tokens, int E, int k,
+                                                           int32_t* __restrict__ topk_ids,
+                                                           float* __restrict__ topk_w) {
   __shared__ float logit[16][kMaxExperts];
   __shared__ float sel_val[16 * kMaxExperts];
   __shared__ int sel_id[16 * kMaxExperts];
   const int tok0 = blockIdx.x * 16;
-  for (int p = threadIdx.x; p < 16 * E; p += 256) {
-    const int r = p / E;
-    const int e = p % E;
+  {
+    const int r = threadIdx.x / kMaxExperts;
+    const int e = threadIdx.x % kMaxExperts;
     const int tok = tok0 + r;
     float v = 0.f;
-    if (tok < T_tokens) {
+    if (tok < T_tokens && e < E) {
       const float* src = partial + static_cast<int64_t>(tok) * E + e;
       const int64_t stride = static_cast<int64_t>(T_tokens) * E;
-      int s = 0;
-      for (; s + 4 <= nsplit; s += 4) {
-        const float a0 = src[(s + 0) * stride], a1 = src[(s + 1) * stride];
-        const float a2 = src[(s + 2) * stride], a3 = src[(s + 3) * stride];
-        v += ((a0 + a1) + (a2 + a3));
+      for (int s0 = 0; s0 < nsplit; s0 += 8) {
+        float a[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a[j] = (s0 + j < nsplit) ? src[(s0 + j) * stride] : 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v += a[j];  // split order
       }
-      for (; s < nsplit; ++s) v += src[s * stride];
     }
     logit[r][e] = v;
   }
@@ -353,7 +353,7 @@ hipError_t launch_nt(const T* X, const T* Wg, const float* bias, int T_tokens, i
                        T_tokens, d, E, k, split_len, nullptr, ids, w);
   }
   if (nsplit > 1)
-    hipLaunchKernelGGL((router_topk_kernel<NT>), dim3((T_tokens + 15) / 16), dim3(256), 0, stream, partial, nsplit,
+    hipLaunchKernelGGL((router_topk_kernel<NT>), dim3((T_tokens + 15) / 16), dim3(1024), 0, stream, partial, nsplit,
                        bias, T_tokens, E, k, ids, w);
   return hipGetLastError();
 }
