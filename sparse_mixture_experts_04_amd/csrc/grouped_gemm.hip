@@ -332,15 +332,24 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
   const int kstages = K * 2 / kStageRowBytes;
   const int64_t row_stride = static_cast<int64_t>(K) * 2;
 
+  // Within an expert, tiles run in groups of up to kGroupM m-tiles: all
+  // n-tiles of the group, m-tile fastest.  A block's run of consecutive tiles
+  // (one XCD's share) then covers a few m-tiles x a few n-tiles, so both the
+  // token rows and the weight rows it streams are reused from that XCD's L2.
   auto coord = [&](int tile) {
+    constexpr int kGroupM = 8;
     int e = 0;
     while (e + 1 < E && s_tile_base[e + 1] * n_tiles_n <= tile) ++e;
     const int mt_e = s_tile_base[e + 1] - s_tile_base[e];
     const int local = tile - s_tile_base[e] * n_tiles_n;
+    const int group = local / (kGroupM * n_tiles_n);
+    const int first_m = group * kGroupM;
+    const int gsize = min(kGroupM, mt_e - first_m);
+    const int in = local - group * kGroupM * n_tiles_n;
     TileCoord t;
     t.e = e;
-    t.n0 = (local / mt_e) * kBig;
-    t.m0 = s_seg0[e] + (local % mt_e) * kBig;
+    t.n0 = (in / gsize) * kBig;
+    t.m0 = s_seg0[e] + (first_m + in % gsize) * kBig;
     t.seg1 = s_seg1[e];
     return t;
   };
