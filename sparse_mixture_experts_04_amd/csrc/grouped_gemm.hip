@@ -223,45 +223,42 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_kernel(const T* 
 }
 
 // ---------------------------------------------------------------------------
-// bf16 main kernel: 256x256 tiles, 4 waves of 128x128, 32x32x16 MFMAs, and a
-// 4-deep ring of LDS stages fed by direct global->LDS loads.
+// bf16 main kernel: 256x256 tiles, 4 waves of 128x128, 32x32x16 MFMAs, fed by
+// direct buffer->LDS loads through a ring of LDS units.
 //
-// * Stage = 32 K-elements (64 bytes) of 256 token rows and 256 weight rows,
-//   32 KB; four stages = 128 KB of LDS.  Loads run three stages ahead, and the
-//   stream of (tile, stage) pairs is continuous across the persistent block's
-//   tiles, so the next tile's first stages load during this tile's last
-//   stages and epilogue.
-// * LDS layout: two 64-byte rows share a 128-byte line; the eight 16-byte
-//   chunks of a line are XOR-permuted by a per-line key so that the fragment
-//   reads of 8 (or 16) consecutive lanes hit distinct banks.
+// * A unit is 64 K-elements (128 bytes: one full cache line per row) of the
+//   256 rows of one operand, 32 KB.  A stage is one weight unit and one token
+//   unit.  Five units (160 KB of LDS) form a ring: while stage s is consumed,
+//   stage s+1 has landed or is landing and the weight unit of stage s+2 is in
+//   flight, so the weight rows (the operand that misses L2 most) are requested
+//   two stages ahead and the token rows one stage ahead.  The two unit streams
+//   run continuously across the persistent block's tiles.
+// * Loads go through buffer resources whose range covers only the tile's
+//   valid rows: rows past an expert's segment or past N read as zero without
+//   any clamping, and per-lane offsets are 32-bit and fixed for the kernel.
+// * LDS layout: row r of a unit at r*128; its 16-byte chunk c at chunk
+//   c ^ key(r), with keys chosen so the fragment reads of every 16 lanes hit 16
+//   distinct 16-byte bank groups (64 banks).
 // * The weight rows are the MFMA A operand and the token rows the B operand,
 //   so a lane of the 32x32 result holds one token row.  The weight rows of
-//   each 32-row fragment are loaded in the order pi(x) = 16*((x>>2)&1) +
+//   each 32-row fragment are read in the order pi(x) = 16*((x>>2)&1) +
 //   4*(x>>3) + (x&3), which makes a lane's 16 results 16 consecutive output
 //   columns: two 16-byte stores.
+// * One barrier per stage (four 16-element k-steps).
 constexpr int kBig = 256;                                 // BM = BN
 constexpr int kBigThreads = 256;                          // 4 waves, 2 x 2
-constexpr int kStageRowBytes = 64;                        // K bytes per row per stage
-constexpr int kOperandBytes = kBig * kStageRowBytes;      // 16 KB
-constexpr int kRingStageBytes = 2 * kOperandBytes;        // tokens + weights
-constexpr int kRing = 4;
-constexpr size_t kBigLds = static_cast<size_t>(kRing) * kRingStageBytes;  // 128 KB
+constexpr int kUnitRow = 128;                             // K bytes per row per unit
+constexpr int kUnitBytes = kBig * kUnitRow;               // 32 KB
+constexpr int kSlots = 5;
+constexpr size_t kBigLds = static_cast<size_t>(kSlots) * kUnitBytes;  // 160 KB
+// Word 3 of a raw (unstructured) buffer resource on the gfx9 family: 32-bit
+// data format, no swizzle; bounds are checked against num_records in bytes.
+constexpr int kRsrcWord3 = 0x00020000;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-__device__ __forceinline__ int key_x(int line) { return ((line >> 1) & 3) ^ ((line & 1) << 1); }
-__device__ __forceinline__ int key_w(int line) {
-  return (((line >> 1) ^ line) & 1) | ((((line >> 3) ^ line) & 1) << 1);
-}
-// Byte offset of logical chunk c (0..3) of `row` within an operand tile.
-__device__ __forceinline__ int off_x(int row, int c) {
-  const int line = row >> 1;
-  return line * 128 + (((((row & 1) << 2) | c) ^ key_x(line)) << 4);
-}
-__device__ __forceinline__ int off_w(int row, int c) {
-  const int line = row >> 1;
-  return line * 128 + (((((row & 1) << 2) | c) ^ key_w(line)) << 4);
-}
+__device__ __forceinline__ int key_x(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int key_w(int r) { return ((r >> 1) & 3) | (((r >> 4) & 1) << 2); }
 
 // x * sigmoid(2u) = 0.5 x (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3),
 // with the hardware exp2 and reciprocal (about 1 ulp each).  Large |x|
@@ -278,6 +275,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   // gfx9 s_waitcnt: vmcnt[3:0] and [15:14], expcnt[6:4] (7 = no wait), lgkmcnt[11:8] (15 = no wait)
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
 
 struct TileCoord {
   int e, m0, n0, seg1;
@@ -290,58 +291,48 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
                                                                         const int32_t* __restrict__ offsets, int E,
                                                                         int N, int K, int max_rows) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  __shared__ int s_tile_base[kMaxExperts + 1];
-  __shared__ int s_seg0[kMaxExperts];
-  __shared__ int s_seg1[kMaxExperts];
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: LDS bases stay scalar
   const int wm = wave >> 1;   // token half of the tile
   const int wn = wave & 1;    // weight half of the tile
 
-  if (tid < kWave) {
-    const int e = tid;
-    int mt = 0, seg0 = 0, seg1 = 0;
-    if (e < E) {
-      seg0 = min(max(offsets[e], 0), max_rows);
-      seg1 = min(max(offsets[e + 1], seg0), max_rows);
-      mt = (seg1 - seg0 + kBig - 1) / kBig;
-    }
-    int incl = mt;
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) {
-      const int o = __shfl_up(incl, m);
-      if (lane >= m) incl += o;
-    }
-    if (e < E) {
-      s_tile_base[e + 1] = incl;
-      s_seg0[e] = seg0;
-      s_seg1[e] = seg1;
-    }
-    if (e == 0) s_tile_base[0] = 0;
+  // Expert table, held by every wave in registers: lane e has expert e's row
+  // segment [seg0, seg1) (clamped to [0, max_rows]: offsets come from device
+  // memory) and the running count of m-tiles before and through it.
+  int t_seg0 = 0, t_seg1 = 0, t_mt = 0;
+  if (lane < E) {
+    t_seg0 = min(max(offsets[lane], 0), max_rows);
+    t_seg1 = min(max(offsets[lane + 1], t_seg0), max_rows);
+    t_mt = (t_seg1 - t_seg0 + kBig - 1) / kBig;
   }
-  __syncthreads();
-
+  int t_incl = t_mt;
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) {
+    const int o = __shfl_up(t_incl, m);
+    if (lane >= m) t_incl += o;
+  }
   const int n_tiles_n = (N + kBig - 1) / kBig;
-  const int total = s_tile_base[E] * n_tiles_n;
+  const int total = __builtin_amdgcn_readlane(t_incl, E - 1) * n_tiles_n;
   const int G = gridDim.x;
   int first = blockIdx.x;
   if ((G & 7) == 0) first = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
   if (first >= total) return;
-  const int kstages = K * 2 / kStageRowBytes;
-  const int64_t row_stride = static_cast<int64_t>(K) * 2;
+  const int kstages = K * 2 / kUnitRow;
+  const int row_stride = K * 2;  // bytes; 256 rows of it fit in 31 bits (checked by the host)
 
-  // Within an expert, tiles run in groups of up to kGroupM m-tiles: all
-  // n-tiles of the group, m-tile fastest.  A block's run of consecutive tiles
-  // (one XCD's share) then covers a few m-tiles x a few n-tiles, so both the
-  // token rows and the weight rows it streams are reused from that XCD's L2.
+  // tile -> (expert, m-tile, n-tile).  Within an expert, tiles run in groups
+  // of up to kGroupM m-tiles: all n-tiles of the group, m-tile fastest, so a
+  // block's run of consecutive tiles (one XCD's share) covers a few m-tiles x
+  // a few n-tiles and reuses both operands from that XCD's L2.
   auto coord = [&](int tile) {
     constexpr int kGroupM = 8;
-    int e = 0;
-    while (e + 1 < E && s_tile_base[e + 1] * n_tiles_n <= tile) ++e;
-    const int mt_e = s_tile_base[e + 1] - s_tile_base[e];
-    const int local = tile - s_tile_base[e] * n_tiles_n;
+    const unsigned long long done = __ballot(lane < E && t_incl * n_tiles_n <= tile);
+    const int e = __builtin_amdgcn_readfirstlane(static_cast<int>(__popcll(done)));
+    const int incl = __builtin_amdgcn_readlane(t_incl, e);
+    const int mt_e = __builtin_amdgcn_readlane(t_mt, e);
+    const int local = tile - (incl - mt_e) * n_tiles_n;
     const int group = local / (kGroupM * n_tiles_n);
     const int first_m = group * kGroupM;
     const int gsize = min(kGroupM, mt_e - first_m);
@@ -349,104 +340,135 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
     TileCoord t;
     t.e = e;
     t.n0 = (in / gsize) * kBig;
-    t.m0 = s_seg0[e] + (first_m + in % gsize) * kBig;
-    t.seg1 = s_seg1[e];
+    t.m0 = __builtin_amdgcn_readlane(t_seg0, e) + (first_m + in % gsize) * kBig;
+    t.seg1 = __builtin_amdgcn_readlane(t_seg1, e);
     return t;
   };
 
-  // ---- producer: direct loads of one stage (4 + 4 instructions of 1 KB per wave)
-  // Instruction t of this wave covers rows wave*64 + t*16 .. +15 = lines L0 .. L0+7,
-  // L0 = wave*32 + t*8; lane p fills line L0 + p/8, physical chunk p%8.
-  const int ld_line_lo = lane >> 3;
-  const int ld_phys = lane & 7;
-  const unsigned char* xsrc[4];
-  const unsigned char* wsrc[4];
-  int p_tile = first, p_ks = 0, p_count = 0;
-  auto producer_setup = [&](int tile) {
-    const TileCoord t = coord(tile);
-    const unsigned char* Ab = reinterpret_cast<const unsigned char*>(A);
-    const unsigned char* Bb = reinterpret_cast<const unsigned char*>(B) + static_cast<int64_t>(t.e) * N * row_stride;
+  // ---- producers: one stream of weight units and one of token units.
+  // Instruction i of this wave fills rows wave*64 + i*8 .. +7 of a unit (1 KB
+  // of LDS); lane p fills row wave*64 + i*8 + p/8, physical chunk p%8.
+  int vw[8], vx[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int line = wave * 32 + i * 8 + ld_line_lo;
-      const int qx = ld_phys ^ key_x(line);
-      const int rx = 2 * line + (qx >> 2);
-      xsrc[i] = Ab + min(t.m0 + rx, t.seg1 - 1) * row_stride + (qx & 3) * 16;
-      const int qw = ld_phys ^ key_w(line);
-      const int rw = 2 * line + (qw >> 2);
-      wsrc[i] = Bb + min(t.n0 + rw, N - 1) * row_stride + (qw & 3) * 16;
+  for (int i = 0; i < 8; ++i) {
+    const int r = wave * 64 + i * 8 + (lane >> 3);
+    vw[i] = r * row_stride + (((lane & 7) ^ key_w(r)) << 4);
+    vx[i] = r * row_stride + (((lane & 7) ^ key_x(r)) << 4);
+  }
+  const unsigned char* const Ab = reinterpret_cast<const unsigned char*>(A);
+  const unsigned char* const Bb = reinterpret_cast<const unsigned char*>(B);
+  struct Stream {
+    const unsigned char* base;  // first row of the tile's operand
+    int rows;                   // valid rows (0 past the last tile)
+    int tile, ks, slot;
+  };
+  Stream ws{nullptr, 0, first, 0, 0};  // weight unit of stage s -> slot 2s mod 5
+  Stream xs{nullptr, 0, first, 0, 1};  // token unit of stage s -> slot 2s+1 mod 5
+  auto setup_w = [&](Stream& s) {
+    if (s.tile < total) {
+      const TileCoord t = coord(s.tile);
+      s.base = Bb + (static_cast<int64_t>(t.e) * N + t.n0) * row_stride;
+      s.rows = min(N - t.n0, kBig);
+    } else {
+      s.rows = 0;
     }
   };
-  // Issue one stage into ring slot p_count % 4.  Past the last tile the
-  // pointers of the last tile are reused (harmless loads into a free slot), so
-  // the issue is branch-free and can be interleaved with the MFMAs.
-  auto produce_issue = [&]() {
-    unsigned char* sx = smem + (p_count & (kRing - 1)) * kRingStageBytes;
-    unsigned char* sw = sx + kOperandBytes;
-    const int64_t koff = static_cast<int64_t>(p_ks) * kStageRowBytes;
+  auto setup_x = [&](Stream& s) {
+    if (s.tile < total) {
+      const TileCoord t = coord(s.tile);
+      s.base = Ab + static_cast<int64_t>(t.m0) * row_stride;
+      s.rows = min(t.seg1 - t.m0, kBig);
+    } else {
+      s.rows = 0;
+    }
+  };
+  // Issue one unit (8 loads of 1 KB per wave).  Past the last tile the range
+  // is empty: the loads return zeros into a free slot without touching memory.
+  auto issue = [&](const Stream& s, const int (&voff)[8]) {
+    const int koff = s.ks * kUnitRow;
+    const int nrec = max(s.rows * row_stride - koff, 0);
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(s.base) + koff, 0, nrec, kRsrcWord3);
+    unsigned char* dst = smem + s.slot * kUnitBytes + wave * 64 * kUnitRow;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int run = (wave * 32 + i * 8) * 128;
-      __builtin_amdgcn_global_load_lds(xsrc[i] + koff, (lds_ptr_t)(sx + run), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(wsrc[i] + koff, (lds_ptr_t)(sw + run), 16, 0, 0);
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(dst + i * 8 * kUnitRow), 16, voff[i], 0, 0, 0);
+  };
+  auto advance_w = [&](Stream& s) {
+    s.slot = s.slot + 2 >= kSlots ? s.slot + 2 - kSlots : s.slot + 2;
+    if (++s.ks == kstages) {
+      s.ks = 0;
+      s.tile += G;
+      setup_w(s);
     }
   };
-  auto produce_advance = [&]() {
-    ++p_count;
-    if (++p_ks == kstages) {
-      p_ks = 0;
-      p_tile += G;
-      if (p_tile < total) producer_setup(p_tile);
+  auto advance_x = [&](Stream& s) {
+    s.slot = s.slot + 2 >= kSlots ? s.slot + 2 - kSlots : s.slot + 2;
+    if (++s.ks == kstages) {
+      s.ks = 0;
+      s.tile += G;
+      setup_x(s);
     }
-  };
-  auto produce = [&]() {
-    produce_issue();
-    produce_advance();
   };
 
-  producer_setup(p_tile);
+  setup_w(ws);
+  setup_x(xs);
+  // Prologue: stages 0 and 1 (units 0..3).
 #pragma unroll
-  for (int i = 0; i < kRing - 1; ++i)
-    if (p_tile < total) produce();
+  for (int i = 0; i < 2; ++i) {
+    issue(ws, vw);
+    advance_w(ws);
+    issue(xs, vx);
+    advance_x(xs);
+  }
 
   const int frow = lane & 31;
   const int fhalf = lane >> 5;
   const int wrow = ((frow >> 2) & 1) * 16 + (frow >> 3) * 4 + (frow & 3);  // pi(frow)
-  int c_count = 0;
+  const int kx = key_x(frow);  // = key_x of every token row this lane reads
+  const int kw = key_w(wrow);  // = key_w of every weight row this lane reads
+  int c_wslot = 0, c_xslot = 1;
 
   // Fragments of one 16-element k-step: 4 weight and 4 token fragments.
   u32x4_t wf0[4], xf0[4], wf1[4], xf1[4];
-  auto read_frags = [&](int slot, int kk, u32x4_t (&wf)[4], u32x4_t (&xf)[4]) {
-    const unsigned char* sx = smem + slot * kRingStageBytes;
-    const unsigned char* sw = sx + kOperandBytes;
-    const int c = kk * 2 + fhalf;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) wf[i] = *reinterpret_cast<const u32x4_t*>(sw + off_w(wn * 128 + i * 32 + wrow, c));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) xf[j] = *reinterpret_cast<const u32x4_t*>(sx + off_x(wm * 128 + j * 32 + frow, c));
+  auto frag_addr_w = [&](int kk, int i) {
+    return smem + c_wslot * kUnitBytes + (wn * 128 + i * 32 + wrow) * kUnitRow + (((kk * 2 + fhalf) ^ kw) << 4);
   };
-  // Issue the 8 fragment reads of the other k-step among the first 4 of the
-  // 16 MFMAs of a region, so their latency hides behind the MFMA stream.
-  auto interleave_reads = [&]() {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
-    __builtin_amdgcn_sched_barrier(0);
+  auto frag_addr_x = [&](int kk, int j) {
+    return smem + c_xslot * kUnitBytes + (wm * 128 + j * 32 + frow) * kUnitRow + (((kk * 2 + fhalf) ^ kx) << 4);
   };
-  // Same, with the 8 global->LDS loads of the next stage spread over the
-  // first 4 MFMAs as well.
-  auto interleave_loads_reads = [&]() {
+  auto read_frags = [&](int kk, u32x4_t (&wf)[4], u32x4_t (&xf)[4]) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // 2 global->LDS loads
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads
+    for (int i = 0; i < 4; ++i) wf[i] = *reinterpret_cast<const u32x4_t*>(frag_addr_w(kk, i));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xf[j] = *reinterpret_cast<const u32x4_t*>(frag_addr_x(kk, j));
+  };
+  // One k-step block, in a fixed issue order: its 16 MFMAs, with the 8
+  // fragment reads of k-step `kk_next` (into wn/xn) after the first 8 MFMAs
+  // one by one and, if `s` is given, a unit's 8 buffer->LDS loads likewise,
+  // so neither the LDS nor the load queue ever holds up the MFMA stream.
+  auto block = [&](f32x16_t (&acc)[4][4], const u32x4_t (&wa)[4], const u32x4_t (&xa)[4], int kk_next,
+                   u32x4_t (&wn_)[4], u32x4_t (&xn_)[4], const Stream* s, const int* voff) {
+    __amdgpu_buffer_rsrc_t rsrc;
+    unsigned char* dst = smem;
+    if (s != nullptr) {
+      const int koff = s->ks * kUnitRow;
+      const int nrec = max(s->rows * row_stride - koff, 0);
+      rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(s->base) + koff, 0, nrec, kRsrcWord3);
+      dst = smem + s->slot * kUnitBytes + wave * 64 * kUnitRow;
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
-    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int i = q >> 2, j = q & 3;
+      acc[i][j] = GemmMma<uint16_t>::run(wa[i], xa[j], acc[i][j]);
+      if (kk_next >= 0) {
+        if (q < 4) wn_[q] = *reinterpret_cast<const u32x4_t*>(frag_addr_w(kk_next, q));
+        else if (q < 8) xn_[q - 4] = *reinterpret_cast<const u32x4_t*>(frag_addr_x(kk_next, q - 4));
+      }
+      if (s != nullptr && q < 8)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(dst + q * 8 * kUnitRow), 16, voff[q], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
   auto barrier = [&]() {
     asm volatile("" ::: "memory");
@@ -454,10 +476,11 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
     asm volatile("" ::: "memory");
   };
 
-  // Stage 0 must be resident before its first fragments are read.
-  wait_vmcnt<0>();
+  // Stage 0 must be resident before its first fragments are read (stage 1,
+  // 16 loads, may still be in flight).
+  wait_vmcnt<16>();
   barrier();
-  read_frags(0, 0, wf0, xf0);
+  read_frags(0, wf0, xf0);
   bool after_epilogue = false;
 
   for (int tile = first; tile < total; tile += G) {
@@ -471,47 +494,51 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
     for (int ks = 0; ks < kstages; ++ks) {
-      // k-step 0 of this stage is in wf0/xf0; read k-step 1, then run k-step 0.
-      const int slot = c_count & (kRing - 1);
-      read_frags(slot, 1, wf1, xf1);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = GemmMma<uint16_t>::run(wf0[i], xf0[j], acc[i][j]);
-      interleave_reads();
-      // The next stage must have landed (one later stage may stay in flight;
-      // right after an epilogue its stores are outstanding too: drain).
-      ++c_count;
-      const int ahead = p_count - c_count - 1;
-      if (after_epilogue || ahead <= 0) wait_vmcnt<0>();
-      else wait_vmcnt<8>();
+      // k-step 0 of this stage is in wf0/xf0.  Its block also issues the
+      // weight unit two stages ahead.
+      block(acc, wf0, xf0, 1, wf1, xf1, &ws, vw);
+      advance_w(ws);
+      block(acc, wf1, xf1, 2, wf0, xf0, nullptr, nullptr);
+      block(acc, wf0, xf0, 3, wf1, xf1, nullptr, nullptr);
+      // The next stage must have landed; the weight unit issued above may stay
+      // in flight (right after an epilogue its stores are outstanding too:
+      // drain).  lgkmcnt(0): this wave's reads of this stage are complete, so
+      // after the barrier its two units are free.
+      if (after_epilogue) wait_vmcnt_lgkm0<0>();
+      else wait_vmcnt_lgkm0<8>();
       after_epilogue = false;
       barrier();
       __builtin_amdgcn_sched_barrier(0);
-      // Every wave is past the slot of stage c_count - 2 (read last iteration): refill it.
-      produce_issue();
-      // (past the last stage this reads a stale slot whose values go unused)
-      read_frags(c_count & (kRing - 1), 0, wf0, xf0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = GemmMma<uint16_t>::run(wf1[i], xf1[j], acc[i][j]);
-      interleave_loads_reads();
-      produce_advance();
+      c_wslot = c_wslot + 2 >= kSlots ? c_wslot + 2 - kSlots : c_wslot + 2;
+      c_xslot = c_xslot + 2 >= kSlots ? c_xslot + 2 - kSlots : c_xslot + 2;
+      // Refill a freed slot with the token unit of the stage after next, and
+      // read k-step 0 of the next stage (past the last stage: a free slot
+      // whose values go unused).
+      block(acc, wf1, xf1, 0, wf0, xf0, &xs, vx);
+      advance_x(xs);
     }
     after_epilogue = true;
 
     // acc[i][j][q]: token row m0 + wm*128 + j*32 + frow, column n0 + wn*128 + i*32 + 16*fhalf + q.
-    // Branch-free per group (only the stores are predicated) so the 16
-    // accumulators of one group are read, converted and stored before the next.
+    // Stores go through a buffer resource over the tile's valid rows of C;
+    // a column past N gets an offset beyond the range.  The hardware drops
+    // out-of-range stores, so the epilogue has no branches and each group of
+    // 16 accumulators is read, converted and stored before the next.
+    const int vrows = min(tc.seg1 - tc.m0, kBig);
+    const __amdgpu_buffer_rsrc_t crsrc = __builtin_amdgcn_make_buffer_rsrc(
+        C + static_cast<int64_t>(tc.m0) * N, 0, vrows * N * 2, kRsrcWord3);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int row = tc.m0 + wm * 128 + j * 32 + frow;
-      const bool row_ok = row < tc.seg1;
-      uint16_t* crow = C + static_cast<int64_t>(row_ok ? row : tc.m0) * N;
+      const int roff = (wm * 128 + j * 32 + frow) * N * 2;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int col = tc.n0 + wn * 128 + i * 32 + 16 * fhalf;
+        const int off = col < N ? roff + col * 2 : static_cast<int>(0x80000000u);
+        // Redefine the group's accumulators here (an empty asm on their
+        // registers), after the previous group's stores: otherwise the
+        // compiler copies all 256 out of the accumulator registers at the loop
+        // exit and runs out of registers for the GELU.
+        asm volatile("" : "+a"(acc[i][j])::"memory");
         float v[16];
 #pragma unroll
         for (int q = 0; q < 16; ++q) v[q] = kGelu ? gelu_tanh_fast(acc[i][j][q]) : acc[i][j][q];
@@ -521,10 +548,8 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
           lo[h] = pack_bf16x2(v[2 * h], v[2 * h + 1]);
           hi[h] = pack_bf16x2(v[8 + 2 * h], v[8 + 2 * h + 1]);
         }
-        if (row_ok && col < N) {
-          st16(crow + col, lo);
-          st16(crow + col + 8, hi);
-        }
+        __builtin_amdgcn_raw_buffer_store_b128(lo, crsrc, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(hi, crsrc, off + 16, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -539,6 +564,11 @@ hipError_t launch_big(const uint16_t* A, const uint16_t* B, uint16_t* C, const i
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                                      static_cast<int>(kBigLds));
   if (attr != hipSuccess) return attr;
+  // 32-bit buffer offsets: 256 rows of K (operands) or N (results) bf16 must
+  // stay below 2^31 bytes.
+  if (static_cast<int64_t>(K) * 2 * kBig >= (int64_t{1} << 31) ||
+      static_cast<int64_t>(N) * 2 * kBig >= (int64_t{1} << 31))
+    return hipErrorInvalidValue;
   const int n_tiles_n = (N + kBig - 1) / kBig;
   const int64_t upper = (static_cast<int64_t>((max_rows + kBig - 1) / kBig) + E) * n_tiles_n;
   int64_t grid = device_cu_count();
