@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const T* __res
         const int row = inv_perm[p0 + s];
         if (row >= 0 && row < Tk) {  // dropped (or an invalid row index) adds nothing
           w[j] = topk_w[p0 + s];
-          y[j] = ld16(Yp + static_cast<int64_t>(row) * d + v * kPer);
+          y[j] = ld16_nt(Yp + static_cast<int64_t>(row) * d + v * kPer);
         }
       }
     }
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const T* __res
   T* oe = reinterpret_cast<T*>(&o);
 #pragma unroll
   for (int q = 0; q < kPer; ++q) oe[q] = Elem<T>::from_f32(acc[q]);
-  st16(out + static_cast<int64_t>(t) * d + v * kPer, o);
+  st16_nt(out + static_cast<int64_t>(t) * d + v * kPer, o);
 }
 
 template <typename T>

@@ -62,5 +62,14 @@ __device__ __forceinline__ u32x4_t ld16(const void* p) {
 __device__ __forceinline__ void st16(void* p, u32x4_t v) {
   *reinterpret_cast<u32x4_t*>(p) = v;
 }
+// Streaming variants (non-temporal cache policy) for data touched once:
+// they keep single-use bytes from displacing reused lines in the caches and
+// stream measurably faster from HBM than the default policy.
+__device__ __forceinline__ u32x4_t ld16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+__device__ __forceinline__ void st16_nt(void* p, u32x4_t v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
+}
 
 }  // namespace moe

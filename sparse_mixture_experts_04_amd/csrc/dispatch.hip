@@ -67,7 +67,7 @@ __device__ __forceinline__ void copy_rows(const T* __restrict__ X, T* __restrict
       if (idx < total) {
         const int tt = idx / nvec;
         const int v = idx % nvec;
-        val[j] = ld16(reinterpret_cast<const unsigned char*>(X + static_cast<int64_t>(tok0 + tt) * d) + v * 16);
+        val[j] = ld16_nt(reinterpret_cast<const unsigned char*>(X + static_cast<int64_t>(tok0 + tt) * d) + v * 16);
       }
     }
 #pragma unroll

@@ -651,36 +651,49 @@ __global__ __launch_bounds__(kWave) void grouped_gemm_bf16_skinny(const uint16_t
 #pragma unroll
   for (int j = 0; j < kGroups; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // Register double buffering: the loads of the next kSkinnyUnroll steps are
+  // in flight while the MFMAs of the current ones run.  Token loads are
+  // unconditional (rows past the expert's last one repeat it; those results
+  // are never stored), so the loop has no branches.
+  constexpr int kU = kGroups == 1 ? kSkinnyUnroll : kSkinnyUnroll / 2;
   const int steps = K / 32;  // 64 bytes of K per step
-  int st = 0;
-  for (; st + kSkinnyUnroll <= steps; st += kSkinnyUnroll) {
-    u32x4_t wa[kSkinnyUnroll], xb[kSkinnyUnroll][kGroups];
+  const int nblk = steps / kU;
+  u32x4_t wa[2][kU], xb[2][kU][kGroups];
+  auto load = [&](int buf, int blk) {
 #pragma unroll
-    for (int u = 0; u < kSkinnyUnroll; ++u) {
-      const int64_t off = static_cast<int64_t>(st + u) * 64;
-      wa[u] = ld16(wp + off);
+    for (int u = 0; u < kU; ++u) {
+      const int64_t off = static_cast<int64_t>(blk * kU + u) * 64;
+      wa[buf][u] = ld16(wp + off);
 #pragma unroll
-      for (int j = 0; j < kGroups; ++j)
-        if (j < groups) xb[u][j] = ld16(xp[j] + off);
+      for (int j = 0; j < kGroups; ++j) xb[buf][u][j] = ld16(xp[j] + off);
     }
+  };
+  auto mma = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < kSkinnyUnroll; ++u)
+    for (int u = 0; u < kU; ++u)
 #pragma unroll
       for (int j = 0; j < kGroups; ++j)
-        if (j < groups)
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wa[u]),
-                                                           __builtin_bit_cast(bf16x8_t, xb[u][j]), acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wa[buf][u]),
+                                                         __builtin_bit_cast(bf16x8_t, xb[buf][u][j]), acc[j], 0, 0, 0);
+  };
+  if (nblk > 0) load(0, 0);
+  int blk = 0;
+  for (; blk + 2 <= nblk; blk += 2) {
+    load(1, blk + 1);
+    mma(0);
+    if (blk + 2 < nblk) load(0, blk + 2);
+    mma(1);
   }
-  for (; st < steps; ++st) {
+  if (blk < nblk) mma(0);  // odd block count: the last block sits in buffer 0
+  for (int st = nblk * kU; st < steps; ++st) {
     const int64_t off = static_cast<int64_t>(st) * 64;
-    const u32x4_t wa = ld16(wp + off);
+    const u32x4_t w = ld16(wp + off);
 #pragma unroll
-    for (int j = 0; j < kGroups; ++j)
-      if (j < groups) {
-        const u32x4_t xb = ld16(xp[j] + off);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wa),
-                                                         __builtin_bit_cast(bf16x8_t, xb), acc[j], 0, 0, 0);
-      }
+    for (int j = 0; j < kGroups; ++j) {
+      const u32x4_t x = ld16(xp[j] + off);
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w), __builtin_bit_cast(bf16x8_t, x),
+                                                       acc[j], 0, 0, 0);
+    }
   }
   // acc[j][q]: weight row n0 + g*4 + q, token row j*16 + r16.
 #pragma unroll
