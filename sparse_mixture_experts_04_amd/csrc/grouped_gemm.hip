@@ -633,20 +633,23 @@ __global__ __launch_bounds__(kWave) void grouped_gemm_bf16_skinny(const uint16_t
   while (e + 1 < E && s_tile_base[e + 1] <= tile) ++e;
   const int n0 = (tile - s_tile_base[e]) * kSkinnyRows;
   const int seg0 = s_seg0[e];
-  const int rows = min(s_seg1[e] - seg0, kGroups * 16);
-  const int groups = (rows + 15) / 16;
+  const int all_rows = s_seg1[e] - seg0;
 
   const int r16 = lane & 15;
   const int g = lane >> 4;  // 16-byte chunk of a 64-byte k-step
   const int64_t stride = static_cast<int64_t>(K) * 2;
   const unsigned char* wp = reinterpret_cast<const unsigned char*>(B) +
                             (static_cast<int64_t>(e) * N + min(n0 + r16, N - 1)) * stride + g * 16;
+  // A pass covers kGroups*16 token rows; an expert with more rows than that
+  // (more than the bound the kernel was picked for) gets further passes.
+  for (int tok0 = 0; tok0 < all_rows; tok0 += kGroups * 16) {
+  const int rows = min(all_rows - tok0, kGroups * 16);
+  const int groups = (rows + 15) / 16;
   const unsigned char* xp[kGroups];
 #pragma unroll
   for (int j = 0; j < kGroups; ++j)
-    xp[j] = reinterpret_cast<const unsigned char*>(A) + static_cast<int64_t>(seg0 + min(j * 16 + r16, rows - 1)) * stride +
-            g * 16;
-
+    xp[j] = reinterpret_cast<const unsigned char*>(A) +
+            static_cast<int64_t>(seg0 + tok0 + min(j * 16 + r16, rows - 1)) * stride + g * 16;
   f32x4_t acc[kGroups];
 #pragma unroll
   for (int j = 0; j < kGroups; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -705,9 +708,184 @@ __global__ __launch_bounds__(kWave) void grouped_gemm_bf16_skinny(const uint16_t
     float v[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) v[q] = kGelu ? gelu_tanh_fast(acc[j][q]) : acc[j][q];
-    *reinterpret_cast<uint2*>(C + static_cast<int64_t>(seg0 + tok) * N + col) =
+    *reinterpret_cast<uint2*>(C + static_cast<int64_t>(seg0 + tok0 + tok) * N + col) =
         make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
   }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode variant (at most 16 token rows per expert): weight streaming with
+// whole-line loads.  One 16x16x32 MFMA takes as its A operand 4 weight rows x
+// 4 K-slices of 32 (each lane's 16 bytes; the 16 lanes of a row cover 256
+// contiguous bytes of it) and as its B operand 4 token rows x the same 4
+// K-slices.  Of the 16x16 products only the 4x4 diagonal blocks (matching
+// K-slices) are wanted: lane l holds slice l%4 of the pair (weight row l/16,
+// token (l%16)/4) in accumulator l%4, and two lane shuffles finish each dot
+// product.  The 4x redundant MFMA work is cheap here, and in exchange every
+// load instruction reads 4 rows x 256 contiguous bytes, which with the
+// non-temporal policy streams the weights at close to full HBM bandwidth.
+// A wave owns 8 weight rows (2 groups of 4) over the whole K; a block of 4
+// waves owns 32 rows of one active expert.  A pass covers kTG groups of 4
+// token rows; token groups past the expert's row count are skipped (uniform
+// per wave), and an expert with more rows than one pass holds gets further
+// passes, so any row count is computed.
+constexpr int kGvGroups = 2;        // 4-row weight groups per wave
+constexpr int kGvWaves = 4;
+constexpr int kGvRows = kGvWaves * kGvGroups * 4;  // weight rows per block
+constexpr int kGvMaxTok = 16;       // token rows per expert this kernel handles
+
+template <bool kGelu, int kTG>
+__global__ __launch_bounds__(kGvWaves * kWave) void grouped_gemm_bf16_gemv(const uint16_t* __restrict__ A,
+                                                                          const uint16_t* __restrict__ B,
+                                                                          uint16_t* __restrict__ C,
+                                                                          const int32_t* __restrict__ offsets,
+                                                                          int E, int N, int K, int max_rows) {
+  __shared__ int s_tile_base[kMaxExperts + 1];
+  __shared__ int s_seg0[kMaxExperts];
+  __shared__ int s_seg1[kMaxExperts];
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
+  const int n_tiles = (N + kGvRows - 1) / kGvRows;
+  if (tid < kWave) {
+    const int e = lane;
+    int nt = 0, seg0 = 0, seg1 = 0;
+    if (e < E) {
+      seg0 = min(max(offsets[e], 0), max_rows);
+      seg1 = min(max(offsets[e + 1], seg0), max_rows);
+      nt = seg1 > seg0 ? n_tiles : 0;
+    }
+    int incl = nt;
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) {
+      const int o = __shfl_up(incl, m);
+      if (lane >= m) incl += o;
+    }
+    if (e < E) {
+      s_tile_base[e + 1] = incl;
+      s_seg0[e] = seg0;
+      s_seg1[e] = seg1;
+    }
+    if (e == 0) s_tile_base[0] = 0;
+  }
+  __syncthreads();
+  const int tile = blockIdx.x;
+  if (tile >= s_tile_base[E]) return;
+  int e = 0;
+  while (e + 1 < E && s_tile_base[e + 1] <= tile) ++e;
+  const int n0 = (tile - s_tile_base[e]) * kGvRows + wave * kGvGroups * 4;
+  if (n0 >= N) return;  // N is a multiple of 8: a wave's rows are all valid or all past the end
+  const int seg0 = s_seg0[e];
+  const int rows = s_seg1[e] - seg0;
+
+  const int i16 = lane & 15;
+  const int g = lane >> 4;
+  const int row_bytes = K * 2;
+  const int lane_off = 64 * (i16 & 3) + 16 * g;  // byte offset within a 256-byte K-chunk
+  const unsigned char* wp[kGvGroups];
+#pragma unroll
+  for (int rg = 0; rg < kGvGroups; ++rg)
+    wp[rg] = reinterpret_cast<const unsigned char*>(B) +
+             (static_cast<int64_t>(e) * N + n0 + rg * 4 + (i16 >> 2)) * row_bytes + lane_off;
+  constexpr int kU = 2;        // 256-byte K-chunks per step, register double-buffered across steps
+  const int nchunk = K / 128;  // K is a multiple of 128 (checked by the host)
+  const int nstep = nchunk / kU;
+
+  for (int tok0 = 0; tok0 < rows; tok0 += kTG * 4) {
+    const int ntok = min(rows - tok0, kTG * 4);
+    const int ntg = (ntok + 3) / 4;
+    const unsigned char* xp[kTG];
+#pragma unroll
+    for (int tg = 0; tg < kTG; ++tg)
+      xp[tg] = reinterpret_cast<const unsigned char*>(A) +
+               static_cast<int64_t>(seg0 + tok0 + min(tg * 4 + (i16 >> 2), ntok - 1)) * row_bytes + lane_off;
+
+    f32x4_t acc[kGvGroups][kTG];
+#pragma unroll
+    for (int rg = 0; rg < kGvGroups; ++rg)
+#pragma unroll
+      for (int tg = 0; tg < kTG; ++tg) acc[rg][tg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    u32x4_t wa[2][kU][kGvGroups], xa[2][kU][kTG];
+    auto load = [&](int buf, int step) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t off = static_cast<int64_t>(step * kU + u) * 256;
+#pragma unroll
+        for (int rg = 0; rg < kGvGroups; ++rg) wa[buf][u][rg] = ld16_nt(wp[rg] + off);
+#pragma unroll
+        for (int tg = 0; tg < kTG; ++tg)
+          if (tg < ntg) xa[buf][u][tg] = ld16(xp[tg] + off);
+      }
+    };
+    auto mma = [&](int buf) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+#pragma unroll
+        for (int tg = 0; tg < kTG; ++tg)
+          if (tg < ntg) {
+#pragma unroll
+            for (int rg = 0; rg < kGvGroups; ++rg)
+              acc[rg][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wa[buf][u][rg]),
+                                                                    __builtin_bit_cast(bf16x8_t, xa[buf][u][tg]),
+                                                                    acc[rg][tg], 0, 0, 0);
+          }
+    };
+    if (nstep > 0) load(0, 0);
+    int st = 0;
+    for (; st + 2 <= nstep; st += 2) {
+      load(1, st + 1);
+      mma(0);
+      if (st + 2 < nstep) load(0, st + 2);
+      mma(1);
+    }
+    if (st < nstep) mma(0);
+    for (int c = nstep * kU; c < nchunk; ++c) {  // odd chunk count: one chunk left
+      const int64_t off = static_cast<int64_t>(c) * 256;
+      u32x4_t w[kGvGroups];
+#pragma unroll
+      for (int rg = 0; rg < kGvGroups; ++rg) w[rg] = ld16_nt(wp[rg] + off);
+#pragma unroll
+      for (int tg = 0; tg < kTG; ++tg)
+        if (tg < ntg) {
+          const u32x4_t x = ld16(xp[tg] + off);
+#pragma unroll
+          for (int rg = 0; rg < kGvGroups; ++rg)
+            acc[rg][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w[rg]),
+                                                                  __builtin_bit_cast(bf16x8_t, x), acc[rg][tg], 0, 0, 0);
+        }
+    }
+
+    // Lane l keeps accumulator l%4 (matching K-slices) and sums it with lanes
+    // l^1, l^2: lane 16r + 4t then holds weight row 4rg + r, token 4tg + t.
+    const int q = lane & 3;
+#pragma unroll
+    for (int tg = 0; tg < kTG; ++tg) {
+      if (tg >= ntg) break;
+#pragma unroll
+      for (int rg = 0; rg < kGvGroups; ++rg) {
+        float v = q == 0 ? acc[rg][tg][0] : q == 1 ? acc[rg][tg][1] : q == 2 ? acc[rg][tg][2] : acc[rg][tg][3];
+        v += __shfl_xor(v, 1);
+        v += __shfl_xor(v, 2);
+        const int tok = tg * 4 + (i16 >> 2);
+        if (q == 0 && tok < ntok) {
+          if (kGelu) v = gelu_tanh_fast(v);
+          C[static_cast<int64_t>(seg0 + tok0 + tok) * N + n0 + rg * 4 + g] = f32_to_bf16(v);
+        }
+      }
+    }
+  }
+}
+
+template <bool kGelu, int kTG>
+hipError_t launch_gemv(const uint16_t* A, const uint16_t* B, uint16_t* C, const int32_t* offsets, int E, int N, int K,
+                       int max_rows, hipStream_t stream) {
+  const int active = max_rows < E ? max_rows : E;
+  const int64_t blocks = static_cast<int64_t>(active) * ((N + kGvRows - 1) / kGvRows);
+  hipLaunchKernelGGL((grouped_gemm_bf16_gemv<kGelu, kTG>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(kGvWaves * kWave), 0, stream, A, B, C, offsets, E, N, K, max_rows);
+  return hipGetLastError();
 }
 
 template <bool kGelu, int kGroups>
@@ -752,6 +930,16 @@ hipError_t launch_grouped_gemm(int dtype, bool gelu, const void* A, const void* 
     const uint16_t* a = static_cast<const uint16_t*>(A);
     const uint16_t* b = static_cast<const uint16_t*>(B);
     uint16_t* c = static_cast<uint16_t*>(C);
+    const bool gemv_ok = K % 128 == 0 && N % (kGvGroups * 4) == 0;
+    if (gemv_ok && max_tokens_per_expert <= 4)
+      return gelu ? launch_gemv<true, 1>(a, b, c, offsets, E, N, K, max_rows, stream)
+                  : launch_gemv<false, 1>(a, b, c, offsets, E, N, K, max_rows, stream);
+    if (gemv_ok && max_tokens_per_expert <= 8)
+      return gelu ? launch_gemv<true, 2>(a, b, c, offsets, E, N, K, max_rows, stream)
+                  : launch_gemv<false, 2>(a, b, c, offsets, E, N, K, max_rows, stream);
+    if (gemv_ok && max_tokens_per_expert <= kGvMaxTok)
+      return gelu ? launch_gemv<true, 4>(a, b, c, offsets, E, N, K, max_rows, stream)
+                  : launch_gemv<false, 4>(a, b, c, offsets, E, N, K, max_rows, stream);
     if (max_tokens_per_expert <= 16)
       return gelu ? launch_skinny<true, 1>(a, b, c, offsets, E, N, K, max_rows, stream)
                   : launch_skinny<false, 1>(a, b, c, offsets, E, N, K, max_rows, stream);

@@ -141,6 +141,47 @@ def test_expert_up_down(case):
     assert (H[N:] == 0).all() and (Yp[N:] == 0).all()
 
 
+@pytest.mark.parametrize("d,F,cap", [(256, 384, 4), (256, 384, 8), (256, 384, 16), (192, 320, 16)],
+                         ids=["gemv_tok4", "gemv_tok8", "gemv_tok16", "skinny_tok16"])
+def test_expert_rows_beyond_the_bound(d, F, cap):
+    """The few-rows expert kernels are chosen by a bound on rows per expert
+    (here the capacity in the config); offsets that give some experts more
+    rows than that must still be computed in full (extra passes), not
+    clipped.  d = 192 (not a multiple of 128) takes the 16-row-tile kernel."""
+    E, k, T = 8, 2, 30
+    counts = np.array([25, 0, 3, 17, 1, 6, 0, 8])
+    Tk = T * k
+    assert counts.sum() == Tk
+    offsets_np = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    inp = workloads.random_case(91, T, d, E, k, F, "bf16", -1, 0.0, w_scale=0.05)
+    Xf = oracle.as_f64(inp.X, "bf16")
+    rows = np.random.default_rng(5).permutation(np.repeat(np.arange(T), k))
+    Xp64 = Xf[rows]
+    H_ref = np.zeros((Tk, F))
+    for e in range(E):
+        a, b = offsets_np[e], offsets_np[e + 1]
+        if b > a:
+            H_ref[a:b] = oracle.gelu_tanh(Xp64[a:b] @ oracle.as_f64(inp.W1[e], "bf16").T)
+    H_in = round_to(H_ref, "bf16")
+    Y_ref = np.zeros((Tk, d))
+    for e in range(E):
+        a, b = offsets_np[e], offsets_np[e + 1]
+        if b > a:
+            Y_ref[a:b] = H_in[a:b] @ oracle.as_f64(inp.W2[e], "bf16").T
+    cfg = moe.config(T, d, F, E, k, cap, "bf16")
+    Xp = torch.from_numpy(Xp64).to(torch.bfloat16).cuda()
+    offsets = torch.from_numpy(offsets_np).cuda()
+    H = torch.zeros((Tk, F), dtype=torch.bfloat16, device="cuda")
+    moe.moe_expert_up(cfg, Xp, offsets, to_dev(inp.W1, "bf16"), H)
+    Yp = torch.zeros((Tk, d), dtype=torch.bfloat16, device="cuda")
+    moe.moe_expert_down(cfg, torch.from_numpy(H_in).to(torch.bfloat16).cuda(), offsets, to_dev(inp.W2, "bf16"), Yp)
+    torch.cuda.synchronize()
+    eh = row_rel_err(dev_to_f64(H), H_ref)
+    assert eh.max() <= rel_tol("bf16"), f"H rel err {eh.max():.3g} (worst row {int(eh.argmax())})"
+    ey = row_rel_err(dev_to_f64(Yp), Y_ref)
+    assert ey.max() <= rel_tol("bf16"), f"Yp rel err {ey.max():.3g} (worst row {int(ey.argmax())})"
+
+
 @pytest.mark.parametrize("case", CASES, ids=IDS)
 def test_combine(case):
     inp, cfg = make(case)
