@@ -17,6 +17,8 @@
 // fragment reads of 8 consecutive rows hit distinct banks.  Each wave owns a
 // (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA tiles.  The reduction order over K
 // is a fixed permutation of the plain order, the same on A and B.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -281,7 +283,7 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
 }
 
 struct TileCoord {
-  int e, m0, n0, seg1;
+  int e, m0, n0, rows;  // rows: the tile's token rows [m0, m0 + rows)
 };
 
 template <bool kGelu>
@@ -301,11 +303,16 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
   // Expert table, held by every wave in registers: lane e has expert e's row
   // segment [seg0, seg1) (clamped to [0, max_rows]: offsets come from device
   // memory) and the running count of m-tiles before and through it.
-  int t_seg0 = 0, t_seg1 = 0, t_mt = 0;
+  // An expert of R rows gets ceil(R/256) m-tiles of equal height (rounded
+  // up to 64 rows, the last one shorter): a 530-row expert runs tiles of
+  // 192, 192 and 146 rows rather than 256, 256 and 18, and each tile runs
+  // only as many 32-row token fragments as it has rows.
+  int t_seg0 = 0, t_seg1 = 0, t_mt = 0, t_h = kBig;
   if (lane < E) {
     t_seg0 = min(max(offsets[lane], 0), max_rows);
     t_seg1 = min(max(offsets[lane + 1], t_seg0), max_rows);
     t_mt = (t_seg1 - t_seg0 + kBig - 1) / kBig;
+    if (t_mt > 0) t_h = min(kBig, ((t_seg1 - t_seg0 + t_mt - 1) / t_mt + 63) & ~63);
   }
   int t_incl = t_mt;
 #pragma unroll
@@ -340,8 +347,8 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
     TileCoord t;
     t.e = e;
     t.n0 = (in / gsize) * kBig;
-    t.m0 = __builtin_amdgcn_readlane(t_seg0, e) + (first_m + in % gsize) * kBig;
-    t.seg1 = __builtin_amdgcn_readlane(t_seg1, e);
+    t.m0 = __builtin_amdgcn_readlane(t_seg0, e) + (first_m + in % gsize) * __builtin_amdgcn_readlane(t_h, e);
+    t.rows = min(__builtin_amdgcn_readlane(t_h, e), __builtin_amdgcn_readlane(t_seg1, e) - t.m0);
     return t;
   };
 
@@ -377,7 +384,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
     if (s.tile < total) {
       const TileCoord t = coord(s.tile);
       s.base = Ab + static_cast<int64_t>(t.m0) * row_stride;
-      s.rows = min(t.seg1 - t.m0, kBig);
+      s.rows = t.rows;
     } else {
       s.rows = 0;
     }
@@ -429,26 +436,38 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
   const int kw = key_w(wrow);  // = key_w of every weight row this lane reads
   int c_wslot = 0, c_xslot = 1;
 
-  // Fragments of one 16-element k-step: 4 weight and 4 token fragments.
+  // Fragments of one 16-element k-step: 4 weight and up to 4 token
+  // fragments.  Token fragment j of this wave covers tile rows
+  // (2j + wm)*32 .. +31: the two token-half waves interleave, so a tile of R
+  // rows has ceil(R/32) fragments with rows and each wave runs
+  // nj = ceil(ceil(R/32)/2) of them (both waves the same count, so the
+  // per-stage barrier costs no idle MFMA time).
   u32x4_t wf0[4], xf0[4], wf1[4], xf1[4];
   auto frag_addr_w = [&](int kk, int i) {
     return smem + c_wslot * kUnitBytes + (wn * 128 + i * 32 + wrow) * kUnitRow + (((kk * 2 + fhalf) ^ kw) << 4);
   };
   auto frag_addr_x = [&](int kk, int j) {
-    return smem + c_xslot * kUnitBytes + (wm * 128 + j * 32 + frow) * kUnitRow + (((kk * 2 + fhalf) ^ kx) << 4);
+    return smem + c_xslot * kUnitBytes + ((2 * j + wm) * 32 + frow) * kUnitRow + (((kk * 2 + fhalf) ^ kx) << 4);
   };
-  auto read_frags = [&](int kk, u32x4_t (&wf)[4], u32x4_t (&xf)[4]) {
+  auto read_frags = [&](auto nj_c, int kk, u32x4_t (&wf)[4], u32x4_t (&xf)[4]) {
+    constexpr int NJ = decltype(nj_c)::value;
 #pragma unroll
     for (int i = 0; i < 4; ++i) wf[i] = *reinterpret_cast<const u32x4_t*>(frag_addr_w(kk, i));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xf[j] = *reinterpret_cast<const u32x4_t*>(frag_addr_x(kk, j));
+    for (int j = 0; j < NJ; ++j) xf[j] = *reinterpret_cast<const u32x4_t*>(frag_addr_x(kk, j));
   };
-  // One k-step block, in a fixed issue order: its 16 MFMAs, with the 8
-  // fragment reads of k-step `kk_next` (into wn/xn) after the first 8 MFMAs
-  // one by one and, if `s` is given, a unit's 8 buffer->LDS loads likewise,
-  // so neither the LDS nor the load queue ever holds up the MFMA stream.
-  auto block = [&](f32x16_t (&acc)[4][4], const u32x4_t (&wa)[4], const u32x4_t (&xa)[4], int kk_next,
+  // One k-step block, in a fixed issue order: its 4*NJ MFMAs, with the 4+NJ
+  // fragment reads of k-step `kk_next` (into wn/xn) spread over the first
+  // half of them and, if `s` is given, a unit's 8 buffer->LDS loads spread
+  // over the first 8, so neither the LDS nor the load queue holds up the
+  // MFMA stream.
+  auto block = [&](auto nj_c, f32x16_t (&acc)[4][4], const u32x4_t (&wa)[4], const u32x4_t (&xa)[4], int kk_next,
                    u32x4_t (&wn_)[4], u32x4_t (&xn_)[4], const Stream* s, const int* voff) {
+    constexpr int NJ = decltype(nj_c)::value;
+    constexpr int kM = 4 * NJ;
+    constexpr int kR = 4 + NJ;
+    constexpr int kRq = kM / 2;
+    constexpr int kLq = kM < 8 ? kM : 8;
     __amdgpu_buffer_rsrc_t rsrc;
     unsigned char* dst = smem;
     if (s != nullptr) {
@@ -458,15 +477,21 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
       dst = smem + s->slot * kUnitBytes + wave * 64 * kUnitRow;
     }
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int i = q >> 2, j = q & 3;
+    for (int q = 0; q < kM; ++q) {
+      const int i = q / NJ, j = q % NJ;
       acc[i][j] = GemmMma<uint16_t>::run(wa[i], xa[j], acc[i][j]);
-      if (kk_next >= 0) {
-        if (q < 4) wn_[q] = *reinterpret_cast<const u32x4_t*>(frag_addr_w(kk_next, q));
-        else if (q < 8) xn_[q - 4] = *reinterpret_cast<const u32x4_t*>(frag_addr_x(kk_next, q - 4));
+      if (kk_next >= 0 && q < kRq) {
+#pragma unroll
+        for (int r = q * kR / kRq; r < (q + 1) * kR / kRq; ++r) {
+          if (r < 4) wn_[r] = *reinterpret_cast<const u32x4_t*>(frag_addr_w(kk_next, r));
+          else xn_[r - 4] = *reinterpret_cast<const u32x4_t*>(frag_addr_x(kk_next, r - 4));
+        }
       }
-      if (s != nullptr && q < 8)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(dst + q * 8 * kUnitRow), 16, voff[q], 0, 0, 0);
+      if (s != nullptr && q < kLq) {
+#pragma unroll
+        for (int l = q * 8 / kLq; l < (q + 1) * 8 / kLq; ++l)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(dst + l * 8 * kUnitRow), 16, voff[l], 0, 0, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -480,11 +505,13 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
   // 16 loads, may still be in flight).
   wait_vmcnt<16>();
   barrier();
-  read_frags(0, wf0, xf0);
   bool after_epilogue = false;
 
-  for (int tile = first; tile < total; tile += G) {
-    const TileCoord tc = coord(tile);
+  // One tile: all K stages with nj token fragments per wave, then its
+  // epilogue.  k-step 0 of the tile's first stage is read here (the previous
+  // tile's last block read it with that tile's nj).
+  auto run_tile = [&](auto nj_c, const TileCoord& tc) {
+    constexpr int NJ = decltype(nj_c)::value;
     f32x16_t acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -492,14 +519,15 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+    read_frags(nj_c, 0, wf0, xf0);
 
     for (int ks = 0; ks < kstages; ++ks) {
       // k-step 0 of this stage is in wf0/xf0.  Its block also issues the
       // weight unit two stages ahead.
-      block(acc, wf0, xf0, 1, wf1, xf1, &ws, vw);
+      block(nj_c, acc, wf0, xf0, 1, wf1, xf1, &ws, vw);
       advance_w(ws);
-      block(acc, wf1, xf1, 2, wf0, xf0, nullptr, nullptr);
-      block(acc, wf0, xf0, 3, wf1, xf1, nullptr, nullptr);
+      block(nj_c, acc, wf1, xf1, 2, wf0, xf0, nullptr, nullptr);
+      block(nj_c, acc, wf0, xf0, 3, wf1, xf1, nullptr, nullptr);
       // The next stage must have landed; the weight unit issued above may stay
       // in flight (right after an epilogue its stores are outstanding too:
       // drain).  lgkmcnt(0): this wave's reads of this stage are complete, so
@@ -514,30 +542,29 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
       // Refill a freed slot with the token unit of the stage after next, and
       // read k-step 0 of the next stage (past the last stage: a free slot
       // whose values go unused).
-      block(acc, wf1, xf1, 0, wf0, xf0, &xs, vx);
+      block(nj_c, acc, wf1, xf1, 0, wf0, xf0, &xs, vx);
       advance_x(xs);
     }
     after_epilogue = true;
 
-    // acc[i][j][q]: token row m0 + wm*128 + j*32 + frow, column n0 + wn*128 + i*32 + 16*fhalf + q.
-    // Stores go through a buffer resource over the tile's valid rows of C;
-    // a column past N gets an offset beyond the range.  The hardware drops
+    // acc[i][j][q]: token row m0 + (2j + wm)*32 + frow, column n0 + wn*128 + i*32 + 16*fhalf + q.
+    // Stores go through a buffer resource over the tile's rows of C; a
+    // column past N gets an offset beyond the range.  The hardware drops
     // out-of-range stores, so the epilogue has no branches and each group of
     // 16 accumulators is read, converted and stored before the next.
-    const int vrows = min(tc.seg1 - tc.m0, kBig);
     const __amdgpu_buffer_rsrc_t crsrc = __builtin_amdgcn_make_buffer_rsrc(
-        C + static_cast<int64_t>(tc.m0) * N, 0, vrows * N * 2, kRsrcWord3);
+        C + static_cast<int64_t>(tc.m0) * N, 0, tc.rows * N * 2, kRsrcWord3);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int roff = (wm * 128 + j * 32 + frow) * N * 2;
+    for (int j = 0; j < NJ; ++j) {
+      const int roff = ((2 * j + wm) * 32 + frow) * N * 2;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int col = tc.n0 + wn * 128 + i * 32 + 16 * fhalf;
         const int off = col < N ? roff + col * 2 : static_cast<int>(0x80000000u);
         // Redefine the group's accumulators here (an empty asm on their
         // registers), after the previous group's stores: otherwise the
-        // compiler copies all 256 out of the accumulator registers at the loop
-        // exit and runs out of registers for the GELU.
+        // compiler copies all of them out of the accumulator registers at the
+        // loop exit and runs out of registers for the GELU.
         asm volatile("" : "+a"(acc[i][j])::"memory");
         float v[16];
 #pragma unroll
@@ -553,6 +580,15 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+  };
+
+  for (int tile = first; tile < total; tile += G) {
+    const TileCoord tc = coord(tile);
+    const int nj = (((tc.rows + 31) >> 5) + 1) >> 1;  // 1..4
+    if (nj >= 4) run_tile(std::integral_constant<int, 4>{}, tc);
+    else if (nj == 3) run_tile(std::integral_constant<int, 3>{}, tc);
+    else if (nj == 2) run_tile(std::integral_constant<int, 2>{}, tc);
+    else run_tile(std::integral_constant<int, 1>{}, tc);
   }
   wait_vmcnt<0>();
 }
