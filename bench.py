@@ -4,11 +4,13 @@
 
 A step is one moe_forward (router, dispatch, expert GEMM1+GELU, GEMM2,
 combine) over one batch of seeded synthetic inputs that are resident in HBM
-before the timed region starts.  Prints one JSON line: tokens/s of the whole
-layer, the roofline fraction of the dominant kernel (HIP events over the
-timed region on the stream the kernels run on), per-stage times, and the CPU
-oracle timed on a bounded sample of the same workload (a baseline, not the
-target).
+before the timed region starts.  The headline times K steps captured in one
+HIP graph and replayed.  Each stage entry point is then timed on its own: K
+back-to-back launches between two HIP events on the stream the kernels run
+on, which gives the kernels' average duration without host gaps.  Prints one
+JSON line: tokens/s of the whole layer, the roofline fraction of the dominant
+kernel, per-stage times, and the CPU oracle timed on a bounded sample of the
+same workload (a baseline, not the target).
 """
 from __future__ import annotations
 
@@ -32,16 +34,16 @@ METRIC = "MoE-layer tokens/sec at 1 GPU; % bf16 MFMA peak (FFN) / % HBM peak (re
 # WRITE_SIZE (KiB per dispatch), scaled by what the same counters read for a
 # plain 1 GiB device copy (FETCH_SIZE x2.0, WRITE_SIZE x1.0); valid only for
 # the GEMM source they were taken on (sha1 prefix), else reported as null.
-TRAFFIC_SOURCE_SHA1 = "a4b2dbc6bb48"
+TRAFFIC_SOURCE_SHA1 = "7beb2593f2b0"
 TRAFFIC_BYTES = {  # (workload, stage) -> (fetch KiB, write KiB) per dispatch, raw counter values
-    ("prefill", "expert_up"): (540435.8, 193243.2),
-    ("prefill", "expert_down"): (711703.8, 65562.2),
-    ("capacity", "expert_up"): (891743.6, 301959.9),
-    ("capacity", "expert_down"): (752908.2, 417563.5),
-    ("skewed", "expert_up"): (9385058.7, 976436.1),
-    ("skewed", "expert_down"): (9011081.1, 262520.5),
-    ("decode", "expert_up"): (123405.9, 80.0),
-    ("decode", "expert_down"): (123581.7, 112.0),
+    ("prefill", "expert_up"): (479415.8, 180233.8),
+    ("prefill", "expert_down"): (585044.9, 65536.2),
+    ("capacity", "expert_up"): (879138.4, 285272.4),
+    ("capacity", "expert_down"): (698102.3, 415763.4),
+    ("skewed", "expert_up"): (7289498.0, 918639.6),
+    ("skewed", "expert_down"): (6444369.1, 262182.7),
+    ("decode", "expert_up"): (123368.4, 80.0),
+    ("decode", "expert_down"): (123236.6, 112.0),
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 
@@ -55,6 +57,23 @@ def gemm_traffic(workload, stage):
         return None
     fetch, write = TRAFFIC_BYTES[(workload, stage)]
     return round((fetch * FETCH_SCALE + write * WRITE_SCALE) * 1024)
+
+
+def gemm_kernel_name(w, capacity, stage):
+    """The expert-GEMM kernel the library runs for this shape (its selection
+    rule: bf16 with at most min(T, C) rows per expert picks the few-rows
+    kernels)."""
+    gelu = "true" if stage == "expert_up" else "false"
+    K = w.d if stage == "expert_up" else w.F
+    N = w.F if stage == "expert_up" else w.d
+    if w.dtype != "bf16":
+        return f"grouped_gemm_kernel<float, 64, 64, 2, 2, {gelu}>"
+    bound = w.T if capacity < 0 else min(w.T, capacity)
+    if K % 128 == 0 and N % 8 == 0 and bound <= 16:
+        return f"grouped_gemm_bf16_gemv<{gelu}, {1 if bound <= 4 else 2 if bound <= 8 else 4}>"
+    if bound <= 64:
+        return f"grouped_gemm_bf16_skinny<{gelu}, {1 if bound <= 16 else 2 if bound <= 32 else 4}>"
+    return f"grouped_gemm_bf16_256<{gelu}>"
 
 
 def parse():
@@ -204,33 +223,42 @@ def main():
         stream = torch.cuda.current_stream()
     ms_step, wall = (eager_ms, eager_wall) if graph_ms is None else (graph_ms, graph_wall)
 
-    # ---- per-stage: the same K steps through the stage entry points, events between stages
-    Xp, H, Yp = b.workspace_view(cfg, "Xp"), b.workspace_view(cfg, "H"), b.workspace_view(cfg, "Yp")
+    # ---- per-stage kernel times: each stage entry point is launched K times
+    # back to back between two HIP events on the launch stream, so the queue
+    # stays full and the interval is the kernels' own time (no host gaps).
+    # Inputs come from forwards of the benchmark's own batches; for
+    # decode-sized layers the stages rotate over up to 4 routings of
+    # consecutive batches, so the expert weights streamed change from launch
+    # to launch as they do in decoding.
     names = ["route", "dispatch", "expert_up", "expert_down", "combine"]
-    stage_ms = {n: 0.0 for n in names}
     rws, rbytes = b.scratch_view(cfg, "route"), moe.moe_workspace_size(cfg, moe.MOE_OP_ROUTE)
     dws, dbytes = b.scratch_view(cfg, "dispatch"), moe.moe_workspace_size(cfg, moe.MOE_OP_DISPATCH)
-    per_step_active, per_step_N = [], []
-    for i in range(args.steps):
-        X = xs[i % len(xs)]
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-        evs[0].record(stream)
-        moe.moe_route(cfg, X, Wg, bias, b.topk_ids, b.topk_w, rws, rbytes)
-        evs[1].record(stream)
-        moe.moe_dispatch(cfg, b.topk_ids, X, b.expert_counts, b.expert_offsets, b.perm, b.inv_perm, Xp, dws, dbytes)
-        evs[2].record(stream)
-        moe.moe_expert_up(cfg, Xp, b.expert_offsets, W1, H)
-        evs[3].record(stream)
-        moe.moe_expert_down(cfg, H, b.expert_offsets, W2, Yp)
-        evs[4].record(stream)
-        moe.moe_combine(cfg, Yp, b.inv_perm, b.topk_w, b.out)
-        evs[5].record(stream)
+    Xp_ws, H_ws, Yp_ws = b.workspace_view(cfg, "Xp"), b.workspace_view(cfg, "H"), b.workspace_view(cfg, "Yp")
+    small = w.T * w.k * max(w.d, w.F) * es <= (64 << 20)
+    nsets = min(4, len(xs)) if small else 1
+    sets, per_step_N, per_step_active = [], [], []
+    for si in range(nsets):
+        layer.forward(xs[si])
         torch.cuda.synchronize()
-        for j, n in enumerate(names):
-            stage_ms[n] += evs[j].elapsed_time(evs[j + 1]) / args.steps
+        keep = (lambda t: t.clone()) if nsets > 1 else (lambda t: t)
+        sets.append({"X": xs[si], "ids": keep(b.topk_ids), "w": keep(b.topk_w), "off": keep(b.expert_offsets),
+                     "inv": keep(b.inv_perm), "Xp": keep(Xp_ws), "H": keep(H_ws), "Yp": keep(Yp_ws)})
         off = b.expert_offsets.cpu().numpy()
         per_step_N.append(int(off[-1]))
         per_step_active.append(int((np.diff(off) > 0).sum()))
+    stage_fn = {
+        "route": lambda q: moe.moe_route(cfg, q["X"], Wg, bias, b.topk_ids, b.topk_w, rws, rbytes),
+        "dispatch": lambda q: moe.moe_dispatch(cfg, q["ids"], q["X"], b.expert_counts, b.expert_offsets, b.perm,
+                                               b.inv_perm, Xp_ws, dws, dbytes),
+        "expert_up": lambda q: moe.moe_expert_up(cfg, q["Xp"], q["off"], W1, q["H"]),
+        "expert_down": lambda q: moe.moe_expert_down(cfg, q["H"], q["off"], W2, q["Yp"]),
+        "combine": lambda q: moe.moe_combine(cfg, q["Yp"], q["inv"], q["w"], b.out),
+    }
+    stage_ms = {}
+    for n in names:
+        fn = stage_fn[n]
+        fn(sets[0])  # untimed
+        stage_ms[n], _ = timed(lambda: [fn(sets[i % nsets]) for i in range(args.steps)])
 
     N = float(np.mean(per_step_N))
     active = float(np.mean(per_step_active))
@@ -257,7 +285,7 @@ def main():
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = gemm_traffic(w.name, dom)
     roof["algorithmic_bytes"] = round(work[dom]["bytes"])
-    roof["kernel"] = ("grouped_gemm_kernel (GEMM1+GELU)" if dom == "expert_up" else "grouped_gemm_kernel (GEMM2)")
+    roof["kernel"] = gemm_kernel_name(w, inp.expert_capacity, dom)
     roof["ms"] = round(ms, 5)
 
     cpu = None

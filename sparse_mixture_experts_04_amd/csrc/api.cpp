@@ -62,21 +62,13 @@ size_t dispatch_bytes(const moe_config* c) {
 size_t h_bytes(const moe_config* c) { return align256(pairs_of(c) * c->intermediate_size * esize(c)); }
 size_t xp_bytes(const moe_config* c) { return align256(pairs_of(c) * c->hidden_size * esize(c)); }
 
-// Rows one expert can hold: every (token, slot) pair at most (ids given to
-// moe_dispatch may repeat an expert within a token), and at most C under a
-// capacity.
+// Bound on the rows one expert holds, used only to pick the expert-GEMM
+// variant: routing picks k distinct experts per token, so at most T rows per
+// expert (and at most C under a capacity).  The expert kernels compute any
+// row count correctly -- an expert beyond the bound costs extra passes -- so
+// offsets from repeated ids (a caller's own ids, or non-finite logits) stay
+// in bounds and are computed in full.
 int rows_per_expert_bound(const moe_config* c) {
-  int b = static_cast<int>(pairs_of(c));
-  if (c->expert_capacity >= 0 && c->expert_capacity < b) b = c->expert_capacity;
-  return b;
-}
-
-// The same bound for the layer's own routing, which picks k distinct experts
-// per token: at most T rows per expert (and at most C).  It only selects the
-// kernel variant: the expert kernels compute any row count correctly (an
-// expert beyond the bound costs extra passes), so repeated ids from
-// non-finite logits stay in bounds and are computed.
-int routed_rows_bound(const moe_config* c) {
   int b = c->num_tokens;
   if (c->expert_capacity >= 0 && c->expert_capacity < b) b = c->expert_capacity;
   return b;
@@ -218,18 +210,8 @@ moe_status moe_forward(const moe_config* cfg, const void* X, const void* Wg, con
       s != MOE_OK)
     return s;
   if (cfg->num_tokens == 0) return MOE_OK;
-  const int pairs = static_cast<int>(pairs_of(cfg));
-  const int bound = routed_rows_bound(cfg);
-  if (hipError_t e = moe::launch_grouped_gemm(cfg->dtype, true, Xp, W1, H, expert_offsets, cfg->num_experts,
-                                              cfg->intermediate_size, cfg->hidden_size, pairs, bound,
-                                              as_stream(stream));
-      e != hipSuccess)
-    return MOE_ERR_HIP;
-  if (hipError_t e = moe::launch_grouped_gemm(cfg->dtype, false, H, W2, Yp, expert_offsets, cfg->num_experts,
-                                              cfg->hidden_size, cfg->intermediate_size, pairs, bound,
-                                              as_stream(stream));
-      e != hipSuccess)
-    return MOE_ERR_HIP;
+  if (moe_status s = moe_expert_up(cfg, Xp, expert_offsets, W1, H, stream); s != MOE_OK) return s;
+  if (moe_status s = moe_expert_down(cfg, H, expert_offsets, W2, Yp, stream); s != MOE_OK) return s;
   return moe_combine(cfg, Yp, inv_perm, topk_w, out, stream);
 }
 
