@@ -203,12 +203,32 @@ moe_status moe_forward(const moe_config* cfg, const void* X, const void* Wg, con
   void* H = p;
   p += h_bytes(cfg);
   void* Yp = p;
-  if (moe_status s = moe_route(cfg, X, Wg, gate_bias, topk_ids, topk_w, rws, route_bytes(cfg), stream); s != MOE_OK)
-    return s;
-  if (moe_status s = moe_dispatch(cfg, topk_ids, X, expert_counts, expert_offsets, perm, inv_perm, Xp, dws,
-                                  dispatch_bytes(cfg), stream);
-      s != MOE_OK)
-    return s;
+  const moe::RouterSplit split =
+      moe::router_split(cfg->num_tokens, cfg->hidden_size, cfg->num_experts, cfg->dtype, rws);
+  if (split.partial != nullptr && moe::dispatch_is_single_block(cfg->num_tokens, cfg->num_experts_per_tok)) {
+    // Small batch with a K-split router: the router writes its partial
+    // logits only, and one block selects and dispatches (one launch fewer,
+    // same results as moe_route followed by moe_dispatch).
+    if (hipError_t e = moe::launch_router(cfg->dtype, X, Wg, gate_bias, cfg->num_tokens, cfg->hidden_size,
+                                          cfg->num_experts, cfg->num_experts_per_tok, topk_ids, topk_w, rws,
+                                          as_stream(stream), /*select=*/false);
+        e != hipSuccess)
+      return MOE_ERR_HIP;
+    if (hipError_t e = moe::launch_topk_dispatch_small(
+            cfg->dtype, split.partial, split.nsplit, gate_bias, topk_ids, topk_w, X, cfg->num_tokens,
+            cfg->hidden_size, cfg->num_experts, cfg->num_experts_per_tok, cfg->expert_capacity, expert_counts,
+            expert_offsets, perm, inv_perm, Xp, as_stream(stream));
+        e != hipSuccess)
+      return MOE_ERR_HIP;
+  } else {
+    if (moe_status s = moe_route(cfg, X, Wg, gate_bias, topk_ids, topk_w, rws, route_bytes(cfg), stream);
+        s != MOE_OK)
+      return s;
+    if (moe_status s = moe_dispatch(cfg, topk_ids, X, expert_counts, expert_offsets, perm, inv_perm, Xp, dws,
+                                    dispatch_bytes(cfg), stream);
+        s != MOE_OK)
+      return s;
+  }
   if (cfg->num_tokens == 0) return MOE_OK;
   if (moe_status s = moe_expert_up(cfg, Xp, expert_offsets, W1, H, stream); s != MOE_OK) return s;
   if (moe_status s = moe_expert_down(cfg, H, expert_offsets, W2, Yp, stream); s != MOE_OK) return s;

@@ -22,6 +22,7 @@
 // offsets) -> keep -> scan of kept counts -> scatter.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "topk.hpp"
 
 namespace moe {
 namespace {
@@ -279,13 +280,15 @@ __global__ __launch_bounds__(kScatterThreads) void dispatch_scatter_kernel(
 constexpr int kSmallMaxT = 4 * kDispatchChunk;
 constexpr int kSmallMaxK = 8;
 
-template <typename T, bool kCap>
-__global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __restrict__ ids, const T* __restrict__ X,
-                                                             int T_tok, int d, int E, int k, int capacity,
-                                                             int32_t* __restrict__ counts,
-                                                             int32_t* __restrict__ offsets,
-                                                             int32_t* __restrict__ perm,
-                                                             int32_t* __restrict__ inv_perm, T* __restrict__ Xp) {
+// Run by a whole block of kThreads (>= 256) threads: the index work uses the
+// first 4 waves (one 64-token chunk each; the other waves hold no tokens), the
+// row copy uses every thread.  Xp == nullptr skips the copy.
+template <int kThreads, typename T, bool kCap>
+__device__ __forceinline__ void dispatch_small_block(const int32_t* __restrict__ ids, const T* __restrict__ X,
+                                                     int T_tok, int d, int E, int k, int capacity,
+                                                     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
+                                                     T* __restrict__ Xp) {
   // per chunk, per (slot, expert): pairs, then exclusive prefix over chunks
   __shared__ int s_cnt[4][kSmallMaxK * kMaxExperts];
   __shared__ int s_slot_base[kSmallMaxK * kMaxExperts];  // capacity: pairs of e in slots < s
@@ -293,13 +296,13 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __re
   __shared__ int s_off[kMaxExperts + 1];
   __shared__ int s_row[kSmallMaxT][kSmallMaxK];
   const int lane = threadIdx.x % kWave;
-  const int chunk = threadIdx.x / kWave;
+  const int chunk = threadIdx.x / kWave;   // waves 4.. hold no tokens (t >= 256 >= T_tok)
   const int t = chunk * kDispatchChunk + lane;
   const uint64_t below = (1ull << lane) - 1ull;
   const int cols = k * E;
 
-  for (int i = threadIdx.x; i < 4 * kSmallMaxK * kMaxExperts; i += 256) (&s_cnt[0][0])[i] = 0;
-  for (int i = threadIdx.x; i < 4 * kMaxExperts; i += 256) (&s_kept[0][0])[i] = 0;
+  for (int i = threadIdx.x; i < 4 * kSmallMaxK * kMaxExperts; i += kThreads) (&s_cnt[0][0])[i] = 0;
+  for (int i = threadIdx.x; i < 4 * kMaxExperts; i += kThreads) (&s_kept[0][0])[i] = 0;
   __syncthreads();
   int e[kSmallMaxK];
 #pragma unroll
@@ -312,7 +315,7 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __re
   }
   __syncthreads();
   // exclusive prefix over the 4 chunks per column; column totals
-  for (int c = threadIdx.x; c < cols; c += 256) {
+  for (int c = threadIdx.x; c < cols; c += kThreads) {
     int acc = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -414,9 +417,44 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __re
     }
   }
   if (threadIdx.x <= E) offsets[threadIdx.x] = s_off[threadIdx.x];
-  for (int r = s_off[E] + threadIdx.x; r < Tk; r += 256) perm[r] = -1;
+  for (int r = s_off[E] + threadIdx.x; r < Tk; r += kThreads) perm[r] = -1;
   __syncthreads();
-  copy_rows<256>(X, Xp, d, k, 0, T_tok, &s_row[0][0], kSmallMaxK);
+  if (Xp != nullptr) copy_rows<kThreads>(X, Xp, d, k, 0, T_tok, &s_row[0][0], kSmallMaxK);
+}
+
+template <typename T, bool kCap>
+__global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __restrict__ ids, const T* __restrict__ X,
+                                                             int T_tok, int d, int E, int k, int capacity,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ perm,
+                                                             int32_t* __restrict__ inv_perm, T* __restrict__ Xp) {
+  dispatch_small_block<256, T, kCap>(ids, X, T_tok, d, E, k, capacity, counts, offsets, perm, inv_perm, Xp);
+}
+
+// Top-k of a K-split router plus the whole dispatch, in one block of 1024
+// threads: 16 tokens at a time, every thread sums one (token, expert) entry
+// of the partial logits in split order and wave 0 selects; then the
+// dispatch of all T tokens (the ids just written are visible to the block
+// after the barrier).
+template <typename T, bool kCap, int NT>
+__global__ __launch_bounds__(1024) void topk_dispatch_small_kernel(const float* __restrict__ partial, int nsplit,
+                                                                   const float* __restrict__ bias,
+                                                                   int32_t* __restrict__ ids, float* __restrict__ w,
+                                                                   const T* __restrict__ X, int T_tok, int d, int E,
+                                                                   int k, int capacity, int32_t* __restrict__ counts,
+                                                                   int32_t* __restrict__ offsets,
+                                                                   int32_t* __restrict__ perm,
+                                                                   int32_t* __restrict__ inv_perm,
+                                                                   T* __restrict__ Xp) {
+  __shared__ float logit[16][kMaxExperts];
+  __shared__ float sel_val[16 * kMaxExperts];
+  __shared__ int sel_id[16 * kMaxExperts];
+  for (int tok0 = 0; tok0 < T_tok; tok0 += 16) {
+    topk_from_partials<NT>(partial, nsplit, bias, T_tok, E, k, tok0, logit, sel_val, sel_id, ids, w);
+    __syncthreads();
+  }
+  dispatch_small_block<1024, T, kCap>(ids, X, T_tok, d, E, k, capacity, counts, offsets, perm, inv_perm, Xp);
 }
 
 template <typename T, int KMAX>
@@ -473,13 +511,56 @@ DispatchScratch carve_dispatch_scratch(void* ws, int T, int E, int k, bool capac
   return s;
 }
 
+bool dispatch_is_single_block(int T, int k) { return T > 0 && T <= kSmallMaxT && k <= kSmallMaxK; }
+
+namespace {
+template <typename T, bool kCap>
+hipError_t launch_topk_dispatch_t(const float* partial, int nsplit, const float* bias, int32_t* ids, float* w,
+                                  const T* X, int T_tok, int d, int E, int k, int capacity, int32_t* counts,
+                                  int32_t* offsets, int32_t* perm, int32_t* inv_perm, T* Xp, hipStream_t stream) {
+#define MOE_TOPK_DISPATCH(NT)                                                                                      \
+  hipLaunchKernelGGL((topk_dispatch_small_kernel<T, kCap, NT>), dim3(1), dim3(1024), 0, stream, partial, nsplit, \
+                     bias, ids, w, X, T_tok, d, E, k, capacity, counts, offsets, perm, inv_perm, Xp)
+  switch ((E + 15) / 16) {
+    case 1: MOE_TOPK_DISPATCH(1); break;
+    case 2: MOE_TOPK_DISPATCH(2); break;
+    case 3: MOE_TOPK_DISPATCH(3); break;
+    default: MOE_TOPK_DISPATCH(4); break;
+  }
+#undef MOE_TOPK_DISPATCH
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_topk_dispatch_small(int dtype, const float* partial, int nsplit, const float* bias, int32_t* ids,
+                                      float* w, const void* X, int T, int d, int E, int k, int capacity,
+                                      int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* Xp,
+                                      hipStream_t stream) {
+  if (!dispatch_is_single_block(T, k) || partial == nullptr) return hipErrorInvalidValue;
+  const bool cap = capacity >= 0;
+  if (dtype == kDtypeBF16) {
+    const uint16_t* x = static_cast<const uint16_t*>(X);
+    uint16_t* xp = static_cast<uint16_t*>(Xp);
+    return cap ? launch_topk_dispatch_t<uint16_t, true>(partial, nsplit, bias, ids, w, x, T, d, E, k, capacity, counts,
+                                                        offsets, perm, inv_perm, xp, stream)
+               : launch_topk_dispatch_t<uint16_t, false>(partial, nsplit, bias, ids, w, x, T, d, E, k, capacity,
+                                                         counts, offsets, perm, inv_perm, xp, stream);
+  }
+  const float* x = static_cast<const float*>(X);
+  float* xp = static_cast<float*>(Xp);
+  return cap ? launch_topk_dispatch_t<float, true>(partial, nsplit, bias, ids, w, x, T, d, E, k, capacity, counts,
+                                                   offsets, perm, inv_perm, xp, stream)
+             : launch_topk_dispatch_t<float, false>(partial, nsplit, bias, ids, w, x, T, d, E, k, capacity, counts,
+                                                    offsets, perm, inv_perm, xp, stream);
+}
+
 hipError_t launch_dispatch(int dtype, const int32_t* ids, const void* X, int T, int d, int E, int k, int capacity,
                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* Xp,
                            const DispatchScratch& sc, hipStream_t stream) {
   const bool cap = capacity >= 0;
   const int nchunks = (T + kDispatchChunk - 1) / kDispatchChunk;
   const int total_pairs = T * k;
-  if (T > 0 && T <= kSmallMaxT && k <= kSmallMaxK) {
+  if (dispatch_is_single_block(T, k)) {
     if (dtype == kDtypeBF16) {
       if (cap)
         hipLaunchKernelGGL((dispatch_small_kernel<uint16_t, true>), dim3(1), dim3(256), 0, stream, ids,

@@ -28,17 +28,36 @@ DispatchScratch carve_dispatch_scratch(void* ws, int T, int E, int k, bool capac
 // Router scratch: the transposed gate and, when T is small, the partial
 // logits of the K splits.
 size_t router_scratch_bytes(int T, int d, int E, int dtype);
+// select = false with a K-split router (small T) writes only the partial
+// logits: the caller selects (launch_topk_dispatch_small).
 hipError_t launch_router(int dtype, const void* X, const void* Wg, const float* bias, int T, int d, int E, int k,
-                         int32_t* ids, float* w, void* scratch, hipStream_t stream);
+                         int32_t* ids, float* w, void* scratch, hipStream_t stream, bool select = true);
+// Where the K-split partial logits live in the router scratch ([nsplit][T][E]
+// float); partial == nullptr when the router runs in one pass.
+struct RouterSplit {
+  const float* partial;
+  int nsplit;
+};
+RouterSplit router_split(int T, int d, int E, int dtype, void* scratch);
 
 hipError_t launch_dispatch(int dtype, const int32_t* ids, const void* X, int T, int d, int E, int k, int capacity,
                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* Xp,
                            const DispatchScratch& scratch, hipStream_t stream);
 
+// Small batches (the single-block dispatch: T <= 256, k <= 8) with a K-split
+// router: one block sums the partial logits, selects the top-k (writing ids
+// and weights) and runs the whole dispatch.  Same results as the router's
+// own selection followed by launch_dispatch.
+bool dispatch_is_single_block(int T, int k);
+hipError_t launch_topk_dispatch_small(int dtype, const float* partial, int nsplit, const float* bias, int32_t* ids,
+                                      float* w, const void* X, int T, int d, int E, int k, int capacity,
+                                      int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* Xp,
+                                      hipStream_t stream);
+
 // C[r, :] = act(A[r, :] . B[e]^T) for the rows r of each expert segment.
-// A: [rows, K]; B: [E, N, K]; C: [rows, N]; rows bounded by max_rows, and
-// no expert holds more than max_tokens_per_expert rows (at most T: a token
-// picks an expert once), which selects the skinny kernel for decode shapes.
+// A: [rows, K]; B: [E, N, K]; C: [rows, N]; rows bounded by max_rows.
+// max_tokens_per_expert is a hint that picks the kernel (the few-rows
+// kernels for decode shapes); any row count is computed correctly.
 hipError_t launch_grouped_gemm(int dtype, bool gelu, const void* A, const void* B, void* C,
                                const int32_t* offsets, int E, int N, int K, int max_rows,
                                int max_tokens_per_expert, hipStream_t stream);

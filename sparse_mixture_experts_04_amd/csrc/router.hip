@@ -23,6 +23,7 @@
 // runs in a fixed order, so results are deterministic.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "topk.hpp"
 
 namespace moe {
 namespace {
@@ -48,69 +49,6 @@ template <> struct RouterMma<float> {
     return c;
   }
 };
-
-__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
-  return va > vb || (va == vb && ia < ib);
-}
-
-// Top-k + renormalisation for one 16-token row tile held in MFMA C layout:
-// acc[t][i] is the logit of token row (lane>>4)*4+i and expert t*16+(lane&15).
-// sel_val / sel_id: LDS scratch [16][k] of the calling wave.
-template <int NT>
-__device__ __forceinline__ void topk_tile(f32x4_t (&acc)[NT], const float* __restrict__ bias, int E, int k,
-                                          int tok0, int T_tokens, float* sel_val, int* sel_id,
-                                          int32_t* __restrict__ topk_ids, float* __restrict__ topk_w) {
-  const int lane = threadIdx.x % kWave;
-  const int n = lane & 15;
-  const int grp = lane >> 4;
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int e = t * 16 + n;
-    const float b = (e < E && bias != nullptr) ? bias[e] : 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[t][i] = (e < E) ? acc[t][i] + b : -INFINITY;
-  }
-  for (int s = 0; s < k; ++s) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float bv = acc[0][i];
-      int bi = n;
-#pragma unroll
-      for (int t = 1; t < NT; ++t)
-        if (better(acc[t][i], t * 16 + n, bv, bi)) { bv = acc[t][i]; bi = t * 16 + n; }
-#pragma unroll
-      for (int m = 1; m < 16; m <<= 1) {
-        const float ov = __shfl_xor(bv, m, 16);
-        const int oi = __shfl_xor(bi, m, 16);
-        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-      }
-      if ((bi & 15) == n) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-          if (t == (bi >> 4)) acc[t][i] = -INFINITY;
-      }
-      if (n == 0) {
-        sel_val[(grp * 4 + i) * kMaxExperts + s] = bv;
-        sel_id[(grp * 4 + i) * kMaxExperts + s] = bi;
-      }
-    }
-  }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  for (int idx = lane; idx < 16 * k; idx += kWave) {
-    const int row = idx / k;
-    const int s = idx % k;
-    const int tok = tok0 + row;
-    if (tok >= T_tokens) continue;
-    const float* v = sel_val + row * kMaxExperts;
-    const float l0 = v[0];
-    float den = 0.f;
-    for (int j = 0; j < k; ++j) den += expf(v[j] - l0);
-    const int64_t o = static_cast<int64_t>(tok) * k + s;
-    topk_ids[o] = sel_id[row * kMaxExperts + s];
-    topk_w[o] = expf(v[s] - l0) / den;
-  }
-}
 
 // WgT[e][k] = W_g[k][e] for e < E, 0 for E <= e < 16*NT.  One block per 32
 // rows of k: the rows are read with 16-byte loads (a run of 32 rows of W_g is
@@ -283,38 +221,8 @@ __global__ __launch_bounds__(1024) void router_topk_kernel(const float* __restri
   __shared__ float logit[16][kMaxExperts];
   __shared__ float sel_val[16 * kMaxExperts];
   __shared__ int sel_id[16 * kMaxExperts];
-  const int tok0 = blockIdx.x * 16;
-  {
-    const int r = threadIdx.x / kMaxExperts;
-    const int e = threadIdx.x % kMaxExperts;
-    const int tok = tok0 + r;
-    float v = 0.f;
-    if (tok < T_tokens && e < E) {
-      const float* src = partial + static_cast<int64_t>(tok) * E + e;
-      const int64_t stride = static_cast<int64_t>(T_tokens) * E;
-      for (int s0 = 0; s0 < nsplit; s0 += 8) {
-        float a[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) a[j] = (s0 + j < nsplit) ? src[(s0 + j) * stride] : 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v += a[j];  // split order
-      }
-    }
-    logit[r][e] = v;
-  }
-  __syncthreads();
-  if (threadIdx.x >= kWave) return;
-  const int lane = threadIdx.x;
-  const int n = lane & 15;
-  const int grp = lane >> 4;
-  f32x4_t acc[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int e = t * 16 + n;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[t][i] = (e < E) ? logit[grp * 4 + i][e] : 0.f;
-  }
-  topk_tile<NT>(acc, bias, E, k, tok0, T_tokens, sel_val, sel_id, topk_ids, topk_w);
+  topk_from_partials<NT>(partial, nsplit, bias, T_tokens, E, k, blockIdx.x * 16, logit, sel_val, sel_id, topk_ids,
+                         topk_w);
 }
 
 // K per split: the whole d when there are enough token blocks, else d split
@@ -337,7 +245,7 @@ size_t gate_t_bytes(int d, int E, size_t esize) { return align256(static_cast<si
 
 template <typename T, int NT>
 hipError_t launch_nt(const T* X, const T* Wg, const float* bias, int T_tokens, int d, int E, int k, int32_t* ids,
-                     float* w, unsigned char* scratch, hipStream_t stream) {
+                     float* w, unsigned char* scratch, bool select, hipStream_t stream) {
   T* WgT = reinterpret_cast<T*>(scratch);
   float* partial = reinterpret_cast<float*>(scratch + gate_t_bytes(d, E, sizeof(T)));
   const int split_len = split_len_of(T_tokens, d);
@@ -352,7 +260,7 @@ hipError_t launch_nt(const T* X, const T* Wg, const float* bias, int T_tokens, i
     hipLaunchKernelGGL((router_kernel<T, NT, false>), grid, dim3(kRouterThreads), 0, stream, X, WgT, Wg, bias,
                        T_tokens, d, E, k, split_len, nullptr, ids, w);
   }
-  if (nsplit > 1)
+  if (nsplit > 1 && select)
     hipLaunchKernelGGL((router_topk_kernel<NT>), dim3((T_tokens + 15) / 16), dim3(1024), 0, stream, partial, nsplit,
                        bias, T_tokens, E, k, ids, w);
   return hipGetLastError();
@@ -360,12 +268,12 @@ hipError_t launch_nt(const T* X, const T* Wg, const float* bias, int T_tokens, i
 
 template <typename T>
 hipError_t launch_t(const T* X, const T* Wg, const float* bias, int T_tokens, int d, int E, int k, int32_t* ids,
-                    float* w, unsigned char* scratch, hipStream_t stream) {
+                    float* w, unsigned char* scratch, bool select, hipStream_t stream) {
   switch ((E + 15) / 16) {
-    case 1: return launch_nt<T, 1>(X, Wg, bias, T_tokens, d, E, k, ids, w, scratch, stream);
-    case 2: return launch_nt<T, 2>(X, Wg, bias, T_tokens, d, E, k, ids, w, scratch, stream);
-    case 3: return launch_nt<T, 3>(X, Wg, bias, T_tokens, d, E, k, ids, w, scratch, stream);
-    default: return launch_nt<T, 4>(X, Wg, bias, T_tokens, d, E, k, ids, w, scratch, stream);
+    case 1: return launch_nt<T, 1>(X, Wg, bias, T_tokens, d, E, k, ids, w, scratch, select, stream);
+    case 2: return launch_nt<T, 2>(X, Wg, bias, T_tokens, d, E, k, ids, w, scratch, select, stream);
+    case 3: return launch_nt<T, 3>(X, Wg, bias, T_tokens, d, E, k, ids, w, scratch, select, stream);
+    default: return launch_nt<T, 4>(X, Wg, bias, T_tokens, d, E, k, ids, w, scratch, select, stream);
   }
 }
 
@@ -381,15 +289,26 @@ size_t router_scratch_bytes(int T_tokens, int d, int E, int dtype) {
   return b;
 }
 
+RouterSplit router_split(int T_tokens, int d, int E, int dtype, void* scratch) {
+  RouterSplit r{nullptr, 1};
+  if (T_tokens <= 0) return r;
+  const int split_len = split_len_of(T_tokens, d);
+  r.nsplit = (d + split_len - 1) / split_len;
+  if (r.nsplit > 1)
+    r.partial = reinterpret_cast<const float*>(static_cast<unsigned char*>(scratch) +
+                                               gate_t_bytes(d, E, dtype == kDtypeBF16 ? 2 : 4));
+  return r;
+}
+
 hipError_t launch_router(int dtype, const void* X, const void* Wg, const float* bias, int T_tokens, int d, int E,
-                         int k, int32_t* ids, float* w, void* scratch, hipStream_t stream) {
+                         int k, int32_t* ids, float* w, void* scratch, hipStream_t stream, bool select) {
   if (T_tokens <= 0) return hipSuccess;
   unsigned char* sc = static_cast<unsigned char*>(scratch);
   if (dtype == kDtypeBF16)
     return launch_t(static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(Wg), bias, T_tokens, d, E, k, ids,
-                    w, sc, stream);
+                    w, sc, select, stream);
   return launch_t(static_cast<const float*>(X), static_cast<const float*>(Wg), bias, T_tokens, d, E, k, ids, w, sc,
-                  stream);
+                  select, stream);
 }
 
 }  // namespace moe

@@ -1,0 +1,123 @@
+// Top-k selection and renormalisation of router logits, shared by the
+// router kernels and the single-block small-batch dispatch.
+//
+// Method ("Qwen2-MoE代码解析" (jsqmd.com/news/1061813) §3.1; Qwen2-MoE
+// walk-through (mlqm.cn/news/48291) §3.2 step 2): the k largest softmax
+// probabilities are those of the k largest logits (softmax is monotone), and
+// after renormalisation p_s / sum_j p_j = exp(l_s - l_0) / sum_j exp(l_j - l_0)
+// over the selected logits (l_0 the largest), so the softmax denominator is
+// never formed.  Equal logits go to the lower expert id.
+#pragma once
+
+#include "common.hpp"
+
+namespace moe {
+
+__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+// Top-k + renormalisation for one 16-token row tile held in MFMA C layout:
+// acc[t][i] is the logit of token row (lane>>4)*4+i and expert t*16+(lane&15).
+// sel_val / sel_id: LDS scratch [16][k] of the calling wave.
+template <int NT>
+__device__ __forceinline__ void topk_tile(f32x4_t (&acc)[NT], const float* __restrict__ bias, int E, int k,
+                                          int tok0, int T_tokens, float* sel_val, int* sel_id,
+                                          int32_t* __restrict__ topk_ids, float* __restrict__ topk_w) {
+  const int lane = threadIdx.x % kWave;
+  const int n = lane & 15;
+  const int grp = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int e = t * 16 + n;
+    const float b = (e < E && bias != nullptr) ? bias[e] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[t][i] = (e < E) ? acc[t][i] + b : -INFINITY;
+  }
+  for (int s = 0; s < k; ++s) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float bv = acc[0][i];
+      int bi = n;
+#pragma unroll
+      for (int t = 1; t < NT; ++t)
+        if (better(acc[t][i], t * 16 + n, bv, bi)) { bv = acc[t][i]; bi = t * 16 + n; }
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) {
+        const float ov = __shfl_xor(bv, m, 16);
+        const int oi = __shfl_xor(bi, m, 16);
+        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+      }
+      if ((bi & 15) == n) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          if (t == (bi >> 4)) acc[t][i] = -INFINITY;
+      }
+      if (n == 0) {
+        sel_val[(grp * 4 + i) * kMaxExperts + s] = bv;
+        sel_id[(grp * 4 + i) * kMaxExperts + s] = bi;
+      }
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  for (int idx = lane; idx < 16 * k; idx += kWave) {
+    const int row = idx / k;
+    const int s = idx % k;
+    const int tok = tok0 + row;
+    if (tok >= T_tokens) continue;
+    const float* v = sel_val + row * kMaxExperts;
+    const float l0 = v[0];
+    float den = 0.f;
+    for (int j = 0; j < k; ++j) den += expf(v[j] - l0);
+    const int64_t o = static_cast<int64_t>(tok) * k + s;
+    topk_ids[o] = sel_id[row * kMaxExperts + s];
+    topk_w[o] = expf(v[s] - l0) / den;
+  }
+}
+
+// Sum the K-split partial logits of tokens tok0 .. tok0+15 in split order into
+// logit[16][kMaxExperts] (LDS), then select with wave 0.  Called by a whole
+// block of 1024 threads (one (token, expert) entry per thread, 8 loads in
+// flight); the caller synchronises the block before and after.
+template <int NT>
+__device__ __forceinline__ void topk_from_partials(const float* __restrict__ partial, int nsplit,
+                                                   const float* __restrict__ bias, int T_tokens, int E, int k,
+                                                   int tok0, float (*logit)[kMaxExperts], float* sel_val,
+                                                   int* sel_id, int32_t* __restrict__ topk_ids,
+                                                   float* __restrict__ topk_w) {
+  {
+    const int r = threadIdx.x / kMaxExperts;
+    const int e = threadIdx.x % kMaxExperts;
+    const int tok = tok0 + r;
+    float v = 0.f;
+    if (tok < T_tokens && e < E) {
+      const float* src = partial + static_cast<int64_t>(tok) * E + e;
+      const int64_t stride = static_cast<int64_t>(T_tokens) * E;
+      for (int s0 = 0; s0 < nsplit; s0 += 8) {
+        float a[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a[j] = (s0 + j < nsplit) ? src[(s0 + j) * stride] : 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v += a[j];  // split order
+      }
+    }
+    logit[r][e] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    const int n = lane & 15;
+    const int grp = lane >> 4;
+    f32x4_t acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int e = t * 16 + n;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[t][i] = (e < E) ? logit[grp * 4 + i][e] : 0.f;
+    }
+    topk_tile<NT>(acc, bias, E, k, tok0, T_tokens, sel_val, sel_id, topk_ids, topk_w);
+  }
+}
+
+}  // namespace moe

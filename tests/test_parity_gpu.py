@@ -31,6 +31,8 @@ CASES = [
     ("skinny_64rows", 64, 256, 2, 1, 192, "bf16", -1, 0.0),
     ("skinny_33rows", 33, 320, 4, 2, 448, "bf16", -1, 0.3),
     ("skinny_cap", 60, 128, 8, 3, 128, "bf16", 9, 0.5),
+    ("splitk_cap_k3", 48, 1024, 16, 3, 256, "bf16", 7, 0.5),
+    ("splitk_t200_e64", 200, 512, 64, 2, 256, "bf16", -1, 0.3),
 ]
 IDS = [c[0] for c in CASES]
 
