@@ -33,6 +33,10 @@ CASES = [
     ("skinny_cap", 60, 128, 8, 3, 128, "bf16", 9, 0.5),
     ("splitk_cap_k3", 48, 1024, 16, 3, 256, "bf16", 7, 0.5),
     ("splitk_t200_e64", 200, 512, 64, 2, 256, "bf16", -1, 0.3),
+    # 256x256-tile GEMM at its edges: K = 64 (one LDS stage per tile), N = 64
+    # (an n-tile of 64 valid weight rows), experts of a few hundred rows
+    ("big_d64_f64", 700, 64, 4, 2, 64, "bf16", -1, 0.0),
+    ("big_e1_k1", 300, 128, 1, 1, 192, "bf16", -1, 0.0),
 ]
 IDS = [c[0] for c in CASES]
 
