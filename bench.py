@@ -59,10 +59,11 @@ def gemm_traffic(workload, stage):
     return round((fetch * FETCH_SCALE + write * WRITE_SCALE) * 1024)
 
 
-def gemm_kernel_name(w, capacity, stage):
+def gemm_kernel_name(w, capacity, stage, gathers):
     """The expert-GEMM kernel the library runs for this shape (its selection
     rule: bf16 with at most min(T, C) rows per expert picks the few-rows
-    kernels)."""
+    kernels; the up-projection of the 256x256 kernel gathers X through perm
+    where moe_expert_up_gather_supported says so)."""
     gelu = "true" if stage == "expert_up" else "false"
     K = w.d if stage == "expert_up" else w.F
     N = w.F if stage == "expert_up" else w.d
@@ -73,7 +74,7 @@ def gemm_kernel_name(w, capacity, stage):
         return f"grouped_gemm_bf16_gemv<{gelu}, {1 if bound <= 4 else 2 if bound <= 8 else 4}>"
     if bound <= 64:
         return f"grouped_gemm_bf16_skinny<{gelu}, {1 if bound <= 16 else 2 if bound <= 32 else 4}>"
-    return f"grouped_gemm_bf16_256<{gelu}>"
+    return f"grouped_gemm_bf16_256<{gelu}, {'true' if gathers and stage == 'expert_up' else 'false'}>"
 
 
 def parse():
@@ -99,12 +100,16 @@ def to_dev(torch, a, dtype):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
 
 
-def stage_work(w, N, active, es):
-    """Algorithmic FLOPs and bytes per launch of each stage (N kept pairs, `active` experts with rows)."""
+def stage_work(w, N, active, es, gathers):
+    """Algorithmic FLOPs and bytes per launch of each stage (N kept pairs,
+    `active` experts with rows).  With the gathered up-projection the
+    dispatch moves indices only and the up-projection reads each pair's row
+    of X in place of the copied row."""
     T, d, F, E, k = w.T, w.d, w.F, w.E, w.k
+    rows = 0 if gathers else T * d * es + N * d * es
     return {
         "route": {"flops": 2.0 * T * d * E, "bytes": T * d * es + d * E * es + T * k * 8},
-        "dispatch": {"flops": 0.0, "bytes": T * d * es + N * d * es + T * k * 4 * 3},
+        "dispatch": {"flops": 0.0, "bytes": rows + T * k * 4 * 3},
         "expert_up": {"flops": 2.0 * N * d * F, "bytes": active * F * d * es + N * d * es + N * F * es},
         "expert_down": {"flops": 2.0 * N * F * d, "bytes": active * d * F * es + N * F * es + N * d * es},
         "combine": {"flops": 0.0, "bytes": N * d * es + T * k * 8 + T * d * es},
@@ -242,15 +247,20 @@ def main():
         torch.cuda.synchronize()
         keep = (lambda t: t.clone()) if nsets > 1 else (lambda t: t)
         sets.append({"X": xs[si], "ids": keep(b.topk_ids), "w": keep(b.topk_w), "off": keep(b.expert_offsets),
-                     "inv": keep(b.inv_perm), "Xp": keep(Xp_ws), "H": keep(H_ws), "Yp": keep(Yp_ws)})
+                     "inv": keep(b.inv_perm), "perm": keep(b.perm), "Xp": keep(Xp_ws), "H": keep(H_ws),
+                     "Yp": keep(Yp_ws)})
         off = b.expert_offsets.cpu().numpy()
         per_step_N.append(int(off[-1]))
         per_step_active.append(int((np.diff(off) > 0).sum()))
+    # The stages as moe_forward runs them: where the up-projection gathers X
+    # through perm, the dispatch writes indices only.
+    gathers = moe.moe_expert_up_gather_supported(cfg)
     stage_fn = {
         "route": lambda q: moe.moe_route(cfg, q["X"], Wg, bias, b.topk_ids, b.topk_w, rws, rbytes),
         "dispatch": lambda q: moe.moe_dispatch(cfg, q["ids"], q["X"], b.expert_counts, b.expert_offsets, b.perm,
-                                               b.inv_perm, Xp_ws, dws, dbytes),
-        "expert_up": lambda q: moe.moe_expert_up(cfg, q["Xp"], q["off"], W1, q["H"]),
+                                               b.inv_perm, None if gathers else Xp_ws, dws, dbytes),
+        "expert_up": (lambda q: moe.moe_expert_up_gather(cfg, q["X"], q["perm"], q["off"], W1, q["H"])) if gathers
+        else (lambda q: moe.moe_expert_up(cfg, q["Xp"], q["off"], W1, q["H"])),
         "expert_down": lambda q: moe.moe_expert_down(cfg, q["H"], q["off"], W2, q["Yp"]),
         "combine": lambda q: moe.moe_combine(cfg, q["Yp"], q["inv"], q["w"], b.out),
     }
@@ -262,7 +272,7 @@ def main():
 
     N = float(np.mean(per_step_N))
     active = float(np.mean(per_step_active))
-    work = stage_work(w, N, active, es)
+    work = stage_work(w, N, active, es, gathers)
     stages = {}
     for n in names:
         ms = stage_ms[n]
@@ -285,7 +295,7 @@ def main():
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = gemm_traffic(w.name, dom)
     roof["algorithmic_bytes"] = round(work[dom]["bytes"])
-    roof["kernel"] = gemm_kernel_name(w, inp.expert_capacity, dom)
+    roof["kernel"] = gemm_kernel_name(w, inp.expert_capacity, dom, gathers)
     roof["ms"] = round(ms, 5)
 
     cpu = None

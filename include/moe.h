@@ -114,6 +114,8 @@ moe_status moe_route(const moe_config* cfg, const void* X, const void* Wg,
  *     Rows are ordered by (expert, token, slot) -- stable by token.
  *   inv_perm [T*k] out: the row of pair t*k+s, or -1 if the pair was dropped.
  *   Xp [T*k, d] out: row r = X[perm[r] / k] for r < N; rows >= N untouched.
+ *     Xp may be NULL: then only counts, offsets, perm and inv_perm are
+ *     written (for moe_expert_up_gather, which reads X through perm).
  *   Capacity (C >= 0): each expert keeps its pairs in (slot, token) order up
  *   to C; the rest are dropped.  Ids outside [0, E) are treated as dropped
  *   and not counted.
@@ -128,6 +130,23 @@ moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_ids, const vo
  * untouched). expert_offsets [E+1] is read on the device. */
 moe_status moe_expert_up(const moe_config* cfg, const void* Xp, const int32_t* expert_offsets,
                          const void* W1, void* H, void* stream);
+
+/* The up-projection with the dispatch's row copy folded in: H[r] =
+ * gelu(W1[e] X[perm[r] / k]) for every row r of expert e's segment -- the
+ * same values, bit for bit, as moe_dispatch's Xp followed by moe_expert_up.
+ * X [T, d], perm [T*k] (from moe_dispatch), expert_offsets [E+1], W1 [E, F, d]
+ * in; H [T*k, F] out (rows >= N untouched).  Entries of perm in an expert's
+ * segment that name no token of X contribute zero rows.
+ * Errors: UNSUPPORTED unless moe_expert_up_gather_supported says 1. */
+moe_status moe_expert_up_gather(const moe_config* cfg, const void* X, const int32_t* perm,
+                                const int32_t* expert_offsets, const void* W1, void* H,
+                                void* stream);
+
+/* Host only: *supported = 1 if moe_expert_up_gather runs for cfg (bf16 with
+ * more than 64 pairs per expert possible, i.e. min(T, C) > 64, and T*d*2 <
+ * 2^31 bytes), else 0.  moe_forward then gathers too and leaves the Xp part of
+ * its workspace unwritten. */
+moe_status moe_expert_up_gather_supported(const moe_config* cfg, int32_t* supported);
 
 /* Expert down-projection: Yp[r] = W2[e] H[r] (the second Linear).
  * H [T*k, F], W2 [E, d, F] in; Yp [T*k, d] out (rows >= N untouched). */
@@ -150,7 +169,9 @@ moe_status moe_combine(const moe_config* cfg, const void* Yp, const int32_t* inv
 /* The whole layer [mlqm §3.2 steps 1-5]: route, dispatch, expert FFN,
  * combine.  The routing and dispatch results are written to the caller's
  * buffers (same meaning as above) so that every stage can be checked; Xp, H
- * and Yp live in ws (moe_workspace_size(cfg, MOE_OP_FORWARD)). */
+ * and Yp live in ws (moe_workspace_size(cfg, MOE_OP_FORWARD)).  Where
+ * moe_expert_up_gather_supported holds, the up-projection reads X through
+ * perm and Xp is not written. */
 moe_status moe_forward(const moe_config* cfg, const void* X, const void* Wg,
                        const float* gate_bias, const void* W1, const void* W2, void* out,
                        int32_t* topk_ids, float* topk_w, int32_t* expert_counts,

@@ -32,7 +32,8 @@ MOE_OP_ROUTE = 3
 
 # Every symbol include/moe.h declares.
 EXPORTED = ("moe_status_string", "moe_version", "moe_workspace_size", "moe_route", "moe_dispatch",
-            "moe_expert_up", "moe_expert_down", "moe_expert_ffn", "moe_combine", "moe_forward")
+            "moe_expert_up", "moe_expert_up_gather", "moe_expert_up_gather_supported", "moe_expert_down",
+            "moe_expert_ffn", "moe_combine", "moe_forward")
 
 
 class MoeConfig(ctypes.Structure):
@@ -55,7 +56,7 @@ class MoeError(RuntimeError):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sparse_mixture_experts_04_amd.build`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python sparse_mixture_experts_04_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.c_void_p
     CFG = ctypes.POINTER(MoeConfig)
@@ -66,6 +67,8 @@ def _load():
         "moe_route": (ctypes.c_int, [CFG, P, P, P, P, P, P, ctypes.c_size_t, P]),
         "moe_dispatch": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
         "moe_expert_up": (ctypes.c_int, [CFG, P, P, P, P, P]),
+        "moe_expert_up_gather": (ctypes.c_int, [CFG, P, P, P, P, P, P]),
+        "moe_expert_up_gather_supported": (ctypes.c_int, [CFG, ctypes.POINTER(ctypes.c_int32)]),
         "moe_expert_down": (ctypes.c_int, [CFG, P, P, P, P, P]),
         "moe_expert_ffn": (ctypes.c_int, [CFG, P, P, P, P, P, P, ctypes.c_size_t, P]),
         "moe_combine": (ctypes.c_int, [CFG, P, P, P, P, P]),
@@ -155,6 +158,18 @@ def moe_dispatch(cfg, topk_ids, X, expert_counts, expert_offsets, perm, inv_perm
 def moe_expert_up(cfg, Xp, expert_offsets, W1, H, stream=None) -> None:
     _check("moe_expert_up", LIB.moe_expert_up(ctypes.byref(cfg), _ptr(Xp), _ptr(expert_offsets), _ptr(W1), _ptr(H),
                                               _stream(stream)))
+
+
+def moe_expert_up_gather(cfg, X, perm, expert_offsets, W1, H, stream=None) -> None:
+    _check("moe_expert_up_gather", LIB.moe_expert_up_gather(ctypes.byref(cfg), _ptr(X), _ptr(perm),
+                                                            _ptr(expert_offsets), _ptr(W1), _ptr(H),
+                                                            _stream(stream)))
+
+
+def moe_expert_up_gather_supported(cfg) -> bool:
+    v = ctypes.c_int32(0)
+    _check("moe_expert_up_gather_supported", LIB.moe_expert_up_gather_supported(ctypes.byref(cfg), ctypes.byref(v)))
+    return bool(v.value)
 
 
 def moe_expert_down(cfg, H, expert_offsets, W2, Yp, stream=None) -> None:

@@ -1,6 +1,8 @@
 """Build libmoe.so (the gfx950 HIP kernels and the C ABI of include/moe.h) in-tree.
 
-    python -m sparse_mixture_experts_04_amd.build
+    python sparse_mixture_experts_04_amd/build.py
+
+(run as a file: importing the package loads libmoe.so, which may be stale).
 
 Compiles every source under csrc/ with hipcc for gfx950 (one object per
 source, in parallel) and links them into sparse_mixture_experts_04_amd/libmoe.so.

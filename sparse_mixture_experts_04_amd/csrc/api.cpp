@@ -74,6 +74,12 @@ int rows_per_expert_bound(const moe_config* c) {
   return b;
 }
 
+// Whether the up-projection reads X through perm (the 256x256 kernel runs
+// and X fits its 32-bit buffer offsets).
+bool gathers(const moe_config* c) {
+  return moe::grouped_gemm_gathers(c->dtype, c->hidden_size, rows_per_expert_bound(c), c->num_tokens);
+}
+
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
@@ -127,7 +133,7 @@ moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_ids, const vo
                         size_t ws_bytes, void* stream) {
   if (moe_status s = check_cfg(cfg); s != MOE_OK) return s;
   if (!expert_counts || !expert_offsets) return MOE_ERR_INVALID_ARG;
-  if (cfg->num_tokens > 0 && (!topk_ids || !X || !perm || !inv_perm || !Xp)) return MOE_ERR_INVALID_ARG;
+  if (cfg->num_tokens > 0 && (!topk_ids || !X || !perm || !inv_perm)) return MOE_ERR_INVALID_ARG;
   const size_t need = dispatch_bytes(cfg);
   if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
   if (need > 0 && ws == nullptr) return MOE_ERR_INVALID_ARG;
@@ -147,6 +153,26 @@ moe_status moe_expert_up(const moe_config* cfg, const void* Xp, const int32_t* e
                                              cfg->intermediate_size, cfg->hidden_size,
                                              static_cast<int>(pairs_of(cfg)), rows_per_expert_bound(cfg),
                                              as_stream(stream)));
+}
+
+moe_status moe_expert_up_gather_supported(const moe_config* cfg, int32_t* supported) {
+  if (supported == nullptr) return MOE_ERR_INVALID_ARG;
+  *supported = 0;
+  if (moe_status s = check_cfg(cfg); s != MOE_OK) return s;
+  *supported = gathers(cfg) ? 1 : 0;
+  return MOE_OK;
+}
+
+moe_status moe_expert_up_gather(const moe_config* cfg, const void* X, const int32_t* perm,
+                                const int32_t* expert_offsets, const void* W1, void* H, void* stream) {
+  if (moe_status s = check_cfg(cfg); s != MOE_OK) return s;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if (!gathers(cfg)) return MOE_ERR_UNSUPPORTED;
+  if (!X || !perm || !expert_offsets || !W1 || !H) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_grouped_gemm_gather(true, X, cfg->num_tokens, perm, cfg->num_experts_per_tok, W1,
+                                                    H, expert_offsets, cfg->num_experts, cfg->intermediate_size,
+                                                    cfg->hidden_size, static_cast<int>(pairs_of(cfg)),
+                                                    as_stream(stream)));
 }
 
 moe_status moe_expert_down(const moe_config* cfg, const void* H, const int32_t* expert_offsets, const void* W2,
@@ -205,6 +231,10 @@ moe_status moe_forward(const moe_config* cfg, const void* X, const void* Wg, con
   void* Yp = p;
   const moe::RouterSplit split =
       moe::router_split(cfg->num_tokens, cfg->hidden_size, cfg->num_experts, cfg->dtype, rws);
+  // Where the up-projection can read each pair's token row from X through
+  // perm, the dispatch writes indices only.
+  const bool gather = gathers(cfg);
+  void* const Xp_out = gather ? nullptr : Xp;
   if (split.partial != nullptr && moe::dispatch_is_single_block(cfg->num_tokens, cfg->num_experts_per_tok)) {
     // Small batch with a K-split router: the router writes its partial
     // logits only, and one block selects and dispatches (one launch fewer,
@@ -217,20 +247,23 @@ moe_status moe_forward(const moe_config* cfg, const void* X, const void* Wg, con
     if (hipError_t e = moe::launch_topk_dispatch_small(
             cfg->dtype, split.partial, split.nsplit, gate_bias, topk_ids, topk_w, X, cfg->num_tokens,
             cfg->hidden_size, cfg->num_experts, cfg->num_experts_per_tok, cfg->expert_capacity, expert_counts,
-            expert_offsets, perm, inv_perm, Xp, as_stream(stream));
+            expert_offsets, perm, inv_perm, Xp_out, as_stream(stream));
         e != hipSuccess)
       return MOE_ERR_HIP;
   } else {
     if (moe_status s = moe_route(cfg, X, Wg, gate_bias, topk_ids, topk_w, rws, route_bytes(cfg), stream);
         s != MOE_OK)
       return s;
-    if (moe_status s = moe_dispatch(cfg, topk_ids, X, expert_counts, expert_offsets, perm, inv_perm, Xp, dws,
+    if (moe_status s = moe_dispatch(cfg, topk_ids, X, expert_counts, expert_offsets, perm, inv_perm, Xp_out, dws,
                                     dispatch_bytes(cfg), stream);
         s != MOE_OK)
       return s;
   }
   if (cfg->num_tokens == 0) return MOE_OK;
-  if (moe_status s = moe_expert_up(cfg, Xp, expert_offsets, W1, H, stream); s != MOE_OK) return s;
+  if (moe_status s = gather ? moe_expert_up_gather(cfg, X, perm, expert_offsets, W1, H, stream)
+                            : moe_expert_up(cfg, Xp, expert_offsets, W1, H, stream);
+      s != MOE_OK)
+    return s;
   if (moe_status s = moe_expert_down(cfg, H, expert_offsets, W2, Yp, stream); s != MOE_OK) return s;
   return moe_combine(cfg, Yp, inv_perm, topk_w, out, stream);
 }

@@ -270,6 +270,7 @@ __global__ __launch_bounds__(kScatterThreads) void dispatch_scatter_kernel(
       }
     }
   }
+  if (Xp == nullptr) return;  // indices only: the expert GEMM gathers the rows itself
   __syncthreads();
   copy_rows<kScatterThreads>(X, Xp, d, k, tok0, min(kScatterTok, T_tok - tok0), &s_row[0][0], KMAX);
 }

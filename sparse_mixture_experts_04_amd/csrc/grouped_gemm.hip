@@ -286,12 +286,18 @@ struct TileCoord {
   int e, m0, n0, rows;  // rows: the tile's token rows [m0, m0 + rows)
 };
 
-template <bool kGelu>
+// kGather: the token rows are not stored in expert order.  Row r of the
+// expert-ordered operand is row gidx[r] / gdiv of A, which then has src_rows
+// rows: the dispatch permutation (entries token*k + slot) read with gdiv = k
+// gathers each token's hidden state straight from the layer input.
+template <bool kGelu, bool kGather>
 __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const uint16_t* __restrict__ A,
                                                                         const uint16_t* __restrict__ B,
                                                                         uint16_t* __restrict__ C,
                                                                         const int32_t* __restrict__ offsets, int E,
-                                                                        int N, int K, int max_rows) {
+                                                                        int N, int K, int max_rows,
+                                                                        const int32_t* __restrict__ gidx, int gdiv,
+                                                                        int src_rows) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
   const int tid = threadIdx.x;
@@ -380,11 +386,43 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
       s.rows = 0;
     }
   };
-  auto setup_x = [&](Stream& s) {
+  // Gathered token rows: the token stream's per-lane offsets change with the
+  // tile.  g[i] receives the gather index of row wave*64 + i*8 + lane/8 of a
+  // tile; the stage loop loads them at the start of the stage whose token
+  // unit is the stream's last of its tile, before that stage's weight unit,
+  // so the stage wait (which leaves only that weight unit in flight) covers
+  // them and the offsets are formed at the stream's tile switch without a
+  // wait of their own.
+  auto load_gidx = [&](int (&g)[8], int tile) {
+    if (tile < total) {
+      const TileCoord t = coord(tile);
+      const __amdgpu_buffer_rsrc_t grsrc = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<int32_t*>(gidx) + t.m0, 0, t.rows * 4, kRsrcWord3);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        g[i] = __builtin_amdgcn_raw_buffer_load_b32(grsrc, (wave * 64 + i * 8 + (lane >> 3)) * 4, 0, 0);
+    }
+  };
+  auto setup_x = [&](Stream& s, const int (&g)[8]) {
     if (s.tile < total) {
       const TileCoord t = coord(s.tile);
-      s.base = Ab + static_cast<int64_t>(t.m0) * row_stride;
-      s.rows = t.rows;
+      if constexpr (kGather) {
+        // Rows past the tile (or a source row out of range) get an offset
+        // beyond the resource: they load zeros.
+        s.base = Ab;
+        s.rows = src_rows;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int r = wave * 64 + i * 8 + (lane >> 3);
+          const unsigned src = static_cast<unsigned>(g[i]) / static_cast<unsigned>(gdiv);
+          vx[i] = r < t.rows && src < static_cast<unsigned>(src_rows)
+                      ? static_cast<int>(src) * row_stride + (((lane & 7) ^ key_x(r)) << 4)
+                      : static_cast<int>(0x80000000u);
+        }
+      } else {
+        s.base = Ab + static_cast<int64_t>(t.m0) * row_stride;
+        s.rows = t.rows;
+      }
     } else {
       s.rows = 0;
     }
@@ -409,24 +447,30 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
       setup_w(s);
     }
   };
-  auto advance_x = [&](Stream& s) {
+  // g: the gather indices of tile s.tile + G (used only when the stream
+  // moves there).
+  auto advance_x = [&](Stream& s, const int (&g)[8]) {
     s.slot = s.slot + 2 >= kSlots ? s.slot + 2 - kSlots : s.slot + 2;
     if (++s.ks == kstages) {
       s.ks = 0;
       s.tile += G;
-      setup_x(s);
+      setup_x(s, g);
     }
   };
 
   setup_w(ws);
-  setup_x(xs);
+  int gp[8];
+  if constexpr (kGather) load_gidx(gp, first);
+  setup_x(xs, gp);
   // Prologue: stages 0 and 1 (units 0..3).
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     issue(ws, vw);
     advance_w(ws);
     issue(xs, vx);
-    advance_x(xs);
+    if constexpr (kGather)
+      if (xs.ks == kstages - 1) load_gidx(gp, xs.tile + G);
+    advance_x(xs, gp);
   }
 
   const int frow = lane & 31;
@@ -522,6 +566,11 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
     read_frags(nj_c, 0, wf0, xf0);
 
     for (int ks = 0; ks < kstages; ++ks) {
+      int gn[8];
+      if constexpr (kGather) {
+        if (xs.ks == kstages - 1) load_gidx(gn, xs.tile + G);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       // k-step 0 of this stage is in wf0/xf0.  Its block also issues the
       // weight unit two stages ahead.
       block(nj_c, acc, wf0, xf0, 1, wf1, xf1, &ws, vw);
@@ -532,8 +581,8 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
       // in flight (right after an epilogue its stores are outstanding too:
       // drain).  lgkmcnt(0): this wave's reads of this stage are complete, so
       // after the barrier its two units are free.
-      if (after_epilogue) wait_vmcnt_lgkm0<0>();
-      else wait_vmcnt_lgkm0<8>();
+      wait_vmcnt_lgkm0<8>();
+      if (after_epilogue) wait_vmcnt<0>();
       after_epilogue = false;
       barrier();
       __builtin_amdgcn_sched_barrier(0);
@@ -543,7 +592,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
       // read k-step 0 of the next stage (past the last stage: a free slot
       // whose values go unused).
       block(nj_c, acc, wf1, xf1, 0, wf0, xf0, &xs, vx);
-      advance_x(xs);
+      advance_x(xs, gn);
     }
     after_epilogue = true;
 
@@ -593,25 +642,28 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
   wait_vmcnt<0>();
 }
 
-template <bool kGelu>
+template <bool kGelu, bool kGather>
 hipError_t launch_big(const uint16_t* A, const uint16_t* B, uint16_t* C, const int32_t* offsets, int E, int N, int K,
-                      int max_rows, hipStream_t stream) {
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_bf16_256<kGelu>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     static_cast<int>(kBigLds));
+                      int max_rows, const int32_t* gidx, int gdiv, int src_rows, hipStream_t stream) {
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_bf16_256<kGelu, kGather>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kBigLds));
   if (attr != hipSuccess) return attr;
-  // 32-bit buffer offsets: 256 rows of K (operands) or N (results) bf16 must
-  // stay below 2^31 bytes.
+  // 32-bit buffer offsets: 256 rows of K (operands) or N (results) bf16, and
+  // for a gather all src_rows rows of A, must stay below 2^31 bytes.
   if (static_cast<int64_t>(K) * 2 * kBig >= (int64_t{1} << 31) ||
       static_cast<int64_t>(N) * 2 * kBig >= (int64_t{1} << 31))
+    return hipErrorInvalidValue;
+  if (kGather && (gidx == nullptr || gdiv < 1 || src_rows < 0 ||
+                  static_cast<int64_t>(src_rows) * K * 2 >= (int64_t{1} << 31)))
     return hipErrorInvalidValue;
   const int n_tiles_n = (N + kBig - 1) / kBig;
   const int64_t upper = (static_cast<int64_t>((max_rows + kBig - 1) / kBig) + E) * n_tiles_n;
   int64_t grid = device_cu_count();
   if (upper < grid) grid = upper;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL((grouped_gemm_bf16_256<kGelu>), dim3(static_cast<unsigned>(grid)), dim3(kBigThreads), kBigLds,
-                     stream, A, B, C, offsets, E, N, K, max_rows);
+  hipLaunchKernelGGL((grouped_gemm_bf16_256<kGelu, kGather>), dim3(static_cast<unsigned>(grid)), dim3(kBigThreads),
+                     kBigLds, stream, A, B, C, offsets, E, N, K, max_rows, gidx, gdiv, src_rows);
   return hipGetLastError();
 }
 
@@ -985,11 +1037,27 @@ hipError_t launch_grouped_gemm(int dtype, bool gelu, const void* A, const void* 
     if (max_tokens_per_expert <= kSkinnyMaxTok)
       return gelu ? launch_skinny<true, 4>(a, b, c, offsets, E, N, K, max_rows, stream)
                   : launch_skinny<false, 4>(a, b, c, offsets, E, N, K, max_rows, stream);
-    return gelu ? launch_big<true>(a, b, c, offsets, E, N, K, max_rows, stream)
-                : launch_big<false>(a, b, c, offsets, E, N, K, max_rows, stream);
+    return gelu ? launch_big<true, false>(a, b, c, offsets, E, N, K, max_rows, nullptr, 1, 0, stream)
+                : launch_big<false, false>(a, b, c, offsets, E, N, K, max_rows, nullptr, 1, 0, stream);
   }
   return launch_cfg<float, 64, 64, 2, 2>(gelu, static_cast<const float*>(A), static_cast<const float*>(B),
                                          static_cast<float*>(C), offsets, E, N, K, max_rows, stream);
+}
+
+bool grouped_gemm_gathers(int dtype, int K, int max_tokens_per_expert, int src_rows) {
+  return dtype == kDtypeBF16 && max_tokens_per_expert > kSkinnyMaxTok &&
+         static_cast<int64_t>(src_rows) * K * 2 < (int64_t{1} << 31);
+}
+
+hipError_t launch_grouped_gemm_gather(bool gelu, const void* X, int src_rows, const int32_t* gidx, int gdiv,
+                                      const void* B, void* C, const int32_t* offsets, int E, int N, int K,
+                                      int max_rows, hipStream_t stream) {
+  if (max_rows <= 0) return hipSuccess;
+  const uint16_t* a = static_cast<const uint16_t*>(X);
+  const uint16_t* b = static_cast<const uint16_t*>(B);
+  uint16_t* c = static_cast<uint16_t*>(C);
+  return gelu ? launch_big<true, true>(a, b, c, offsets, E, N, K, max_rows, gidx, gdiv, src_rows, stream)
+              : launch_big<false, true>(a, b, c, offsets, E, N, K, max_rows, gidx, gdiv, src_rows, stream);
 }
 
 }  // namespace moe

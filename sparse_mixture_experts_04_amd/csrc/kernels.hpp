@@ -40,6 +40,8 @@ struct RouterSplit {
 };
 RouterSplit router_split(int T, int d, int E, int dtype, void* scratch);
 
+// Xp == nullptr computes counts, offsets, perm and inv_perm only (for an
+// expert GEMM that gathers the token rows itself).
 hipError_t launch_dispatch(int dtype, const int32_t* ids, const void* X, int T, int d, int E, int k, int capacity,
                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* Xp,
                            const DispatchScratch& scratch, hipStream_t stream);
@@ -61,6 +63,16 @@ hipError_t launch_topk_dispatch_small(int dtype, const float* partial, int nspli
 hipError_t launch_grouped_gemm(int dtype, bool gelu, const void* A, const void* B, void* C,
                                const int32_t* offsets, int E, int N, int K, int max_rows,
                                int max_tokens_per_expert, hipStream_t stream);
+
+// The same product with the rows of A gathered: row r of the expert-ordered
+// operand is X[gidx[r] / gdiv], X: [src_rows, K] (gidx = the dispatch
+// permutation and gdiv = k read each pair's token row).  Only where
+// grouped_gemm_gathers() holds, i.e. where launch_grouped_gemm runs its
+// 256x256 kernel and X fits 32-bit buffer offsets.
+bool grouped_gemm_gathers(int dtype, int K, int max_tokens_per_expert, int src_rows);
+hipError_t launch_grouped_gemm_gather(bool gelu, const void* X, int src_rows, const int32_t* gidx, int gdiv,
+                                      const void* B, void* C, const int32_t* offsets, int E, int N, int K,
+                                      int max_rows, hipStream_t stream);
 
 hipError_t launch_combine(int dtype, const void* Yp, const int32_t* inv_perm, const float* topk_w, void* out, int T,
                           int d, int k, hipStream_t stream);

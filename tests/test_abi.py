@@ -139,3 +139,34 @@ def test_workspace_sizes():
     assert moe.moe_workspace_size(capcfg, moe.MOE_OP_DISPATCH) > disp
     # T = 0 is valid and needs (almost) nothing
     assert moe.moe_workspace_size(moe.config(0, d, F, E, k), moe.MOE_OP_EXPERT_FFN) == 0
+
+
+def test_gathered_up_projection_support():
+    # bf16 with experts that may hold more than 64 pairs (min(T, C) > 64)
+    assert moe.moe_expert_up_gather_supported(moe.config(8192, 2048, 5632, 32, 2, -1, "bf16"))
+    assert moe.moe_expert_up_gather_supported(moe.config(65, 128, 128, 8, 2, -1, "bf16"))
+    assert moe.moe_expert_up_gather_supported(moe.config(32768, 2048, 1408, 32, 4, 4096, "bf16"))
+    assert not moe.moe_expert_up_gather_supported(moe.config(64, 128, 128, 8, 2, -1, "bf16"))
+    assert not moe.moe_expert_up_gather_supported(moe.config(8192, 2048, 5632, 32, 2, 64, "bf16"))
+    assert not moe.moe_expert_up_gather_supported(moe.config(8192, 2048, 5632, 32, 2, -1, "f32"))
+    assert not moe.moe_expert_up_gather_supported(moe.config(8, 3584, 2560, 64, 2, -1, "bf16"))
+    # X must fit 32-bit buffer offsets: T * d * 2 < 2^31
+    assert moe.moe_expert_up_gather_supported(moe.config((1 << 31) // 8192 - 1, 4096, 128, 8, 2, -1, "bf16"))
+    assert not moe.moe_expert_up_gather_supported(moe.config((1 << 31) // 8192, 4096, 128, 8, 2, -1, "bf16"))
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_expert_up_gather_supported(_cfg(k=9))
+    assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+
+
+def test_gathered_up_projection_rejects_before_launch():
+    cfg = moe.config(300, 128, 128, 8, 2, -1, "bf16")
+    for args in [(None, 1, 1, 1, 1), (1, None, 1, 1, 1), (1, 1, None, 1, 1), (1, 1, 1, None, 1), (1, 1, 1, 1, None)]:
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_expert_up_gather(cfg, *args, stream=0)
+        assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    for unsupported in (moe.config(64, 128, 128, 8, 2, -1, "bf16"), moe.config(300, 128, 128, 8, 2, -1, "f32")):
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_expert_up_gather(unsupported, 1, 1, 1, 1, 1, stream=0)
+        assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
+    # T = 0 is a no-op for any pointers
+    moe.moe_expert_up_gather(moe.config(0, 128, 128, 8, 2, -1, "bf16"), None, None, None, None, None, stream=0)

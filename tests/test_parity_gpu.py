@@ -147,6 +147,134 @@ def test_expert_up_down(case):
     assert (H[N:] == 0).all() and (Yp[N:] == 0).all()
 
 
+GATHER_CASES = [c for c in CASES if moe.moe_expert_up_gather_supported(moe.config(c[1], c[2], c[5], c[3], c[4], c[7],
+                                                                                   c[6]))]
+
+
+def test_gather_cases_exist():
+    # the gathered up-projection must be exercised at K = 64, 128 and >= 192
+    assert {c[2] for c in GATHER_CASES} >= {64, 128, 256, 512}
+
+
+@pytest.mark.parametrize("case", GATHER_CASES, ids=[c[0] for c in GATHER_CASES])
+def test_expert_up_gather(case):
+    """H from X read through perm: bitwise the up-projection of the copied
+    rows, and within tolerance of the oracle; rows past N untouched."""
+    inp, cfg = make(case)
+    w = inp.workload
+    Xf = oracle.as_f64(inp.X, w.dtype)
+    r = oracle.route(Xf, oracle.as_f64(inp.Wg, w.dtype), inp.bias, w.k)
+    disp = oracle.dispatch(r.ids, w.E, inp.expert_capacity)
+    N = int(disp.offsets[-1])
+    Tk = w.T * w.k
+    perm_np = np.full(Tk, -1, dtype=np.int32)
+    perm_np[:N] = disp.perm
+    X = to_dev(inp.X, w.dtype)
+    perm = torch.from_numpy(perm_np).cuda()
+    offsets = torch.from_numpy(disp.offsets.astype(np.int32)).cuda()
+    W1 = to_dev(inp.W1, w.dtype)
+    Xp = torch.zeros((Tk, w.d), dtype=X.dtype, device="cuda")
+    if N:
+        Xp[:N] = X[torch.from_numpy((disp.perm // w.k).astype(np.int64)).cuda()]
+    H_copy = torch.zeros((Tk, w.F), dtype=X.dtype, device="cuda")
+    moe.moe_expert_up(cfg, Xp, offsets, W1, H_copy)
+    H = torch.full((Tk, w.F), 3.0, dtype=X.dtype, device="cuda")
+    moe.moe_expert_up_gather(cfg, X, perm, offsets, W1, H)
+    torch.cuda.synchronize()
+    assert torch.equal(H[:N], H_copy[:N]), "gathered and copied rows give different H"
+    assert (H[N:] == 3.0).all(), "rows past N were written"
+    H_ref = np.zeros((N, w.F))
+    for e, a, b in _segments(disp, w.E):
+        if b > a:
+            H_ref[a:b] = oracle.gelu_tanh(Xf[disp.perm[a:b] // w.k] @ oracle.as_f64(inp.W1[e], w.dtype).T)
+    if N:
+        eh = row_rel_err(dev_to_f64(H[:N]), H_ref)
+        assert eh.max() <= rel_tol(w.dtype), f"H rel err {eh.max():.3g}"
+
+
+def test_expert_up_gather_bad_perm_entries():
+    """perm entries inside a segment that name no token (negative, or
+    token >= T) read zero rows: H = gelu(0) = 0 there; the rest is exact."""
+    T, d, F, E, k = 130, 128, 192, 2, 2
+    inp = workloads.random_case(23, T, d, E, k, F, "bf16", -1, 0.0, w_scale=0.05)
+    cfg = moe.config(T, d, F, E, k, -1, "bf16")
+    assert moe.moe_expert_up_gather_supported(cfg)
+    Tk = T * k
+    perm_np = np.random.default_rng(3).permutation(Tk).astype(np.int32)
+    bad = np.array([0, 5, 100, 200, 259])
+    perm_np[bad] = np.array([-1, T * k, T * k + 7, -(1 << 30), 2 ** 31 - 1], dtype=np.int64).astype(np.int32)
+    offsets_np = np.array([0, 150, Tk], dtype=np.int32)
+    X = to_dev(inp.X, "bf16")
+    W1 = to_dev(inp.W1, "bf16")
+    H = torch.full((Tk, F), 3.0, dtype=torch.bfloat16, device="cuda")
+    moe.moe_expert_up_gather(cfg, X, torch.from_numpy(perm_np).cuda(), torch.from_numpy(offsets_np).cuda(), W1, H)
+    torch.cuda.synchronize()
+    got = dev_to_f64(H)
+    assert (got[bad] == 0).all()
+    good = np.setdiff1d(np.arange(Tk), bad)
+    Xf = oracle.as_f64(inp.X, "bf16")
+    ref = np.zeros((Tk, F))
+    for e in range(E):
+        a, b = offsets_np[e], offsets_np[e + 1]
+        rows = np.arange(a, b)
+        rows = rows[np.isin(rows, good)]
+        ref[rows] = oracle.gelu_tanh(Xf[perm_np[rows] // k] @ oracle.as_f64(inp.W1[e], "bf16").T)
+    err = row_rel_err(got[good], ref[good])
+    assert err.max() <= rel_tol("bf16"), f"H rel err {err.max():.3g}"
+
+
+@pytest.mark.parametrize("case", GATHER_CASES, ids=[c[0] for c in GATHER_CASES])
+def test_dispatch_indices_only(case):
+    """moe_dispatch with Xp = NULL writes the same indices."""
+    inp, cfg = make(case)
+    w = inp.workload
+    r = oracle.route(oracle.as_f64(inp.X, w.dtype), oracle.as_f64(inp.Wg, w.dtype), inp.bias, w.k)
+    disp = oracle.dispatch(r.ids, w.E, inp.expert_capacity)
+    Tk = w.T * w.k
+    ids = torch.from_numpy(r.ids.astype(np.int32)).cuda()
+    counts = torch.full((w.E,), -7, dtype=torch.int32, device="cuda")
+    offsets = torch.full((w.E + 1,), -7, dtype=torch.int32, device="cuda")
+    perm = torch.full((Tk,), -7, dtype=torch.int32, device="cuda")
+    inv = torch.full((Tk,), -7, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(1, moe.moe_workspace_size(cfg, moe.MOE_OP_DISPATCH)), dtype=torch.uint8, device="cuda")
+    moe.moe_dispatch(cfg, ids, to_dev(inp.X, w.dtype), counts, offsets, perm, inv, None, ws)
+    torch.cuda.synchronize()
+    check_dispatch_exact(counts.cpu().numpy(), offsets.cpu().numpy(), perm.cpu().numpy(), inv.cpu().numpy(), disp, Tk)
+
+
+@pytest.mark.parametrize("case", GATHER_CASES, ids=[c[0] for c in GATHER_CASES])
+def test_forward_equals_staged_calls(case):
+    """moe_forward (which gathers here) gives bitwise the output of the
+    staged entry points with the copied rows."""
+    inp, cfg = make(case)
+    w = inp.workload
+    X, Wg = to_dev(inp.X, w.dtype), to_dev(inp.Wg, w.dtype)
+    W1, W2 = to_dev(inp.W1, w.dtype), to_dev(inp.W2, w.dtype)
+    bias = to_dev(inp.bias, "f32")
+    layer = moe.MoELayer(cfg, Wg, W1, W2, bias)
+    out = layer.forward(X).clone()
+    Tk = w.T * w.k
+    ids = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
+    tw = torch.empty((w.T, w.k), dtype=torch.float32, device="cuda")
+    rws = torch.empty(max(1, moe.moe_workspace_size(cfg, moe.MOE_OP_ROUTE)), dtype=torch.uint8, device="cuda")
+    moe.moe_route(cfg, X, Wg, bias, ids, tw, rws)
+    counts = torch.empty((w.E,), dtype=torch.int32, device="cuda")
+    offsets = torch.empty((w.E + 1,), dtype=torch.int32, device="cuda")
+    perm = torch.empty((Tk,), dtype=torch.int32, device="cuda")
+    inv = torch.empty((Tk,), dtype=torch.int32, device="cuda")
+    Xp = torch.empty((Tk, w.d), dtype=X.dtype, device="cuda")
+    dws = torch.empty(max(1, moe.moe_workspace_size(cfg, moe.MOE_OP_DISPATCH)), dtype=torch.uint8, device="cuda")
+    moe.moe_dispatch(cfg, ids, X, counts, offsets, perm, inv, Xp, dws)
+    Yp = torch.empty((Tk, w.d), dtype=X.dtype, device="cuda")
+    fws = torch.empty(max(1, moe.moe_workspace_size(cfg, moe.MOE_OP_EXPERT_FFN)), dtype=torch.uint8, device="cuda")
+    moe.moe_expert_ffn(cfg, Xp, offsets, W1, W2, Yp, fws)
+    staged = torch.empty_like(out)
+    moe.moe_combine(cfg, Yp, inv, tw, staged)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, layer.buf.topk_ids) and torch.equal(perm, layer.buf.perm)
+    assert torch.equal(out, staged), "moe_forward differs from the staged calls"
+
+
 @pytest.mark.parametrize("d,F,cap", [(256, 384, 4), (256, 384, 8), (256, 384, 16), (192, 320, 16)],
                          ids=["gemv_tok4", "gemv_tok8", "gemv_tok16", "skinny_tok16"])
 def test_expert_rows_beyond_the_bound(d, F, cap):
