@@ -309,16 +309,53 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
   // Expert table, held by every wave in registers: lane e has expert e's row
   // segment [seg0, seg1) (clamped to [0, max_rows]: offsets come from device
   // memory) and the running count of m-tiles before and through it.
-  // An expert of R rows gets ceil(R/256) m-tiles of equal height (rounded
-  // up to 64 rows, the last one shorter): a 530-row expert runs tiles of
-  // 192, 192 and 146 rows rather than 256, 256 and 18, and each tile runs
-  // only as many 32-row token fragments as it has rows.
-  int t_seg0 = 0, t_seg1 = 0, t_mt = 0, t_h = kBig;
+  // An expert of R rows gets ceil(R/H) m-tiles of equal height (rounded up
+  // to 64 rows, the last one shorter): with H = 256 a 530-row expert runs
+  // tiles of 192, 192 and 146 rows rather than 256, 256 and 18, and each
+  // tile runs only as many 32-row token fragments as it has rows.
+  int t_seg0 = 0, t_seg1 = 0;
   if (lane < E) {
     t_seg0 = min(max(offsets[lane], 0), max_rows);
     t_seg1 = min(max(offsets[lane + 1], t_seg0), max_rows);
-    t_mt = (t_seg1 - t_seg0 + kBig - 1) / kBig;
-    if (t_mt > 0) t_h = min(kBig, ((t_seg1 - t_seg0 + t_mt - 1) / t_mt + 63) & ~63);
+  }
+  const int t_rows = t_seg1 - t_seg0;
+  const int n_tiles_n = (N + kBig - 1) / kBig;
+  const int G = gridDim.x;
+  // The height cap H (128, 192 or 256 rows) is chosen per launch from an
+  // estimate of the run: the G blocks take the tiles in rounds, so the run
+  // is about ceil(tiles / G) rounds of one tile each, and a tile of h rows
+  // costs about kTileCost[h/64 - 1] (relative per-stage times of 64-, 128-,
+  // 192- and 256-row tiles measured on MI355X with a weight tile per tile).
+  // The estimate overstates what smaller tiles gain (they share each weight
+  // tile among more m-tiles, and the GPU is partly bandwidth-bound), so a
+  // smaller cap must be estimated at least 8% faster.  Experts of 460-570
+  // rows on 8 n-tiles (N = 2048) run 3 full rounds of 192-row tiles about
+  // 2.5% faster than 2.5 rounds of 256-row ones.  Every block computes the
+  // same choice.
+  int H = kBig;
+  {
+    constexpr int kTileCost[4] = {70, 76, 88, 100};
+    int best = 0;
+#pragma unroll
+    for (int c = 4; c >= 2; --c) {
+      int m = (t_rows + 64 * c - 1) / (64 * c);
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) m += __shfl_xor(m, o);
+      const int rounds = (m * n_tiles_n + G - 1) / G;
+      const int est = rounds * kTileCost[c - 1];
+      if (c == 4) {
+        best = est;
+      } else if (est * 100 < best * 92) {
+        best = est;
+        H = 64 * c;
+      }
+    }
+    H = __builtin_amdgcn_readfirstlane(H);
+  }
+  int t_mt = 0, t_h = H;
+  if (lane < E) {
+    t_mt = (t_rows + H - 1) / H;
+    if (t_mt > 0) t_h = min(H, ((t_rows + t_mt - 1) / t_mt + 63) & ~63);
   }
   int t_incl = t_mt;
 #pragma unroll
@@ -326,9 +363,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
     const int o = __shfl_up(t_incl, m);
     if (lane >= m) t_incl += o;
   }
-  const int n_tiles_n = (N + kBig - 1) / kBig;
   const int total = __builtin_amdgcn_readlane(t_incl, E - 1) * n_tiles_n;
-  const int G = gridDim.x;
   int first = blockIdx.x;
   if ((G & 7) == 0) first = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
   if (first >= total) return;
@@ -658,7 +693,8 @@ hipError_t launch_big(const uint16_t* A, const uint16_t* B, uint16_t* C, const i
                   static_cast<int64_t>(src_rows) * K * 2 >= (int64_t{1} << 31)))
     return hipErrorInvalidValue;
   const int n_tiles_n = (N + kBig - 1) / kBig;
-  const int64_t upper = (static_cast<int64_t>((max_rows + kBig - 1) / kBig) + E) * n_tiles_n;
+  // At most this many tiles (m-tiles of at least 128 rows but the last of each expert).
+  const int64_t upper = (static_cast<int64_t>((max_rows + 127) / 128) + E) * n_tiles_n;
   int64_t grid = device_cu_count();
   if (upper < grid) grid = upper;
   if (grid < 1) grid = 1;

@@ -275,6 +275,48 @@ def test_forward_equals_staged_calls(case):
     assert torch.equal(out, staged), "moe_forward differs from the staged calls"
 
 
+PREFILL_LIKE_ROWS = [463, 467, 468, 478, 485, 486, 488, 488, 490, 491, 491, 494, 498, 501, 507, 516,
+                     519, 519, 519, 519, 523, 523, 524, 525, 536, 536, 542, 551, 553, 554, 560, 570]
+
+
+@pytest.mark.parametrize("rows", [PREFILL_LIKE_ROWS, [400] * 8, [512] * 32, [700, 0, 2, 255, 256, 257, 64, 900]],
+                         ids=["rows_460_570", "rows_400", "rows_512", "rows_mixed"])
+def test_expert_gemm_tile_heights(rows):
+    """The 256x256 kernel caps its m-tile height per launch (256, 192 or 128
+    rows) from the routed counts and the number of blocks: 460-570-row
+    experts on 8 n-tiles take 192-row tiles, eight 400-row experts 128-row
+    tiles, 512-row experts 256-row tiles.  Every choice must compute every
+    row (through the gathered and the copied up-projection)."""
+    E = len(rows)
+    k = 2
+    Tk = sum(rows)
+    T = Tk // k
+    d, F = 128, 2048
+    inp = workloads.random_case(57, T, d, E, k, F, "bf16", -1, 0.0, w_scale=0.05)
+    cfg = moe.config(T, d, F, E, k, -1, "bf16")
+    assert moe.moe_expert_up_gather_supported(cfg)
+    offsets_np = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    perm_np = np.random.default_rng(9).permutation(Tk).astype(np.int32)
+    Xf = oracle.as_f64(inp.X, "bf16")
+    Xp64 = Xf[perm_np // k]
+    H_ref = np.zeros((Tk, F))
+    for e in range(E):
+        a, b = offsets_np[e], offsets_np[e + 1]
+        if b > a:
+            H_ref[a:b] = oracle.gelu_tanh(Xp64[a:b] @ oracle.as_f64(inp.W1[e], "bf16").T)
+    X = to_dev(inp.X, "bf16")
+    W1 = to_dev(inp.W1, "bf16")
+    offsets = torch.from_numpy(offsets_np).cuda()
+    H = torch.zeros((Tk, F), dtype=torch.bfloat16, device="cuda")
+    moe.moe_expert_up(cfg, torch.from_numpy(Xp64).to(torch.bfloat16).cuda(), offsets, W1, H)
+    Hg = torch.zeros((Tk, F), dtype=torch.bfloat16, device="cuda")
+    moe.moe_expert_up_gather(cfg, X, torch.from_numpy(perm_np).cuda(), offsets, W1, Hg)
+    torch.cuda.synchronize()
+    assert torch.equal(H, Hg)
+    eh = row_rel_err(dev_to_f64(H), H_ref)
+    assert eh.max() <= rel_tol("bf16"), f"H rel err {eh.max():.3g} (worst row {int(eh.argmax())})"
+
+
 @pytest.mark.parametrize("d,F,cap", [(256, 384, 4), (256, 384, 8), (256, 384, 16), (192, 320, 16)],
                          ids=["gemv_tok4", "gemv_tok8", "gemv_tok16", "skinny_tok16"])
 def test_expert_rows_beyond_the_bound(d, F, cap):
