@@ -21,6 +21,9 @@
 // across blocks: each writes partial logits to the workspace and a second
 // kernel sums the splits in a fixed order and selects.  The reduction over K
 // runs in a fixed order, so results are deterministic.
+#include <algorithm>
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "topk.hpp"
@@ -210,6 +213,249 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(
   topk_tile<NT>(sum, bias, E, k, rtok0, T_tokens, sel_val[r], sel_id[r], topk_ids, topk_w);
 }
 
+// bf16 router for many tokens when the whole transposed gate fits in LDS
+// (16*ceil(E/16) * d <= 64K elements): one persistent block per CU
+// transposes W_g into LDS itself (no transpose launch, and the gate is read
+// from L2 once per CU rather than once per 32 tokens), then streams its own
+// contiguous range of 16*RT tokens.
+//
+// * W_g^T in LDS: row e (16*NT rows, rows >= E zero) holds the d gate values
+//   of expert e; its 16-byte chunk c sits at chunk c ^ (e & 15), so the 16
+//   rows of one fragment read hit 16 distinct bank groups.
+// * K runs in 64-wide double steps.  Lane (m, g) loads 32 bytes of token row
+//   m, k = 64s + 16g .. 16g + 15 (four lanes cover a row's whole 128-byte
+//   line), and feeds its two halves to two 16x16x32 MFMAs; the B fragments
+//   of the same k come from LDS, so both operands use one K order.
+// * The 4 waves split the row tiles (RT >= 4) or, for RT < 4, the double
+//   steps; split partials are summed in LDS in wave order (deterministic).
+// * The owner wave of each 16-token row tile selects the top k.
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(std::integral_constant<int, N - 1>{});
+  }
+}
+
+constexpr int kLdsRouterScratch = 4 * 2 * 16 * kMaxExperts * 4;  // per-wave top-k scratch, 32 KB
+constexpr int kLdsRouterMaxGate = 64 * 1024;                      // gate elements that fit beside it
+
+template <int NT, int RT>
+__global__ __launch_bounds__(kRouterThreads, 1) void router_lds_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wg, const float* __restrict__ bias, int T_tokens,
+    int d, int E, int k, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w) {
+  constexpr int WT = RT >= 4 ? 4 : RT;  // token groups of waves
+  constexpr int WK = 4 / WT;            // K splits per token group
+  constexpr int RW = RT / WT;           // row tiles per wave
+  constexpr int kU = RW == 1 ? 8 : 4;   // double steps in flight per batch (16 loads per lane)
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  unsigned char* const gate = smem;
+  const int row_bytes = d * 2;
+  unsigned char* const scratch = smem + static_cast<size_t>(16 * NT) * row_bytes;
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int n = lane & 15;
+  const int grp = lane >> 4;
+
+  const int wt = wave / WK;
+  const int wk = wave % WK;
+  const int nds = d / 64;
+  float* const sel_val = reinterpret_cast<float*>(scratch + wave * (2 * 16 * kMaxExperts * 4));
+  int* const sel_id = reinterpret_cast<int*>(scratch + wave * (2 * 16 * kMaxExperts * 4) + 16 * kMaxExperts * 4);
+  f32x4_t* const red = reinterpret_cast<f32x4_t*>(scratch);  // [4 waves][RW][NT][64 lanes], aliases the top-k scratch
+
+  // Token rows of this wave in the current pass, and its double steps
+  // s = wk, wk + WK, ... in batches of kU, two batches in flight.
+  const unsigned char* xrow[RW];
+  auto set_rows = [&](int tok_base) {
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      const int tok = min(tok_base + (wt * RW + r) * 16 + n, T_tokens - 1);  // rows past T repeat the last token
+      xrow[r] = reinterpret_cast<const unsigned char*>(X + static_cast<int64_t>(tok) * d) + grp * 32;
+    }
+  };
+  const int nsteps = (nds - wk + WK - 1) / WK;
+  const int nbatch = (nsteps + kU - 1) / kU;
+  typedef u32x4_t Batch[kU][RW][2];
+  auto load_batch = [&](int b, Batch& a) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int st = wk + (b * kU + u) * WK;
+      if (st < nds) {
+#pragma unroll
+        for (int r = 0; r < RW; ++r) {
+          const int64_t off = static_cast<int64_t>(st) * 128;
+          a[u][r][0] = ld16(xrow[r] + off);
+          a[u][r][1] = ld16(xrow[r] + off + 16);
+        }
+      }
+    }
+  };
+  Batch bufA, bufB;
+  int tok_base = blockIdx.x * 16 * RT;  // < T_tokens: the grid has no block without tokens
+  set_rows(tok_base);
+
+  // ---- W_g^T into LDS: unit (kb, eg) = 8 consecutive k x 8 experts, read as
+  // 8 rows of 16 bytes (W_g is [d, E], experts contiguous) and written as 8
+  // rows-of-W_g^T chunks of 16 bytes.
+  {
+    constexpr int kBatch = 4;  // units per thread with their loads in flight together
+    const int egs = 2 * NT;    // 8-expert groups, padding included
+    const int units = (d / 8) * egs;
+    // Vector loads go through a buffer resource over W_g (d*E*2 < 2^31
+    // bytes, as d*16*NT <= 64K): padding experts and units past the end take
+    // an offset beyond the range and read zeros, so no load sits behind a
+    // branch.  E not a multiple of 8 (rows not 16-byte aligned): 2-byte loads.
+    const __amdgpu_buffer_rsrc_t wrsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Wg), 0, d * E * 2, 0x00020000);
+    // One batch of units; the first also issues the first two batches of
+    // token loads right after its gate loads, so all are in flight together.
+    auto do_batch = [&](int u0, auto vec_c, auto first_c) {
+      constexpr bool kVec = decltype(vec_c)::value;
+      {
+        uint32_t in[kBatch][8][4];
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+          const int u = u0 + b * kRouterThreads;
+          const int kb = u / egs;
+          const int eg = u % egs;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            if constexpr (kVec) {
+              const int off =
+                  u < units && eg * 8 < E ? ((kb * 8 + j) * E + eg * 8) * 2 : static_cast<int>(0x80000000u);
+              const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, off, 0, 0));
+#pragma unroll
+              for (int q = 0; q < 4; ++q) in[b][j][q] = v[q];
+            } else {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const int e0 = eg * 8 + 2 * q;
+                const int o = (kb * 8 + j) * E + e0;
+                const uint32_t lo = u < units && e0 < E ? Wg[o] : 0u;
+                const uint32_t hi = u < units && e0 + 1 < E ? Wg[o + 1] : 0u;
+                in[b][j][q] = lo | (hi << 16);
+              }
+            }
+          }
+        }
+        if constexpr (decltype(first_c)::value) {
+          load_batch(0, bufA);
+          if (nbatch > 1) load_batch(1, bufB);
+        }
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+          const int u = u0 + b * kRouterThreads;
+          if (u >= units) break;
+          const int kb = u / egs;
+          const int eg = u % egs;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            // expert eg*8+i: its 8 values of k = 8kb .. 8kb+7, two per word
+            u32x4_t o;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              const uint32_t lo = in[b][2 * p][i >> 1], hi = in[b][2 * p + 1][i >> 1];
+              o[p] = (i & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+            }
+            const int e = eg * 8 + i;
+            *reinterpret_cast<u32x4_t*>(gate + e * row_bytes + ((kb ^ (e & 15)) << 4)) = o;
+          }
+        }
+      }
+    };
+    auto transpose = [&](auto vec_c) {
+      do_batch(tid, vec_c, std::true_type{});
+      for (int u0 = tid + kBatch * kRouterThreads; u0 < units; u0 += kBatch * kRouterThreads)
+        do_batch(u0, vec_c, std::false_type{});
+    };
+    if (E % 8 == 0) transpose(std::true_type{});
+    else transpose(std::false_type{});
+  }
+  __syncthreads();
+
+  for (;;) {
+    f32x4_t acc[RW][NT];
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto mma_step = [&](int st, const u32x4_t (&a)[RW][2]) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = st * 8 + grp * 2 + h;  // 16-byte chunk of k = 64s + 16g + 8h
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int e = t * 16 + n;
+          const u32x4_t b = *reinterpret_cast<const u32x4_t*>(gate + e * row_bytes + ((c ^ n) << 4));
+#pragma unroll
+          for (int r = 0; r < RW; ++r) acc[r][t] = RouterMma<uint16_t>::run(a[r][h], b, acc[r][t]);
+        }
+      }
+    };
+    auto mma_batch = [&](int b, const Batch& a) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int st = wk + (b * kU + u) * WK;
+        if (st < nds) mma_step(st, a[u]);
+      }
+    };
+    // Batches b and b + 1 are in flight at the top of each iteration.
+    for (int b = 0; b < nbatch; b += 2) {
+      mma_batch(b, bufA);
+      if (b + 2 < nbatch) load_batch(b + 2, bufA);
+      if (b + 1 < nbatch) {
+        mma_batch(b + 1, bufB);
+        if (b + 3 < nbatch) load_batch(b + 3, bufB);
+      }
+    }
+    // The next pass's first token loads go out before this pass's selection,
+    // which they overlap.
+    const int cur_base = tok_base;
+    tok_base += gridDim.x * 16 * RT;
+    const bool more = tok_base < T_tokens;
+    if (more) {
+      set_rows(tok_base);
+      load_batch(0, bufA);
+      if (nbatch > 1) load_batch(1, bufB);
+    }
+
+    if constexpr (WK > 1) {
+      // Sum the K splits of each token group in wave order.
+#pragma unroll
+      for (int r = 0; r < RW; ++r)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) red[((wave * RW + r) * NT + t) * kWave + lane] = acc[r][t];
+      __syncthreads();
+      if (wk == 0) {
+#pragma unroll
+        for (int r = 0; r < RW; ++r)
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            f32x4_t v = red[((wave * RW + r) * NT + t) * kWave + lane];
+#pragma unroll
+            for (int w = 1; w < WK; ++w) v += red[(((wave + w) * RW + r) * NT + t) * kWave + lane];
+            acc[r][t] = v;
+          }
+      }
+      __syncthreads();  // the sums are read before the top-k scratch (same LDS) is written
+    }
+    if (wk == 0) {
+      // One call per row tile with a constant index: a loop over r would
+      // index acc dynamically, and the compiler would move acc to memory.
+      static_for<RW>([&](auto r_c) {
+        constexpr int r = decltype(r_c)::value;
+        topk_tile<NT>(acc[r], bias, E, k, cur_base + (wt * RW + r) * 16, T_tokens, sel_val, sel_id, topk_ids,
+                      topk_w);
+      });
+    }
+    if (!more) break;
+    __syncthreads();  // the scratch is reused by the next pass
+  }
+}
+
 // Sum the K-split partial logits in split order, then top-k.  A block of 1024
 // threads owns 16 tokens: one thread per (token, expert) entry sums the splits
 // with 8 loads in flight, the sums meet in LDS, and wave 0 selects.
@@ -243,9 +489,49 @@ size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
 size_t gate_t_bytes(int d, int E, size_t esize) { return align256(static_cast<size_t>((E + 15) / 16) * 16 * d * esize); }
 
+// Whether router_lds_kernel runs: bf16, no K split, W_g^T fits in LDS, and
+// d a multiple of 128 (the chunk swizzle permutes chunks within runs of 16).
+bool lds_router(int dtype, int T_tokens, int d, int E) {
+  return dtype == kDtypeBF16 && split_len_of(T_tokens, d) == d && d % 128 == 0 &&
+         (E + 15) / 16 * 16 * d <= kLdsRouterMaxGate;
+}
+
+template <int NT, int RT>
+hipError_t launch_lds_rt(const uint16_t* X, const uint16_t* Wg, const float* bias, int T_tokens, int d, int E, int k,
+                         int32_t* ids, float* w, int grid, hipStream_t stream) {
+  const size_t lds = static_cast<size_t>(16 * NT) * d * 2 + kLdsRouterScratch;
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&router_lds_kernel<NT, RT>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kLdsRouterMaxGate * 2 + kLdsRouterScratch);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((router_lds_kernel<NT, RT>), dim3(grid), dim3(kRouterThreads), lds, stream, X, Wg, bias,
+                     T_tokens, d, E, k, ids, w);
+  return hipGetLastError();
+}
+
+template <int NT>
+hipError_t launch_lds(const uint16_t* X, const uint16_t* Wg, const float* bias, int T_tokens, int d, int E, int k,
+                      int32_t* ids, float* w, hipStream_t stream) {
+  // One block per CU (fewer if there are fewer 16-token tiles), each with a
+  // contiguous range of 16*RT tokens per pass.
+  // The grid then shrinks to the blocks that have tokens in their first pass.
+  const int tiles = (T_tokens + 15) / 16;
+  const int cus = std::max(1, std::min(device_cu_count(), tiles));
+  const int per = (tiles + cus - 1) / cus;
+  const int rt = per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : 8;
+  const int grid = std::min(cus, (tiles + rt - 1) / rt);
+  if (rt == 1) return launch_lds_rt<NT, 1>(X, Wg, bias, T_tokens, d, E, k, ids, w, grid, stream);
+  if (rt == 2) return launch_lds_rt<NT, 2>(X, Wg, bias, T_tokens, d, E, k, ids, w, grid, stream);
+  if (rt == 4) return launch_lds_rt<NT, 4>(X, Wg, bias, T_tokens, d, E, k, ids, w, grid, stream);
+  return launch_lds_rt<NT, 8>(X, Wg, bias, T_tokens, d, E, k, ids, w, grid, stream);
+}
+
 template <typename T, int NT>
 hipError_t launch_nt(const T* X, const T* Wg, const float* bias, int T_tokens, int d, int E, int k, int32_t* ids,
                      float* w, unsigned char* scratch, bool select, hipStream_t stream) {
+  if constexpr (std::is_same<T, uint16_t>::value) {
+    if (lds_router(kDtypeBF16, T_tokens, d, E)) return launch_lds<NT>(X, Wg, bias, T_tokens, d, E, k, ids, w, stream);
+  }
   T* WgT = reinterpret_cast<T*>(scratch);
   float* partial = reinterpret_cast<float*>(scratch + gate_t_bytes(d, E, sizeof(T)));
   const int split_len = split_len_of(T_tokens, d);

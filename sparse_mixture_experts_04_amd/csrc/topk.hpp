@@ -17,6 +17,32 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
+// One step of a 16-lane arg-max: take the (value, id) of the lane that DPP
+// control kCtrl names in this lane's row of 16, keep the better.  DPP moves
+// are plain VALU operations (no LDS round trip, unlike a lane shuffle).
+template <int kCtrl>
+__device__ __forceinline__ void argmax_dpp_step(float& bv, int& bi) {
+  const float ov = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, bv), kCtrl, 0xF,
+                                                                         0xF, false));
+  const int oi = __builtin_amdgcn_update_dpp(0, bi, kCtrl, 0xF, 0xF, false);
+  if (better(ov, oi, bv, bi)) {
+    bv = ov;
+    bi = oi;
+  }
+}
+
+// Arg-max over each row of 16 lanes, left in every lane of the row: pairs
+// (quad_perm 1,0,3,2), quads (quad_perm 2,3,0,1), then the two quads of each
+// half-row (row_half_mirror: lane i with 7-i) and the two halves
+// (row_mirror: lane i with 15-i).  better() is a total order, so the result
+// does not depend on the pairing.
+__device__ __forceinline__ void argmax16(float& bv, int& bi) {
+  argmax_dpp_step<0xB1>(bv, bi);
+  argmax_dpp_step<0x4E>(bv, bi);
+  argmax_dpp_step<0x141>(bv, bi);
+  argmax_dpp_step<0x140>(bv, bi);
+}
+
 // Top-k + renormalisation for one 16-token row tile held in MFMA C layout:
 // acc[t][i] is the logit of token row (lane>>4)*4+i and expert t*16+(lane&15).
 // sel_val / sel_id: LDS scratch [16][k] of the calling wave.
@@ -42,12 +68,7 @@ __device__ __forceinline__ void topk_tile(f32x4_t (&acc)[NT], const float* __res
 #pragma unroll
       for (int t = 1; t < NT; ++t)
         if (better(acc[t][i], t * 16 + n, bv, bi)) { bv = acc[t][i]; bi = t * 16 + n; }
-#pragma unroll
-      for (int m = 1; m < 16; m <<= 1) {
-        const float ov = __shfl_xor(bv, m, 16);
-        const int oi = __shfl_xor(bi, m, 16);
-        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-      }
+      argmax16(bv, bi);
       if ((bi & 15) == n) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)

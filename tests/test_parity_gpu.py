@@ -69,6 +69,26 @@ def test_route(case):
     assert np.max(np.abs(tw.cpu().numpy().sum(1) - 1)) < 1e-5
 
 
+@pytest.mark.parametrize("T,d,E,k", [(12000, 256, 16, 2), (40000, 128, 8, 2), (9000, 128, 40, 3), (5000, 256, 5, 2),
+                                     (20000, 2048, 32, 2)],
+                         ids=["t12000_rows4", "t40000_two_passes", "e40_nt3", "e5_gathered_gate", "t20000_d2048"])
+def test_route_many_tokens(T, d, E, k):
+    """Router shapes where one block per CU covers 48-128 tokens per pass
+    (and a second pass past 32768 tokens), with gates whose expert count is
+    or is not a multiple of 8."""
+    inp = workloads.random_case(71 + T, T, d, E, k, 64, "bf16", -1, 0.7, w_scale=0.05)
+    cfg = moe.config(T, d, 64, E, k, -1, "bf16")
+    X, Wg = to_dev(inp.X, "bf16"), to_dev(inp.Wg, "bf16")
+    bias = to_dev(inp.bias, "f32")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    tw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    rws = torch.empty(max(1, moe.moe_workspace_size(cfg, moe.MOE_OP_ROUTE)), dtype=torch.uint8, device="cuda")
+    moe.moe_route(cfg, X, Wg, bias, ids, tw, rws)
+    torch.cuda.synchronize()
+    r = oracle.route(oracle.as_f64(inp.X, "bf16"), oracle.as_f64(inp.Wg, "bf16"), inp.bias, k)
+    check_routing(ids.cpu().numpy(), tw.cpu().numpy(), r)
+
+
 @pytest.mark.parametrize("case", CASES, ids=IDS)
 def test_dispatch(case):
     inp, cfg = make(case)
