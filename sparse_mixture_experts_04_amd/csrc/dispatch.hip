@@ -135,20 +135,35 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(int32_t* __
     const int L = (nrows + P - 1) / P;
     const int r0 = p * L;
     const int r1 = min(nrows, r0 + L);
+    // Rows go in batches of kScanBatch independent loads, so a thread's
+    // L rows cost ceil(L / kScanBatch) memory round trips per pass.
+    constexpr int kScanBatch = 16;
     int sum = 0;
     if (p < P)
-      for (int r = r0; r < r1; ++r) sum += M[static_cast<int64_t>(r) * ncols + col0 + ci];
+      for (int rb = r0; rb < r1; rb += kScanBatch) {
+        int v[kScanBatch];
+#pragma unroll
+        for (int j = 0; j < kScanBatch; ++j)
+          v[j] = rb + j < r1 ? M[static_cast<int64_t>(rb + j) * ncols + col0 + ci] : 0;
+#pragma unroll
+        for (int j = 0; j < kScanBatch; ++j) sum += v[j];
+      }
     s_part[tid] = sum;
     __syncthreads();
     if (p < P) {
       int base = 0;
       for (int q = 0; q < p; ++q) base += s_part[q * gcols + ci];
       if (p == P - 1) s_tot[col0 + ci] = base + sum;
-      for (int r = r0; r < r1; ++r) {
-        int32_t* m = &M[static_cast<int64_t>(r) * ncols + col0 + ci];
-        const int v = *m;
-        *m = base;
-        base += v;
+      for (int rb = r0; rb < r1; rb += kScanBatch) {
+        int v[kScanBatch];
+#pragma unroll
+        for (int j = 0; j < kScanBatch; ++j)
+          v[j] = rb + j < r1 ? M[static_cast<int64_t>(rb + j) * ncols + col0 + ci] : 0;
+#pragma unroll
+        for (int j = 0; j < kScanBatch; ++j) {
+          if (rb + j < r1) M[static_cast<int64_t>(rb + j) * ncols + col0 + ci] = base;
+          base += v[j];
+        }
       }
     }
     __syncthreads();
