@@ -34,16 +34,16 @@ METRIC = "MoE-layer tokens/sec at 1 GPU; % bf16 MFMA peak (FFN) / % HBM peak (re
 # WRITE_SIZE (KiB per dispatch), scaled by what the same counters read for a
 # plain 1 GiB device copy (FETCH_SIZE x2.0, WRITE_SIZE x1.0); valid only for
 # the GEMM source they were taken on (sha1 prefix), else reported as null.
-TRAFFIC_SOURCE_SHA1 = "7beb2593f2b0"
+TRAFFIC_SOURCE_SHA1 = "902f10cb0752"
 TRAFFIC_BYTES = {  # (workload, stage) -> (fetch KiB, write KiB) per dispatch, raw counter values
-    ("prefill", "expert_up"): (479415.8, 180233.8),
-    ("prefill", "expert_down"): (585044.9, 65536.2),
-    ("capacity", "expert_up"): (879138.4, 285272.4),
-    ("capacity", "expert_down"): (698102.3, 415763.4),
-    ("skewed", "expert_up"): (7289498.0, 918639.6),
-    ("skewed", "expert_down"): (6444369.1, 262182.7),
-    ("decode", "expert_up"): (123368.4, 80.0),
-    ("decode", "expert_down"): (123236.6, 112.0),
+    ("prefill", "expert_up"): (483002.4, 180230.0),
+    ("prefill", "expert_down"): (805338.1, 65536.2),
+    ("capacity", "expert_up"): (850517.9, 285279.8),
+    ("capacity", "expert_down"): (706134.0, 415804.4),
+    ("skewed", "expert_up"): (7236229.3, 919371.3),
+    ("skewed", "expert_down"): (6423766.4, 262173.2),
+    ("decode", "expert_up"): (122941.2, 80.0),
+    ("decode", "expert_down"): (122812.6, 112.0),
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 

@@ -310,9 +310,11 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
   // segment [seg0, seg1) (clamped to [0, max_rows]: offsets come from device
   // memory) and the running count of m-tiles before and through it.
   // An expert of R rows gets ceil(R/H) m-tiles of equal height (rounded up
-  // to 64 rows, the last one shorter): with H = 256 a 530-row expert runs
+  // to 32 rows, the last one shorter): with H = 256 a 530-row expert runs
   // tiles of 192, 192 and 146 rows rather than 256, 256 and 18, and each
-  // tile runs only as many 32-row token fragments as it has rows.
+  // tile runs only as many 32-row token fragments as it has rows.  Equal
+  // fragment counts keep the m-tiles that share a weight tile in lockstep
+  // (a 463-row expert under H = 192: 160, 160, 143 rather than 192, 192, 79).
   int t_seg0 = 0, t_seg1 = 0;
   if (lane < E) {
     t_seg0 = min(max(offsets[lane], 0), max_rows);
@@ -355,7 +357,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
   int t_mt = 0, t_h = H;
   if (lane < E) {
     t_mt = (t_rows + H - 1) / H;
-    if (t_mt > 0) t_h = min(H, ((t_rows + t_mt - 1) / t_mt + 63) & ~63);
+    if (t_mt > 0) t_h = min(H, ((t_rows + t_mt - 1) / t_mt + 31) & ~31);
   }
   int t_incl = t_mt;
 #pragma unroll
