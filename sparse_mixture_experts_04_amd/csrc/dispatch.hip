@@ -20,6 +20,8 @@
 // Kernels (dropless): count -> scan -> scatter.
 // Kernels (capacity): count per (slot, expert) -> scan (priority bases and
 // offsets) -> keep -> scan of kept counts -> scatter.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "topk.hpp"
@@ -92,6 +94,50 @@ __device__ __forceinline__ int load_id(const int32_t* ids, int t, int T, int k, 
   return (e >= 0 && e < E) ? e : kNone;
 }
 
+// The expert ids of token t's slots s0 .. s0+N-1 (kNone for s >= k, t >= T,
+// or an id outside [0, E)), all N loads issued together: through a buffer
+// resource over ids an invalid slot takes an offset past the range and reads
+// zero, so no load sits behind a branch (a branch per load makes the
+// compiler wait for each load before the next).  ids beyond 2^31 bytes use
+// plain loads.
+template <int N>
+__device__ __forceinline__ void load_ids(const int32_t* __restrict__ ids, int t, int T, int k, int E, int s0,
+                                         int (&e)[N]) {
+  if (static_cast<int64_t>(T) * k * 4 < (int64_t{1} << 31)) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(ids), 0, T * k * 4, 0x00020000);
+    int v[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const bool ok = s0 + j < k && t < T;
+      v[j] = static_cast<int>(
+          __builtin_amdgcn_raw_buffer_load_b32(r, ok ? (t * k + s0 + j) * 4 : static_cast<int>(0x80000000u), 0, 0));
+    }
+#pragma unroll
+    for (int j = 0; j < N; ++j) e[j] = (s0 + j < k && t < T && v[j] >= 0 && v[j] < E) ? v[j] : kNone;
+  } else {
+#pragma unroll
+    for (int j = 0; j < N; ++j) e[j] = s0 + j < k ? load_id(ids, t, T, k, s0 + j, E) : kNone;
+  }
+}
+
+// The keep flags of token t's slots 0 .. N-1 (0 for s >= k or t >= T), the
+// same way.
+template <int N>
+__device__ __forceinline__ void load_keep(const int8_t* __restrict__ keep, int t, int T, int k, int (&kp)[N]) {
+  if (static_cast<int64_t>(T) * k < (int64_t{1} << 31)) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(keep), 0, T * k, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const bool ok = j < k && t < T;
+      kp[j] = __builtin_amdgcn_raw_buffer_load_b8(r, ok ? t * k + j : static_cast<int>(0x80000000u), 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < N; ++j) kp[j] = (j < k && t < T) ? keep[static_cast<int64_t>(t) * k + j] : 0;
+  }
+}
+
 // Histogram of one chunk: cols = E (dropless, col = e) or k*E (capacity, col = s*E + e).
 __global__ __launch_bounds__(kWave) void dispatch_count_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
                                                                bool per_slot, int32_t* __restrict__ hist) {
@@ -100,9 +146,12 @@ __global__ __launch_bounds__(kWave) void dispatch_count_kernel(const int32_t* __
   for (int c = threadIdx.x; c < cols; c += kWave) s_hist[c] = 0;
   __syncthreads();
   const int t = blockIdx.x * kDispatchChunk + threadIdx.x;
-  for (int s = 0; s < k; ++s) {
-    const int e = load_id(ids, t, T, k, s, E);
-    if (e != kNone) atomicAdd(&s_hist[per_slot ? s * E + e : e], 1);
+  for (int s0 = 0; s0 < k; s0 += 8) {
+    int e[8];
+    load_ids(ids, t, T, k, E, s0, e);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (e[j] != kNone) atomicAdd(&s_hist[per_slot ? (s0 + j) * E + e[j] : e[j]], 1);
   }
   __syncthreads();
   int32_t* out = hist + static_cast<int64_t>(blockIdx.x) * cols;
@@ -136,36 +185,53 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(int32_t* __
     const int r0 = p * L;
     const int r1 = min(nrows, r0 + L);
     // Rows go in batches of kScanBatch independent loads, so a thread's
-    // L rows cost ceil(L / kScanBatch) memory round trips per pass.
+    // L rows cost ceil(L / kScanBatch) memory round trips per pass.  The
+    // loads go through a buffer resource over M: a row past the thread's
+    // range takes an offset beyond the resource and reads zero, so no load
+    // sits behind a branch (which would serialise them).  M beyond 2^31
+    // bytes (past 8 M tokens at k*E = 4096 columns) uses plain loads.
     constexpr int kScanBatch = 16;
-    int sum = 0;
-    if (p < P)
-      for (int rb = r0; rb < r1; rb += kScanBatch) {
-        int v[kScanBatch];
+    const __amdgpu_buffer_rsrc_t mrsrc =
+        __builtin_amdgcn_make_buffer_rsrc(M, 0, nrows * ncols * 4, 0x00020000);
+    auto scan_col = [&](auto buffered_c) {
+      constexpr bool kBuf = decltype(buffered_c)::value;
+      auto load_row = [&](int r) {
+        if constexpr (!kBuf) {
+          return r < r1 ? M[static_cast<int64_t>(r) * ncols + col0 + ci] : 0;
+        } else {
+          const int off = r < r1 ? (r * ncols + col0 + ci) * 4 : static_cast<int>(0x80000000u);
+          return static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(mrsrc, off, 0, 0));
+        }
+      };
+      int sum = 0;
+      if (p < P)
+        for (int rb = r0; rb < r1; rb += kScanBatch) {
+          int v[kScanBatch];
 #pragma unroll
-        for (int j = 0; j < kScanBatch; ++j)
-          v[j] = rb + j < r1 ? M[static_cast<int64_t>(rb + j) * ncols + col0 + ci] : 0;
+          for (int j = 0; j < kScanBatch; ++j) v[j] = load_row(rb + j);
 #pragma unroll
-        for (int j = 0; j < kScanBatch; ++j) sum += v[j];
-      }
-    s_part[tid] = sum;
-    __syncthreads();
-    if (p < P) {
-      int base = 0;
-      for (int q = 0; q < p; ++q) base += s_part[q * gcols + ci];
-      if (p == P - 1) s_tot[col0 + ci] = base + sum;
-      for (int rb = r0; rb < r1; rb += kScanBatch) {
-        int v[kScanBatch];
+          for (int j = 0; j < kScanBatch; ++j) sum += v[j];
+        }
+      s_part[tid] = sum;
+      __syncthreads();
+      if (p < P) {
+        int base = 0;
+        for (int q = 0; q < p; ++q) base += s_part[q * gcols + ci];
+        if (p == P - 1) s_tot[col0 + ci] = base + sum;
+        for (int rb = r0; rb < r1; rb += kScanBatch) {
+          int v[kScanBatch];
 #pragma unroll
-        for (int j = 0; j < kScanBatch; ++j)
-          v[j] = rb + j < r1 ? M[static_cast<int64_t>(rb + j) * ncols + col0 + ci] : 0;
+          for (int j = 0; j < kScanBatch; ++j) v[j] = load_row(rb + j);
 #pragma unroll
-        for (int j = 0; j < kScanBatch; ++j) {
-          if (rb + j < r1) M[static_cast<int64_t>(rb + j) * ncols + col0 + ci] = base;
-          base += v[j];
+          for (int j = 0; j < kScanBatch; ++j) {
+            if (rb + j < r1) M[static_cast<int64_t>(rb + j) * ncols + col0 + ci] = base;
+            base += v[j];
+          }
         }
       }
-    }
+    };
+    if (static_cast<int64_t>(nrows) * ncols * 4 < (int64_t{1} << 31)) scan_col(std::true_type{});
+    else scan_col(std::false_type{});
     __syncthreads();
   }
   if (tid == 0) {
@@ -217,16 +283,23 @@ __global__ __launch_bounds__(kWave) void dispatch_keep_kernel(const int32_t* __r
   const int t = blockIdx.x * kDispatchChunk + lane;
   const uint64_t below = (1ull << lane) - 1ull;
   const int32_t* cb = chunk_base + static_cast<int64_t>(blockIdx.x) * k * E;
-  for (int s = 0; s < k; ++s) {
-    const int e = load_id(ids, t, T, k, s, E);
-    const Ballots B = ballots_of(e);
-    bool kept = false;
-    if (e != kNone) {
-      const int prio = slot_base[s * E + e] + cb[s * E + e] + __popcll(match(B, e) & below);
-      kept = prio < capacity;
-      if (kept) atomicAdd(&s_kept[e], 1);
+  for (int s0 = 0; s0 < k; s0 += 8) {
+    int ev[8];
+    load_ids(ids, t, T, k, E, s0, ev);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int s = s0 + j;
+      if (s >= k) break;
+      const int e = ev[j];
+      const Ballots B = ballots_of(e);
+      bool kept = false;
+      if (e != kNone) {
+        const int prio = slot_base[s * E + e] + cb[s * E + e] + __popcll(match(B, e) & below);
+        kept = prio < capacity;
+        if (kept) atomicAdd(&s_kept[e], 1);
+      }
+      if (t < T) keep[static_cast<int64_t>(t) * k + s] = kept ? 1 : 0;
     }
-    if (t < T) keep[static_cast<int64_t>(t) * k + s] = kept ? 1 : 0;
   }
   __syncthreads();
   if (lane < E) chunk_kept[static_cast<int64_t>(blockIdx.x) * E + lane] = s_kept[lane];
@@ -248,15 +321,16 @@ __global__ __launch_bounds__(kScatterThreads) void dispatch_scatter_kernel(
     const uint64_t below = (1ull << lane) - 1ull;
     int e[KMAX];
     int cnt[KMAX];
+    load_ids(ids, t, T_tok, k, E, 0, e);
+    if constexpr (kCap) {
+      int kp[KMAX];
+      load_keep(keep, t, T_tok, k, kp);
 #pragma unroll
-    for (int s = 0; s < KMAX; ++s) {
-      cnt[s] = 0;
-      e[s] = kNone;
-      if (s < k) {
-        e[s] = load_id(ids, t, T_tok, k, s, E);
-        if (kCap && e[s] != kNone && !keep[static_cast<int64_t>(t) * k + s]) e[s] = kNone;
-      }
+      for (int s = 0; s < KMAX; ++s)
+        if (!kp[s]) e[s] = kNone;
     }
+#pragma unroll
+    for (int s = 0; s < KMAX; ++s) cnt[s] = 0;
 #pragma unroll
     for (int s2 = 0; s2 < KMAX; ++s2) {
       if (s2 < k) {
@@ -321,14 +395,10 @@ __device__ __forceinline__ void dispatch_small_block(const int32_t* __restrict__
   for (int i = threadIdx.x; i < 4 * kMaxExperts; i += kThreads) (&s_kept[0][0])[i] = 0;
   __syncthreads();
   int e[kSmallMaxK];
+  load_ids(ids, t, T_tok, k, E, 0, e);
 #pragma unroll
-  for (int s = 0; s < kSmallMaxK; ++s) {
-    e[s] = kNone;
-    if (s < k) {
-      e[s] = load_id(ids, t, T_tok, k, s, E);
-      if (e[s] != kNone) atomicAdd(&s_cnt[chunk][s * E + e[s]], 1);
-    }
-  }
+  for (int s = 0; s < kSmallMaxK; ++s)
+    if (e[s] != kNone) atomicAdd(&s_cnt[chunk][s * E + e[s]], 1);
   __syncthreads();
   // exclusive prefix over the 4 chunks per column; column totals
   for (int c = threadIdx.x; c < cols; c += kThreads) {
