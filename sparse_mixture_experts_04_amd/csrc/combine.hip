@@ -14,15 +14,17 @@ namespace {
 constexpr int kCombineThreads = 256;
 
 // One token per blockIdx.x; each thread owns one 16-byte chunk of the output
-// row (blockIdx.y covers rows longer than 256 chunks) and issues the k slot
-// loads together, so a step costs one memory round trip.
-template <typename T>
+// row (blockIdx.y covers rows longer than 256 chunks) and issues the loads of
+// KS slots together, so a round of KS slots costs one memory round trip.  No
+// load sits behind a branch: the slot indices are clamped to k-1 and a
+// dropped slot reads row 0 and is then masked out (a branch per load would
+// make each wait for the previous one).
+template <typename T, int KS>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const T* __restrict__ Yp,
                                                                   const int32_t* __restrict__ inv_perm,
                                                                   const float* __restrict__ topk_w,
                                                                   T* __restrict__ out, int T_tok, int d, int k) {
   constexpr int kPer = Elem<T>::kPer16B;
-  constexpr int kMaxSlots = 8;  // slots whose loads are issued together; more are handled in rounds
   const int t = blockIdx.x;
   const int v = blockIdx.y * kCombineThreads + threadIdx.x;
   const int nvec = d / kPer;
@@ -32,27 +34,27 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const T* __res
   float acc[kPer];
 #pragma unroll
   for (int q = 0; q < kPer; ++q) acc[q] = 0.f;
-  for (int s0 = 0; s0 < k; s0 += kMaxSlots) {
-    u32x4_t y[kMaxSlots];
-    float w[kMaxSlots];
+  for (int s0 = 0; s0 < k; s0 += KS) {
+    int row[KS];
+    float w[KS];
 #pragma unroll
-    for (int j = 0; j < kMaxSlots; ++j) {
-      const int s = s0 + j;
-      w[j] = 0.f;
-      y[j] = u32x4_t{0u, 0u, 0u, 0u};
-      if (s < k) {
-        const int row = inv_perm[p0 + s];
-        if (row >= 0 && row < Tk) {  // dropped (or an invalid row index) adds nothing
-          w[j] = topk_w[p0 + s];
-          y[j] = ld16_nt(Yp + static_cast<int64_t>(row) * d + v * kPer);
-        }
-      }
+    for (int j = 0; j < KS; ++j) {
+      const int sc = min(s0 + j, k - 1);
+      row[j] = inv_perm[p0 + sc];
+      w[j] = topk_w[p0 + sc];
+    }
+    bool ok[KS];
+    u32x4_t y[KS];
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      ok[j] = s0 + j < k && row[j] >= 0 && row[j] < Tk;  // dropped (or an invalid row index) adds nothing
+      y[j] = ld16_nt(Yp + static_cast<int64_t>(ok[j] ? row[j] : 0) * d + v * kPer);
     }
 #pragma unroll
-    for (int j = 0; j < kMaxSlots; ++j) {
+    for (int j = 0; j < KS; ++j) {
       const T* ye = reinterpret_cast<const T*>(&y[j]);
 #pragma unroll
-      for (int q = 0; q < kPer; ++q) acc[q] += w[j] * Elem<T>::to_f32(ye[q]);
+      for (int q = 0; q < kPer; ++q) acc[q] += ok[j] ? w[j] * Elem<T>::to_f32(ye[q]) : 0.f;
     }
   }
   u32x4_t o;
@@ -67,7 +69,15 @@ hipError_t launch_t(const T* Yp, const int32_t* inv_perm, const float* w, T* out
                     hipStream_t stream) {
   const int nvec = d / Elem<T>::kPer16B;
   const dim3 grid(T_tok, (nvec + kCombineThreads - 1) / kCombineThreads);
-  hipLaunchKernelGGL(combine_kernel<T>, grid, dim3(kCombineThreads), 0, stream, Yp, inv_perm, w, out, T_tok, d, k);
+  if (k <= 2)
+    hipLaunchKernelGGL((combine_kernel<T, 2>), grid, dim3(kCombineThreads), 0, stream, Yp, inv_perm, w, out, T_tok, d,
+                       k);
+  else if (k <= 4)
+    hipLaunchKernelGGL((combine_kernel<T, 4>), grid, dim3(kCombineThreads), 0, stream, Yp, inv_perm, w, out, T_tok, d,
+                       k);
+  else
+    hipLaunchKernelGGL((combine_kernel<T, 8>), grid, dim3(kCombineThreads), 0, stream, Yp, inv_perm, w, out, T_tok, d,
+                       k);
   return hipGetLastError();
 }
 

@@ -55,7 +55,9 @@ __device__ __forceinline__ uint64_t match(const Ballots& B, int e) {
 
 // Copy hidden-state rows tok0 .. tok0+ntok-1 of X to their dispatched rows
 // (row_of[t * row_stride + s], -1 = none).  Each thread issues 8 16-byte loads
-// before their stores, so the copy is not one memory round trip per chunk.
+// before their stores, so the copy is not one memory round trip per chunk;
+// a load past the end re-reads the last chunk (its value unused) instead of
+// sitting behind a branch, which would make each load wait for the previous.
 template <int kThreads, typename T>
 __device__ __forceinline__ void copy_rows(const T* __restrict__ X, T* __restrict__ Xp, int d, int k, int tok0,
                                           int ntok, const int* row_of, int row_stride) {
@@ -66,12 +68,10 @@ __device__ __forceinline__ void copy_rows(const T* __restrict__ X, T* __restrict
     u32x4_t val[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      const int idx = base + j * kThreads;
-      if (idx < total) {
-        const int tt = idx / nvec;
-        const int v = idx % nvec;
-        val[j] = ld16_nt(reinterpret_cast<const unsigned char*>(X + static_cast<int64_t>(tok0 + tt) * d) + v * 16);
-      }
+      const int idx = min(base + j * kThreads, total - 1);
+      const int tt = idx / nvec;
+      const int v = idx % nvec;
+      val[j] = ld16_nt(reinterpret_cast<const unsigned char*>(X + static_cast<int64_t>(tok0 + tt) * d) + v * 16);
     }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
