@@ -36,14 +36,14 @@ METRIC = "MoE-layer tokens/sec at 1 GPU; % bf16 MFMA peak (FFN) / % HBM peak (re
 # the GEMM source they were taken on (sha1 prefix), else reported as null.
 TRAFFIC_SOURCE_SHA1 = "902f10cb0752"
 TRAFFIC_BYTES = {  # (workload, stage) -> (fetch KiB, write KiB) per dispatch, raw counter values
-    ("prefill", "expert_up"): (483002.4, 180230.0),
-    ("prefill", "expert_down"): (805338.1, 65536.2),
-    ("capacity", "expert_up"): (850517.9, 285279.8),
-    ("capacity", "expert_down"): (706134.0, 415804.4),
-    ("skewed", "expert_up"): (7236229.3, 919371.3),
-    ("skewed", "expert_down"): (6423766.4, 262173.2),
+    ("prefill", "expert_up"): (477144.0, 180229.5),
+    ("prefill", "expert_down"): (795743.7, 65536.1),
+    ("capacity", "expert_up"): (842199.4, 285280.1),
+    ("capacity", "expert_down"): (717284.0, 415961.3),
+    ("skewed", "expert_up"): (7224735.2, 919327.8),
+    ("skewed", "expert_down"): (6395353.6, 262182.2),
     ("decode", "expert_up"): (122941.2, 80.0),
-    ("decode", "expert_down"): (122812.6, 112.0),
+    ("decode", "expert_down"): (122812.7, 112.0),
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 
