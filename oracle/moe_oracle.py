@@ -11,8 +11,11 @@ Sources (the web pages this layer is taken from):
   [P4] MoE / "GPT-4 activates 2%" article, www.wmrh.cn/news/106769
 
 What the layer computes, step by step (each function below cites its step):
-  router      logits = X W_g (+ b); p = softmax(logits); top-k of p;
-              renormalise the k weights to sum to 1        [P2 §3.1; P3 §3.2 steps 1-2]
+  router      logits = X W_g (+ b); p = softmax(logits / tau); top-k of p;
+              renormalise the k weights to sum to 1        [P2 §3.1; P3 §3.2 steps 1-2;
+                                                            temperature tau: P4 §5.2]
+  statistics  mean probability and selection frequency per expert, and
+              E * their dot product                         [P2 §3.3]
   capacity    C = ceil(T/E) * k; pairs beyond C per expert dropped [P3 §2.2]
   dispatch    group (token, slot) pairs by expert              [P2 §3.1 detail 3; P4 §2.2]
   experts     per expert Linear -> GELU -> Linear              [P3 §2.2; P4 §2.2]
@@ -41,6 +44,7 @@ import numpy as np
 
 __all__ = [
     "as_f64", "gelu_tanh", "router_logits", "softmax", "topk_route", "route",
+    "router_stats", "RouterStats",
     "expert_capacity_formula", "capacity_keep", "dispatch", "expert_ffn",
     "combine", "moe_forward", "dense_bruteforce", "Routing", "Dispatch",
 ]
@@ -66,10 +70,14 @@ def router_logits(X: np.ndarray, Wg: np.ndarray, bias: Optional[np.ndarray]) -> 
     return logits
 
 
-def softmax(logits: np.ndarray) -> np.ndarray:
-    """Softmax over the expert axis [P2 §3.1; P3 §3.2 step 2]; max-subtracted."""
-    m = logits.max(axis=-1, keepdims=True)
-    z = np.exp(logits - m)
+def softmax(logits: np.ndarray, temperature: float = 1.0) -> np.ndarray:
+    """Softmax over the expert axis [P2 §3.1; P3 §3.2 step 2]; max-subtracted.
+    With a router temperature the logits are divided by it first [P4 §5.2:
+    the router softmax's temperature, 1.0 by default; above 1 the
+    probabilities flatten, below 1 they sharpen]."""
+    z = np.asarray(logits, dtype=np.float64) / float(temperature)
+    m = z.max(axis=-1, keepdims=True)
+    z = np.exp(z - m)
     return z / z.sum(axis=-1, keepdims=True)
 
 
@@ -109,12 +117,39 @@ def topk_route(probs: np.ndarray, k: int):
     return ids, w, margin
 
 
-def route(X: np.ndarray, Wg: np.ndarray, bias: Optional[np.ndarray], k: int) -> Routing:
-    """The router, all steps: gate Linear, softmax, top-k, renormalise."""
+def route(X: np.ndarray, Wg: np.ndarray, bias: Optional[np.ndarray], k: int,
+          temperature: float = 1.0) -> Routing:
+    """The router, all steps: gate Linear, softmax (at the given temperature),
+    top-k, renormalise."""
     logits = router_logits(X, Wg, bias)
-    probs = softmax(logits)
+    probs = softmax(logits, temperature)
     ids, w, margin = topk_route(probs, k)
     return Routing(logits, probs, ids, w, margin)
+
+
+@dataclass
+class RouterStats:
+    prob_mean: np.ndarray  # [E] mean router probability of each expert over the tokens
+    sel_freq: np.ndarray   # [E] fraction of the tokens whose top-k holds the expert
+    aux: float             # E * sum_e prob_mean[e] * sel_freq[e]
+
+
+def router_stats(probs: np.ndarray, ids: np.ndarray, E: int) -> RouterStats:
+    """The load-balancing statistics of one batch [P2 §3.3, its
+    load_balancing_loss listing]: the mean over tokens of the router
+    probabilities (the soft "tendency" of the gate), the mean over tokens of
+    the 0/1 top-k selection mask (the hard "outcome"), and their dot product
+    times the number of experts (balanced routing gives products near 1/E per
+    expert, so the value is then near k).  probs: [T, E]; ids: [T, k]."""
+    probs = np.asarray(probs, dtype=np.float64)
+    T = probs.shape[0]
+    mask = np.zeros((T, E), dtype=np.float64)
+    for t in range(T):
+        for e in ids[t]:
+            mask[t, int(e)] = 1.0
+    prob_mean = probs.mean(axis=0) if T else np.zeros(E)
+    sel_freq = mask.mean(axis=0) if T else np.zeros(E)
+    return RouterStats(prob_mean, sel_freq, float(E * np.sum(prob_mean * sel_freq)))
 
 
 # --------------------------------------------------------------------------- dispatch

@@ -160,6 +160,67 @@ def test_router_relabelling_equivariance():
     assert (pi[rp.ids] == r.ids).all()
 
 
+def test_temperature_closed_forms():
+    """Router temperature: softmax(l / tau).  Two experts: the logistic
+    function of (l0 - l1) / tau; the selection does not depend on tau (> 0);
+    the renormalised top-2 weight is the logistic function of the top-2 gap
+    over tau; huge tau flattens to 1/E, tiny tau gives a one-hot."""
+    l = np.array([[1.5, -0.5], [0.2, 0.7]])
+    for tau in (0.5, 1.0, 2.0, 3.0):
+        p = oracle.softmax(l, tau)
+        for t in range(2):
+            want0 = 1.0 / (1.0 + math.exp((l[t, 1] - l[t, 0]) / tau))
+            assert abs(p[t, 0] - want0) < 1e-15 and abs(p[t, 1] - (1 - want0)) < 1e-15
+    case = _case(12, T=40, E=8, k=2, bias_scale=0.5)
+    X, Wg = oracle.as_f64(case.X, "f32"), oracle.as_f64(case.Wg, "f32")
+    r1 = oracle.route(X, Wg, case.bias, 2)
+    for tau in (0.25, 0.5, 2.0, 7.0):
+        rt = oracle.route(X, Wg, case.bias, 2, temperature=tau)
+        assert (rt.ids == r1.ids).all()
+        top = np.take_along_axis(rt.logits, rt.ids, 1)
+        want = 1.0 / (1.0 + np.exp((top[:, 1] - top[:, 0]) / tau))
+        assert np.max(np.abs(rt.weights[:, 0] - want)) < 1e-14
+    flat = oracle.softmax(r1.logits, 1e12)
+    assert np.max(np.abs(flat - 1.0 / 8)) < 1e-10
+    sharp = oracle.softmax(r1.logits, 1e-4)
+    assert (np.argmax(sharp, 1) == r1.ids[:, 0]).all() and np.max(np.abs(sharp.max(1) - 1.0)) < 1e-12
+
+
+def test_router_stats_properties():
+    """Load-balancing statistics: the mean probabilities sum to 1, the
+    selection frequencies to k; uniform logits give 1/E each and a value of
+    exactly k; a balanced selection gives k whatever the probabilities; a
+    collapse onto one expert at k = 1 with sharp probabilities gives E (the
+    worst value)."""
+    case = _case(13, T=64, E=8, k=3, bias_scale=1.0)
+    X, Wg = oracle.as_f64(case.X, "f32"), oracle.as_f64(case.Wg, "f32")
+    r = oracle.route(X, Wg, case.bias, 3)
+    st = oracle.router_stats(r.probs, r.ids, 8)
+    assert abs(st.prob_mean.sum() - 1.0) < 1e-12 and abs(st.sel_freq.sum() - 3.0) < 1e-12
+    assert (st.sel_freq >= 0).all() and (st.sel_freq <= 1).all()
+    # uniform logits
+    ru = oracle.route(X, np.zeros_like(Wg), None, 3)
+    su = oracle.router_stats(ru.probs, ru.ids, 8)
+    assert np.max(np.abs(su.prob_mean - 1.0 / 8)) < 1e-15 and abs(su.aux - 3.0) < 1e-12
+    # a balanced selection: 8 tokens, k = 2, each expert picked twice
+    ids = np.array([[e, (e + 1) % 4] for e in range(4)] * 2)
+    probs = np.random.default_rng(0).dirichlet(np.ones(4), size=8)
+    assert abs(oracle.router_stats(probs, ids, 4).aux - 2.0) < 1e-12
+    # collapse
+    logits = np.tile(np.array([5.0, 0.0, -1.0, 0.5, 0.2]), (10, 1))
+    rc_probs = oracle.softmax(logits, 1e-3)
+    sc = oracle.router_stats(rc_probs, np.zeros((10, 1), dtype=np.int64), 5)
+    assert abs(sc.aux - 5.0) < 1e-12
+    # the value from the frequencies and probabilities of a hand case:
+    # T = 2, E = 2, k = 1; token 0 picks expert 0 with p0 = s(1), token 1
+    # picks expert 1 with p1 = s(2) (s the logistic function)
+    s1, s2 = 1 / (1 + math.exp(-1.0)), 1 / (1 + math.exp(-2.0))
+    hp = np.array([[s1, 1 - s1], [1 - s2, s2]])
+    hs = oracle.router_stats(hp, np.array([[0], [1]]), 2)
+    assert np.allclose(hs.prob_mean, [(s1 + 1 - s2) / 2, (1 - s1 + s2) / 2], atol=1e-15)
+    assert np.allclose(hs.sel_freq, [0.5, 0.5]) and abs(hs.aux - 1.0) < 1e-15
+
+
 def test_topk_ties_go_to_lower_id_and_margin():
     p = np.array([[0.25, 0.25, 0.25, 0.25],
                   [0.1, 0.4, 0.1, 0.4],
