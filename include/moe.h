@@ -77,7 +77,8 @@ typedef enum moe_op {
   MOE_OP_DISPATCH = 0,   /* moe_dispatch                                  */
   MOE_OP_EXPERT_FFN = 1, /* moe_expert_ffn (holds H)                      */
   MOE_OP_FORWARD = 2,    /* moe_forward (all scratch + Xp + H + Yp)       */
-  MOE_OP_ROUTE = 3       /* moe_route (partial logits when K is split)    */
+  MOE_OP_ROUTE = 3,      /* moe_route (partial logits when K is split)    */
+  MOE_OP_ROUTE_STATS = 4 /* moe_route_stats (as moe_route + per-tile sums) */
 } moe_op;
 
 /* Human-readable name of a status.  Static string; never NULL. */
@@ -103,6 +104,23 @@ moe_status moe_workspace_size(const moe_config* cfg, int32_t op, size_t* bytes);
 moe_status moe_route(const moe_config* cfg, const void* X, const void* Wg,
                      const float* gate_bias, int32_t* topk_ids, float* topk_w,
                      void* ws, size_t ws_bytes, void* stream);
+
+/* Router with a temperature, and the load-balancing statistics of the batch
+ * [jsqmd §3.3, its load_balancing_loss listing; the temperature of the
+ * router softmax: wmrh §5.2].  Same outputs as moe_route, the weights now
+ * exp((l_s - l_0)/tau) / sum_j exp((l_j - l_0)/tau) over the selected logits
+ * (tau = 1 gives moe_route's bits; the selection does not depend on tau), and
+ *   prob_mean [E] float out: mean over the T tokens of softmax(logits / tau)
+ *   sel_freq  [E] float out: fraction of the tokens whose top-k holds expert e
+ *   aux       [1] float out: E * sum_e prob_mean[e] * sel_freq[e]
+ *                            (k for balanced routing, E for a collapse at k = 1)
+ * All three are device pointers; the sums run in a fixed order (deterministic).
+ * temperature: finite and > 0, else INVALID_ARG.  T = 0 writes nothing.
+ * ws / ws_bytes: moe_workspace_size(cfg, MOE_OP_ROUTE_STATS). */
+moe_status moe_route_stats(const moe_config* cfg, const void* X, const void* Wg,
+                           const float* gate_bias, float temperature, int32_t* topk_ids,
+                           float* topk_w, float* prob_mean, float* sel_freq, float* aux,
+                           void* ws, size_t ws_bytes, void* stream);
 
 /* Dispatcher: group the (token, slot) pairs by expert
  * [jsqmd §3.1 detail 3; wmrh §2.2; capacity: jsqmd §3.4, mlqm §2.2].

@@ -29,9 +29,10 @@ MOE_OP_DISPATCH = 0
 MOE_OP_EXPERT_FFN = 1
 MOE_OP_FORWARD = 2
 MOE_OP_ROUTE = 3
+MOE_OP_ROUTE_STATS = 4
 
 # Every symbol include/moe.h declares.
-EXPORTED = ("moe_status_string", "moe_version", "moe_workspace_size", "moe_route", "moe_dispatch",
+EXPORTED = ("moe_status_string", "moe_version", "moe_workspace_size", "moe_route", "moe_route_stats", "moe_dispatch",
             "moe_expert_up", "moe_expert_up_gather", "moe_expert_up_gather_supported", "moe_expert_down",
             "moe_expert_ffn", "moe_combine", "moe_forward")
 
@@ -65,6 +66,7 @@ def _load():
         "moe_version": (ctypes.c_char_p, []),
         "moe_workspace_size": (ctypes.c_int, [CFG, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]),
         "moe_route": (ctypes.c_int, [CFG, P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "moe_route_stats": (ctypes.c_int, [CFG, P, P, P, ctypes.c_float, P, P, P, P, P, P, ctypes.c_size_t, P]),
         "moe_dispatch": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
         "moe_expert_up": (ctypes.c_int, [CFG, P, P, P, P, P]),
         "moe_expert_up_gather": (ctypes.c_int, [CFG, P, P, P, P, P, P]),
@@ -144,6 +146,16 @@ def moe_route(cfg, X, Wg, gate_bias, topk_ids, topk_w, ws=None, ws_bytes=None, s
         ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check("moe_route", LIB.moe_route(ctypes.byref(cfg), _ptr(X), _ptr(Wg), _ptr(gate_bias), _ptr(topk_ids),
                                       _ptr(topk_w), _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def moe_route_stats(cfg, X, Wg, gate_bias, temperature, topk_ids, topk_w, prob_mean, sel_freq, aux, ws=None,
+                    ws_bytes=None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check("moe_route_stats", LIB.moe_route_stats(ctypes.byref(cfg), _ptr(X), _ptr(Wg), _ptr(gate_bias),
+                                                  float(temperature), _ptr(topk_ids), _ptr(topk_w), _ptr(prob_mean),
+                                                  _ptr(sel_freq), _ptr(aux), _ptr(ws), int(ws_bytes),
+                                                  _stream(stream)))
 
 
 def moe_dispatch(cfg, topk_ids, X, expert_counts, expert_offsets, perm, inv_perm, Xp, ws, ws_bytes=None,

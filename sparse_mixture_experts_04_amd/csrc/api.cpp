@@ -1,6 +1,7 @@
 // C ABI of the MoE layer (declared in include/moe.h): argument checks,
 // workspace carving and the launch sequence.  Every check runs on the host
 // before anything is enqueued.
+#include <cmath>
 #include "../../include/moe.h"
 
 #include <hip/hip_runtime.h>
@@ -106,6 +107,9 @@ moe_status moe_workspace_size(const moe_config* cfg, int32_t op, size_t* bytes) 
   if (moe_status s = check_cfg(cfg); s != MOE_OK) return s;
   switch (op) {
     case MOE_OP_ROUTE: *bytes = route_bytes(cfg); return MOE_OK;
+    case MOE_OP_ROUTE_STATS:
+      *bytes = align256(route_bytes(cfg)) + moe::router_stats_scratch_bytes(cfg->num_tokens, cfg->num_experts);
+      return MOE_OK;
     case MOE_OP_DISPATCH: *bytes = dispatch_bytes(cfg); return MOE_OK;
     case MOE_OP_EXPERT_FFN: *bytes = h_bytes(cfg); return MOE_OK;
     case MOE_OP_FORWARD:
@@ -126,6 +130,28 @@ moe_status moe_route(const moe_config* cfg, const void* X, const void* Wg, const
   return hip_status(moe::launch_router(cfg->dtype, X, Wg, gate_bias, cfg->num_tokens, cfg->hidden_size,
                                        cfg->num_experts, cfg->num_experts_per_tok, topk_ids, topk_w, ws,
                                        as_stream(stream)));
+}
+
+moe_status moe_route_stats(const moe_config* cfg, const void* X, const void* Wg, const float* gate_bias,
+                           float temperature, int32_t* topk_ids, float* topk_w, float* prob_mean, float* sel_freq,
+                           float* aux, void* ws, size_t ws_bytes, void* stream) {
+  if (moe_status s = check_cfg(cfg); s != MOE_OK) return s;
+  if (!(temperature > 0.f) || !std::isfinite(temperature)) return MOE_ERR_INVALID_ARG;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if (!X || !Wg || !topk_ids || !topk_w || !prob_mean || !sel_freq || !aux) return MOE_ERR_INVALID_ARG;
+  size_t need = 0;
+  moe_workspace_size(cfg, MOE_OP_ROUTE_STATS, &need);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (ws == nullptr) return MOE_ERR_INVALID_ARG;
+  float* prob_sum = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + align256(route_bytes(cfg)));
+  if (hipError_t e = moe::launch_router(cfg->dtype, X, Wg, gate_bias, cfg->num_tokens, cfg->hidden_size,
+                                        cfg->num_experts, cfg->num_experts_per_tok, topk_ids, topk_w, ws,
+                                        as_stream(stream), /*select=*/true, 1.f / temperature, prob_sum);
+      e != hipSuccess)
+    return MOE_ERR_HIP;
+  return hip_status(moe::launch_router_stats(prob_sum, topk_ids, cfg->num_tokens, cfg->num_experts,
+                                             cfg->num_experts_per_tok, prob_mean, sel_freq, aux,
+                                             as_stream(stream)));
 }
 
 moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_ids, const void* X, int32_t* expert_counts,

@@ -32,6 +32,12 @@ namespace moe {
 namespace {
 
 constexpr int kRouterThreads = 256;               // 4 waves
+
+// Temperature and load-balancing statistics of a routing call (see topk_tile).
+struct RouteExtra {
+  float inv_tau;
+  float* prob_sum;
+};
 constexpr int kRouterTok = 32;                    // tokens per block: 2 row tiles of 16
 constexpr int kRowTiles = kRouterTok / 16;
 constexpr int kChunkBytes = 64;                   // K bytes per MFMA k-step per row (4 lane groups x 16 B)
@@ -109,7 +115,7 @@ template <typename T, int NT, bool kDirect>
 __global__ __launch_bounds__(kRouterThreads) void router_kernel(
     const T* __restrict__ X, const T* __restrict__ WgT, const T* __restrict__ Wg, const float* __restrict__ bias,
     int T_tokens, int d, int E, int k, int split_len, float* __restrict__ partial, int32_t* __restrict__ topk_ids,
-    float* __restrict__ topk_w) {
+    float* __restrict__ topk_w, float inv_tau, float* __restrict__ prob_sum) {
   constexpr int kStepElems = kChunkBytes / sizeof(T);  // K per k-step (32 bf16 / 16 fp32)
   __shared__ f32x4_t red[4][kRowTiles][NT][kWave];
   __shared__ float sel_val[2][16 * kMaxExperts];
@@ -210,7 +216,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(
     }
     return;
   }
-  topk_tile<NT>(sum, bias, E, k, rtok0, T_tokens, sel_val[r], sel_id[r], topk_ids, topk_w);
+  topk_tile<NT>(sum, bias, E, k, rtok0, T_tokens, sel_val[r], sel_id[r], topk_ids, topk_w, inv_tau, prob_sum);
 }
 
 // bf16 router for many tokens when the whole transposed gate fits in LDS
@@ -243,7 +249,8 @@ constexpr int kLdsRouterMaxGate = 64 * 1024;                      // gate elemen
 template <int NT, int RT>
 __global__ __launch_bounds__(kRouterThreads, 1) void router_lds_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wg, const float* __restrict__ bias, int T_tokens,
-    int d, int E, int k, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w) {
+    int d, int E, int k, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, float inv_tau,
+    float* __restrict__ prob_sum) {
   constexpr int WT = RT >= 4 ? 4 : RT;  // token groups of waves
   constexpr int WK = 4 / WT;            // K splits per token group
   constexpr int RW = RT / WT;           // row tiles per wave
@@ -448,7 +455,7 @@ __global__ __launch_bounds__(kRouterThreads, 1) void router_lds_kernel(
       static_for<RW>([&](auto r_c) {
         constexpr int r = decltype(r_c)::value;
         topk_tile<NT>(acc[r], bias, E, k, cur_base + (wt * RW + r) * 16, T_tokens, sel_val, sel_id, topk_ids,
-                      topk_w);
+                      topk_w, inv_tau, prob_sum);
       });
     }
     if (!more) break;
@@ -463,12 +470,63 @@ template <int NT>
 __global__ __launch_bounds__(1024) void router_topk_kernel(const float* __restrict__ partial, int nsplit,
                                                            const float* __restrict__ bias, int T_tokens, int E, int k,
                                                            int32_t* __restrict__ topk_ids,
-                                                           float* __restrict__ topk_w) {
+                                                           float* __restrict__ topk_w, float inv_tau,
+                                                           float* __restrict__ prob_sum) {
   __shared__ float logit[16][kMaxExperts];
   __shared__ float sel_val[16 * kMaxExperts];
   __shared__ int sel_id[16 * kMaxExperts];
   topk_from_partials<NT>(partial, nsplit, bias, T_tokens, E, k, blockIdx.x * 16, logit, sel_val, sel_id, topk_ids,
-                         topk_w);
+                         topk_w, inv_tau, prob_sum);
+}
+
+// The load-balancing statistics from the per-tile probability sums and the
+// selected ids ("Qwen2-MoE代码解析" §3.3): prob_mean[e] = (sum over tiles, in
+// tile order, of prob_sum[tile][e]) / T; sel_freq[e] = (tokens whose top-k
+// holds e) / T; aux = E * sum_e prob_mean[e] * sel_freq[e], summed in expert
+// order.  One block; thread (e, j) sums tiles j, j + 16, ... and the 16
+// partials meet in a fixed order, so the result is deterministic.
+constexpr int kStatsThreads = 1024;
+__global__ __launch_bounds__(kStatsThreads) void router_stats_kernel(const float* __restrict__ prob_sum, int ntiles,
+                                                                     const int32_t* __restrict__ ids, int T_tokens,
+                                                                     int E, int k, float* __restrict__ prob_mean,
+                                                                     float* __restrict__ sel_freq,
+                                                                     float* __restrict__ aux) {
+  __shared__ float s_part[16][kMaxExperts];
+  __shared__ int s_cnt[kMaxExperts];
+  __shared__ float s_pm[kMaxExperts], s_sf[kMaxExperts];
+  const int tid = threadIdx.x;
+  if (tid < kMaxExperts) s_cnt[tid] = 0;
+  __syncthreads();
+  {
+    const int e = tid % kMaxExperts;
+    const int j = tid / kMaxExperts;  // 0..15
+    float v = 0.f;
+    if (e < E)
+      for (int r = j; r < ntiles; r += 16) v += prob_sum[static_cast<int64_t>(r) * E + e];
+    s_part[j][e] = v;
+  }
+  const int64_t pairs = static_cast<int64_t>(T_tokens) * k;
+  for (int64_t q = tid; q < pairs; q += kStatsThreads) {
+    const int e = ids[q];
+    if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);  // integer counts: order-free
+  }
+  __syncthreads();
+  if (tid < E) {
+    float v = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v += s_part[j][tid];
+    const float inv_t = 1.f / static_cast<float>(T_tokens);
+    s_pm[tid] = v * inv_t;
+    s_sf[tid] = static_cast<float>(s_cnt[tid]) * inv_t;
+    prob_mean[tid] = s_pm[tid];
+    sel_freq[tid] = s_sf[tid];
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float a = 0.f;
+    for (int e = 0; e < E; ++e) a += s_pm[e] * s_sf[e];
+    aux[0] = static_cast<float>(E) * a;
+  }
 }
 
 // K per split: the whole d when there are enough token blocks, else d split
@@ -498,20 +556,20 @@ bool lds_router(int dtype, int T_tokens, int d, int E) {
 
 template <int NT, int RT>
 hipError_t launch_lds_rt(const uint16_t* X, const uint16_t* Wg, const float* bias, int T_tokens, int d, int E, int k,
-                         int32_t* ids, float* w, int grid, hipStream_t stream) {
+                         int32_t* ids, float* w, int grid, const RouteExtra& x, hipStream_t stream) {
   const size_t lds = static_cast<size_t>(16 * NT) * d * 2 + kLdsRouterScratch;
   static const hipError_t attr =
       hipFuncSetAttribute(reinterpret_cast<const void*>(&router_lds_kernel<NT, RT>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, kLdsRouterMaxGate * 2 + kLdsRouterScratch);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((router_lds_kernel<NT, RT>), dim3(grid), dim3(kRouterThreads), lds, stream, X, Wg, bias,
-                     T_tokens, d, E, k, ids, w);
+                     T_tokens, d, E, k, ids, w, x.inv_tau, x.prob_sum);
   return hipGetLastError();
 }
 
 template <int NT>
 hipError_t launch_lds(const uint16_t* X, const uint16_t* Wg, const float* bias, int T_tokens, int d, int E, int k,
-                      int32_t* ids, float* w, hipStream_t stream) {
+                      int32_t* ids, float* w, const RouteExtra& x, hipStream_t stream) {
   // One block per CU (fewer if there are fewer 16-token tiles), each with a
   // contiguous range of 16*RT tokens per pass.
   // The grid then shrinks to the blocks that have tokens in their first pass.
@@ -520,17 +578,18 @@ hipError_t launch_lds(const uint16_t* X, const uint16_t* Wg, const float* bias, 
   const int per = (tiles + cus - 1) / cus;
   const int rt = per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : 8;
   const int grid = std::min(cus, (tiles + rt - 1) / rt);
-  if (rt == 1) return launch_lds_rt<NT, 1>(X, Wg, bias, T_tokens, d, E, k, ids, w, grid, stream);
-  if (rt == 2) return launch_lds_rt<NT, 2>(X, Wg, bias, T_tokens, d, E, k, ids, w, grid, stream);
-  if (rt == 4) return launch_lds_rt<NT, 4>(X, Wg, bias, T_tokens, d, E, k, ids, w, grid, stream);
-  return launch_lds_rt<NT, 8>(X, Wg, bias, T_tokens, d, E, k, ids, w, grid, stream);
+  if (rt == 1) return launch_lds_rt<NT, 1>(X, Wg, bias, T_tokens, d, E, k, ids, w, grid, x, stream);
+  if (rt == 2) return launch_lds_rt<NT, 2>(X, Wg, bias, T_tokens, d, E, k, ids, w, grid, x, stream);
+  if (rt == 4) return launch_lds_rt<NT, 4>(X, Wg, bias, T_tokens, d, E, k, ids, w, grid, x, stream);
+  return launch_lds_rt<NT, 8>(X, Wg, bias, T_tokens, d, E, k, ids, w, grid, x, stream);
 }
 
 template <typename T, int NT>
 hipError_t launch_nt(const T* X, const T* Wg, const float* bias, int T_tokens, int d, int E, int k, int32_t* ids,
-                     float* w, unsigned char* scratch, bool select, hipStream_t stream) {
+                     float* w, unsigned char* scratch, bool select, const RouteExtra& x, hipStream_t stream) {
   if constexpr (std::is_same<T, uint16_t>::value) {
-    if (lds_router(kDtypeBF16, T_tokens, d, E)) return launch_lds<NT>(X, Wg, bias, T_tokens, d, E, k, ids, w, stream);
+    if (lds_router(kDtypeBF16, T_tokens, d, E))
+      return launch_lds<NT>(X, Wg, bias, T_tokens, d, E, k, ids, w, x, stream);
   }
   T* WgT = reinterpret_cast<T*>(scratch);
   float* partial = reinterpret_cast<float*>(scratch + gate_t_bytes(d, E, sizeof(T)));
@@ -540,26 +599,26 @@ hipError_t launch_nt(const T* X, const T* Wg, const float* bias, int T_tokens, i
   if (nsplit > 1) {
     // few token blocks: gather from W_g directly, no transpose launch
     hipLaunchKernelGGL((router_kernel<T, NT, true>), grid, dim3(kRouterThreads), 0, stream, X, WgT, Wg, bias, T_tokens,
-                       d, E, k, split_len, partial, ids, w);
+                       d, E, k, split_len, partial, ids, w, x.inv_tau, x.prob_sum);
   } else {
     hipLaunchKernelGGL((gate_transpose_kernel<T, NT>), dim3(d / 32), dim3(256), 0, stream, Wg, d, E, WgT);
     hipLaunchKernelGGL((router_kernel<T, NT, false>), grid, dim3(kRouterThreads), 0, stream, X, WgT, Wg, bias,
-                       T_tokens, d, E, k, split_len, nullptr, ids, w);
+                       T_tokens, d, E, k, split_len, nullptr, ids, w, x.inv_tau, x.prob_sum);
   }
   if (nsplit > 1 && select)
     hipLaunchKernelGGL((router_topk_kernel<NT>), dim3((T_tokens + 15) / 16), dim3(1024), 0, stream, partial, nsplit,
-                       bias, T_tokens, E, k, ids, w);
+                       bias, T_tokens, E, k, ids, w, x.inv_tau, x.prob_sum);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_t(const T* X, const T* Wg, const float* bias, int T_tokens, int d, int E, int k, int32_t* ids,
-                    float* w, unsigned char* scratch, bool select, hipStream_t stream) {
+                    float* w, unsigned char* scratch, bool select, const RouteExtra& x, hipStream_t stream) {
   switch ((E + 15) / 16) {
-    case 1: return launch_nt<T, 1>(X, Wg, bias, T_tokens, d, E, k, ids, w, scratch, select, stream);
-    case 2: return launch_nt<T, 2>(X, Wg, bias, T_tokens, d, E, k, ids, w, scratch, select, stream);
-    case 3: return launch_nt<T, 3>(X, Wg, bias, T_tokens, d, E, k, ids, w, scratch, select, stream);
-    default: return launch_nt<T, 4>(X, Wg, bias, T_tokens, d, E, k, ids, w, scratch, select, stream);
+    case 1: return launch_nt<T, 1>(X, Wg, bias, T_tokens, d, E, k, ids, w, scratch, select, x, stream);
+    case 2: return launch_nt<T, 2>(X, Wg, bias, T_tokens, d, E, k, ids, w, scratch, select, x, stream);
+    case 3: return launch_nt<T, 3>(X, Wg, bias, T_tokens, d, E, k, ids, w, scratch, select, x, stream);
+    default: return launch_nt<T, 4>(X, Wg, bias, T_tokens, d, E, k, ids, w, scratch, select, x, stream);
   }
 }
 
@@ -587,14 +646,28 @@ RouterSplit router_split(int T_tokens, int d, int E, int dtype, void* scratch) {
 }
 
 hipError_t launch_router(int dtype, const void* X, const void* Wg, const float* bias, int T_tokens, int d, int E,
-                         int k, int32_t* ids, float* w, void* scratch, hipStream_t stream, bool select) {
+                         int k, int32_t* ids, float* w, void* scratch, hipStream_t stream, bool select,
+                         float inv_tau, float* prob_sum) {
   if (T_tokens <= 0) return hipSuccess;
   unsigned char* sc = static_cast<unsigned char*>(scratch);
+  const RouteExtra x{inv_tau, prob_sum};
   if (dtype == kDtypeBF16)
     return launch_t(static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(Wg), bias, T_tokens, d, E, k, ids,
-                    w, sc, select, stream);
+                    w, sc, select, x, stream);
   return launch_t(static_cast<const float*>(X), static_cast<const float*>(Wg), bias, T_tokens, d, E, k, ids, w, sc,
-                  select, stream);
+                  select, x, stream);
+}
+
+size_t router_stats_scratch_bytes(int T_tokens, int E) {
+  return T_tokens <= 0 ? 0 : static_cast<size_t>((T_tokens + 15) / 16) * E * sizeof(float);
+}
+
+hipError_t launch_router_stats(const float* prob_sum, const int32_t* ids, int T_tokens, int E, int k,
+                               float* prob_mean, float* sel_freq, float* aux, hipStream_t stream) {
+  if (T_tokens <= 0) return hipSuccess;
+  hipLaunchKernelGGL(router_stats_kernel, dim3(1), dim3(kStatsThreads), 0, stream, prob_sum, (T_tokens + 15) / 16, ids,
+                     T_tokens, E, k, prob_mean, sel_freq, aux);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -31,6 +31,28 @@ __device__ __forceinline__ void argmax_dpp_step(float& bv, int& bi) {
   }
 }
 
+// Sum and max over each row of 16 lanes, left in every lane of the row (the
+// same pairing as argmax16: every step pairs each lane with one holding the
+// complementary part of the row).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float sum16(float v) {
+  v += dpp_move<0xB1>(v);
+  v += dpp_move<0x4E>(v);
+  v += dpp_move<0x141>(v);
+  v += dpp_move<0x140>(v);
+  return v;
+}
+__device__ __forceinline__ float max16(float v) {
+  v = fmaxf(v, dpp_move<0xB1>(v));
+  v = fmaxf(v, dpp_move<0x4E>(v));
+  v = fmaxf(v, dpp_move<0x141>(v));
+  v = fmaxf(v, dpp_move<0x140>(v));
+  return v;
+}
+
 // Arg-max over each row of 16 lanes, left in every lane of the row: pairs
 // (quad_perm 1,0,3,2), quads (quad_perm 2,3,0,1), then the two quads of each
 // half-row (row_half_mirror: lane i with 7-i) and the two halves
@@ -46,10 +68,21 @@ __device__ __forceinline__ void argmax16(float& bv, int& bi) {
 // Top-k + renormalisation for one 16-token row tile held in MFMA C layout:
 // acc[t][i] is the logit of token row (lane>>4)*4+i and expert t*16+(lane&15).
 // sel_val / sel_id: LDS scratch [16][k] of the calling wave.
+// inv_tau: 1 / router temperature.  The selection is on the logits (the
+// softmax at any temperature > 0 is monotone); the weights are
+// exp((l_s - l_0) * inv_tau) / sum_j exp((l_j - l_0) * inv_tau) over the
+// selected logits ("Qwen2-MoE代码解析" §3.1; the temperature: "GPT-4
+// activates 2%" article §5.2).  inv_tau = 1 gives the same bits as no
+// temperature.
+// prob_sum (may be null): row tok0/16 of a [ceil(T/16)][E] array receives,
+// per expert, the sum over the tile's tokens of the full router
+// probability softmax(logits * inv_tau) -- the per-tile part of the mean
+// probability of the load-balancing statistics ("Qwen2-MoE代码解析" §3.3).
 template <int NT>
 __device__ __forceinline__ void topk_tile(f32x4_t (&acc)[NT], const float* __restrict__ bias, int E, int k,
                                           int tok0, int T_tokens, float* sel_val, int* sel_id,
-                                          int32_t* __restrict__ topk_ids, float* __restrict__ topk_w) {
+                                          int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
+                                          float inv_tau = 1.f, float* __restrict__ prob_sum = nullptr) {
   const int lane = threadIdx.x % kWave;
   const int n = lane & 15;
   const int grp = lane >> 4;
@@ -59,6 +92,36 @@ __device__ __forceinline__ void topk_tile(f32x4_t (&acc)[NT], const float* __res
     const float b = (e < E && bias != nullptr) ? bias[e] : 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[t][i] = (e < E) ? acc[t][i] + b : -INFINITY;
+  }
+  if (prob_sum != nullptr && tok0 < T_tokens) {  // a tile wholly past T has no row in prob_sum
+    // Full softmax of each token row; column sums over the tile's tokens.
+    float col[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) col[t] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float m = acc[0][i];
+#pragma unroll
+      for (int t = 1; t < NT; ++t) m = fmaxf(m, acc[t][i]);
+      m = max16(m);
+      float z[NT], den = 0.f;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        z[t] = t * 16 + n < E ? expf((acc[t][i] - m) * inv_tau) : 0.f;
+        den += z[t];
+      }
+      den = sum16(den);
+      const bool live = tok0 + grp * 4 + i < T_tokens;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) col[t] += live ? z[t] / den : 0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      col[t] += __shfl_xor(col[t], 16);
+      col[t] += __shfl_xor(col[t], 32);
+      const int e = t * 16 + n;
+      if (grp == 0 && e < E) prob_sum[static_cast<int64_t>(tok0 / 16) * E + e] = col[t];
+    }
   }
   for (int s = 0; s < k; ++s) {
 #pragma unroll
@@ -90,10 +153,10 @@ __device__ __forceinline__ void topk_tile(f32x4_t (&acc)[NT], const float* __res
     const float* v = sel_val + row * kMaxExperts;
     const float l0 = v[0];
     float den = 0.f;
-    for (int j = 0; j < k; ++j) den += expf(v[j] - l0);
+    for (int j = 0; j < k; ++j) den += expf((v[j] - l0) * inv_tau);
     const int64_t o = static_cast<int64_t>(tok) * k + s;
     topk_ids[o] = sel_id[row * kMaxExperts + s];
-    topk_w[o] = expf(v[s] - l0) / den;
+    topk_w[o] = expf((v[s] - l0) * inv_tau) / den;
   }
 }
 
@@ -106,7 +169,8 @@ __device__ __forceinline__ void topk_from_partials(const float* __restrict__ par
                                                    const float* __restrict__ bias, int T_tokens, int E, int k,
                                                    int tok0, float (*logit)[kMaxExperts], float* sel_val,
                                                    int* sel_id, int32_t* __restrict__ topk_ids,
-                                                   float* __restrict__ topk_w) {
+                                                   float* __restrict__ topk_w, float inv_tau = 1.f,
+                                                   float* __restrict__ prob_sum = nullptr) {
   {
     const int r = threadIdx.x / kMaxExperts;
     const int e = threadIdx.x % kMaxExperts;
@@ -137,7 +201,7 @@ __device__ __forceinline__ void topk_from_partials(const float* __restrict__ par
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[t][i] = (e < E) ? logit[grp * 4 + i][e] : 0.f;
     }
-    topk_tile<NT>(acc, bias, E, k, tok0, T_tokens, sel_val, sel_id, topk_ids, topk_w);
+    topk_tile<NT>(acc, bias, E, k, tok0, T_tokens, sel_val, sel_id, topk_ids, topk_w, inv_tau, prob_sum);
   }
 }
 

@@ -170,3 +170,25 @@ def test_gathered_up_projection_rejects_before_launch():
         assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
     # T = 0 is a no-op for any pointers
     moe.moe_expert_up_gather(moe.config(0, 128, 128, 8, 2, -1, "bf16"), None, None, None, None, None, stream=0)
+
+
+def test_route_stats_rejects_before_launch():
+    cfg = moe.config(64, 128, 256, 8, 2, -1, "bf16")
+    need = moe.moe_workspace_size(cfg, moe.MOE_OP_ROUTE_STATS)
+    assert need >= moe.moe_workspace_size(cfg, moe.MOE_OP_ROUTE) + 4 * 8 * 4  # 4 tiles of 16 tokens x E floats
+    for tau in (0.0, -1.0, float("nan"), float("inf")):
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_route_stats(cfg, 1, 1, None, tau, 1, 1, 1, 1, 1, 1, need, stream=0)
+        assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    for i in range(7):
+        args = [1] * 7
+        args[i] = None
+        X, Wg, ids, w, pm, sf, aux = args
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_route_stats(cfg, X, Wg, None, 1.0, ids, w, pm, sf, aux, 1, need, stream=0)
+        assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_route_stats(cfg, 1, 1, None, 1.0, 1, 1, 1, 1, 1, 1, need - 1, stream=0)
+    assert ei.value.status == moe.MOE_ERR_WORKSPACE_TOO_SMALL
+    # T = 0: nothing to do, any pointers
+    moe.moe_route_stats(moe.config(0, 128, 256, 8, 2), None, None, None, 1.0, None, None, None, None, None, stream=0)

@@ -89,6 +89,60 @@ def test_route_many_tokens(T, d, E, k):
     check_routing(ids.cpu().numpy(), tw.cpu().numpy(), r)
 
 
+STATS_CASES = [c for c in CASES if c[0] in ("tiny_like", "ragged_bf16", "e64_tail", "cap_k4", "f32_e5_k3", "bf16_e3_k1",
+                                            "decode_like_splitk", "splitk_e24_f32", "single_token")]
+
+
+def _route_stats_dev(cfg, X, Wg, bias, tau, T, E, k):
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    tw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    pm = torch.full((E,), -1.0, dtype=torch.float32, device="cuda")
+    sf = torch.full((E,), -1.0, dtype=torch.float32, device="cuda")
+    aux = torch.full((1,), -1.0, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, moe.moe_workspace_size(cfg, moe.MOE_OP_ROUTE_STATS)), dtype=torch.uint8, device="cuda")
+    moe.moe_route_stats(cfg, X, Wg, bias, tau, ids, tw, pm, sf, aux, ws)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), tw.cpu().numpy(), pm.cpu().numpy(), sf.cpu().numpy(), float(aux.cpu()[0])
+
+
+def _check_route_stats(inp, cfg, tau):
+    w = inp.workload
+    X, Wg = to_dev(inp.X, w.dtype), to_dev(inp.Wg, w.dtype)
+    bias = to_dev(inp.bias, "f32")
+    ids, tw, pm, sf, aux = _route_stats_dev(cfg, X, Wg, bias, tau, w.T, w.E, w.k)
+    r = oracle.route(oracle.as_f64(inp.X, w.dtype), oracle.as_f64(inp.Wg, w.dtype), inp.bias, w.k, temperature=tau)
+    check_routing(ids, tw, r)
+    st = oracle.router_stats(r.probs, ids, w.E)  # frequencies of the ids the GPU selected
+    assert np.max(np.abs(pm - st.prob_mean)) <= 1e-5, "mean probabilities"
+    assert np.max(np.abs(sf - st.sel_freq)) <= 1e-6, "selection frequencies"
+    assert abs(aux - st.aux) <= 1e-5 * max(1.0, st.aux), "load-balancing value"
+    return X, Wg, bias, ids, tw
+
+
+@pytest.mark.parametrize("tau", [1.0, 0.5, 2.0])
+@pytest.mark.parametrize("case", STATS_CASES, ids=[c[0] for c in STATS_CASES])
+def test_route_stats(case, tau):
+    """Router temperature and load-balancing statistics against the oracle;
+    at tau = 1 ids and weights are bitwise those of moe_route."""
+    inp, cfg = make(case)
+    w = inp.workload
+    X, Wg, bias, ids, tw = _check_route_stats(inp, cfg, tau)
+    if tau == 1.0:
+        ids0 = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
+        tw0 = torch.empty((w.T, w.k), dtype=torch.float32, device="cuda")
+        rws = torch.empty(max(1, moe.moe_workspace_size(cfg, moe.MOE_OP_ROUTE)), dtype=torch.uint8, device="cuda")
+        moe.moe_route(cfg, X, Wg, bias, ids0, tw0, rws)
+        torch.cuda.synchronize()
+        assert np.array_equal(ids0.cpu().numpy(), ids) and np.array_equal(tw0.cpu().numpy(), tw)
+
+
+@pytest.mark.parametrize("T,d,E,k", [(12000, 256, 16, 2), (40000, 128, 8, 2), (9000, 128, 40, 3)],
+                         ids=["t12000_rows4", "t40000_two_passes", "e40_nt3"])
+def test_route_stats_many_tokens(T, d, E, k):
+    inp = workloads.random_case(171 + T, T, d, E, k, 64, "bf16", -1, 0.7, w_scale=0.05)
+    _check_route_stats(inp, moe.config(T, d, 64, E, k, -1, "bf16"), 0.7)
+
+
 @pytest.mark.parametrize("case", CASES, ids=IDS)
 def test_dispatch(case):
     inp, cfg = make(case)
