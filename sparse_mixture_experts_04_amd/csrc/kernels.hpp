@@ -31,16 +31,17 @@ size_t router_scratch_bytes(int T, int d, int E, int dtype);
 // select = false with a K-split router (small T) writes only the partial
 // logits: the caller selects (launch_topk_dispatch_small).
 // inv_tau: 1 / router temperature (weights exp((l_s - l_0) * inv_tau) / sum);
-// prob_sum (may be null): [ceil(T/16)][E] per-16-token-tile sums of the full
-// router probabilities, for launch_router_stats.
+// prob_sum (may be null): [ceil(T/16)][2E] per-16-token-tile sums of the full
+// router probabilities and selection counts, for launch_router_stats.
 hipError_t launch_router(int dtype, const void* X, const void* Wg, const float* bias, int T, int d, int E, int k,
                          int32_t* ids, float* w, void* scratch, hipStream_t stream, bool select = true,
                          float inv_tau = 1.f, float* prob_sum = nullptr);
 
-// The load-balancing statistics from launch_router's prob_sum and the ids:
-// prob_mean[E], sel_freq[E] and aux[1] (E * their dot product).
+// The load-balancing statistics from launch_router's prob_sum (at the start
+// of a router_stats_scratch_bytes(T, E) scratch, whose rest holds the block
+// partials): prob_mean[E], sel_freq[E] and aux[1] (E * their dot product).
 size_t router_stats_scratch_bytes(int T, int E);
-hipError_t launch_router_stats(const float* prob_sum, const int32_t* ids, int T, int E, int k, float* prob_mean,
+hipError_t launch_router_stats(float* prob_sum, const int32_t* ids, int T, int E, int k, float* prob_mean,
                                float* sel_freq, float* aux, hipStream_t stream);
 // Where the K-split partial logits live in the router scratch ([nsplit][T][E]
 // float); partial == nullptr when the router runs in one pass.

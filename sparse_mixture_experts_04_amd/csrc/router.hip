@@ -479,52 +479,67 @@ __global__ __launch_bounds__(1024) void router_topk_kernel(const float* __restri
                          topk_w, inv_tau, prob_sum);
 }
 
-// The load-balancing statistics from the per-tile probability sums and the
-// selected ids ("Qwen2-MoE代码解析" §3.3): prob_mean[e] = (sum over tiles, in
-// tile order, of prob_sum[tile][e]) / T; sel_freq[e] = (tokens whose top-k
-// holds e) / T; aux = E * sum_e prob_mean[e] * sel_freq[e], summed in expert
-// order.  One block; thread (e, j) sums tiles j, j + 16, ... and the 16
-// partials meet in a fixed order, so the result is deterministic.
-constexpr int kStatsThreads = 1024;
-__global__ __launch_bounds__(kStatsThreads) void router_stats_kernel(const float* __restrict__ prob_sum, int ntiles,
-                                                                     const int32_t* __restrict__ ids, int T_tokens,
-                                                                     int E, int k, float* __restrict__ prob_mean,
-                                                                     float* __restrict__ sel_freq,
-                                                                     float* __restrict__ aux) {
-  __shared__ float s_part[16][kMaxExperts];
-  __shared__ int s_cnt[kMaxExperts];
-  __shared__ float s_pm[kMaxExperts], s_sf[kMaxExperts];
-  const int tid = threadIdx.x;
-  if (tid < kMaxExperts) s_cnt[tid] = 0;
-  __syncthreads();
-  {
-    const int e = tid % kMaxExperts;
-    const int j = tid / kMaxExperts;  // 0..15
-    float v = 0.f;
-    if (e < E)
-      for (int r = j; r < ntiles; r += 16) v += prob_sum[static_cast<int64_t>(r) * E + e];
-    s_part[j][e] = v;
-  }
-  const int64_t pairs = static_cast<int64_t>(T_tokens) * k;
-  for (int64_t q = tid; q < pairs; q += kStatsThreads) {
-    const int e = ids[q];
-    if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);  // integer counts: order-free
-  }
-  __syncthreads();
-  if (tid < E) {
-    float v = 0.f;
+// The load-balancing statistics from the per-tile sums of topk_tile
+// ("Qwen2-MoE代码解析" §3.3): prob_sum is [ntiles][2E] (probability sums,
+// then selection counts, per 16-token tile).  Stage 1: block b sums tiles
+// 64b .. 64b+63 (thread (c, j) sums 8 of them with independent loads, the 8
+// partials meet in a fixed order) into part[b][2E].  Stage 2 (one block)
+// sums the blocks in order and writes prob_mean = sum / T, sel_freq =
+// count / T and aux = E * sum_e prob_mean[e] * sel_freq[e] (expert order).
+// Every sum runs in a fixed order, so the result is deterministic.
+constexpr int kStatsTilesPerBlock = 64;
+constexpr int kStatsThreads = 1024;  // 128 columns x 8 row groups
+
+__global__ __launch_bounds__(kStatsThreads) void router_stats_partial_kernel(const float* __restrict__ prob_sum,
+                                                                             int ntiles, int E,
+                                                                             float* __restrict__ part) {
+  __shared__ float s_part[8][2 * kMaxExperts];
+  const int c = threadIdx.x % (2 * kMaxExperts);
+  const int j = threadIdx.x / (2 * kMaxExperts);
+  const int cols = 2 * E;
+  const int r0 = blockIdx.x * kStatsTilesPerBlock + j * 8;
+  float v = 0.f;
+  if (c < cols) {
+    float x[8];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v += s_part[j][tid];
-    const float inv_t = 1.f / static_cast<float>(T_tokens);
-    s_pm[tid] = v * inv_t;
-    s_sf[tid] = static_cast<float>(s_cnt[tid]) * inv_t;
-    prob_mean[tid] = s_pm[tid];
-    sel_freq[tid] = s_sf[tid];
+    for (int q = 0; q < 8; ++q) {
+      const int r = min(r0 + q, ntiles - 1);  // in range; a row past the end is read and masked
+      x[q] = prob_sum[static_cast<int64_t>(r) * cols + c];
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v += r0 + q < ntiles ? x[q] : 0.f;
   }
+  s_part[j][c] = v;
   __syncthreads();
-  if (tid == 0) {
+  if (threadIdx.x < cols) {
+    float t = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) t += s_part[q][threadIdx.x];
+    part[static_cast<int64_t>(blockIdx.x) * cols + threadIdx.x] = t;
+  }
+}
+
+__global__ __launch_bounds__(2 * kMaxExperts) void router_stats_final_kernel(const float* __restrict__ part,
+                                                                             int nblocks, int T_tokens, int E,
+                                                                             float* __restrict__ prob_mean,
+                                                                             float* __restrict__ sel_freq,
+                                                                             float* __restrict__ aux) {
+  __shared__ float s_v[2 * kMaxExperts];
+  const int c = threadIdx.x;
+  const int cols = 2 * E;
+  float v = 0.f;
+  if (c < cols)
+    for (int b = 0; b < nblocks; ++b) v += part[static_cast<int64_t>(b) * cols + c];
+  const float inv_t = 1.f / static_cast<float>(T_tokens);
+  s_v[c] = v * inv_t;
+  __syncthreads();
+  if (c < E) {
+    prob_mean[c] = s_v[c];
+    sel_freq[c] = s_v[E + c];
+  }
+  if (c == 0) {
     float a = 0.f;
-    for (int e = 0; e < E; ++e) a += s_pm[e] * s_sf[e];
+    for (int e = 0; e < E; ++e) a += s_v[e] * s_v[E + e];
     aux[0] = static_cast<float>(E) * a;
   }
 }
@@ -659,14 +674,25 @@ hipError_t launch_router(int dtype, const void* X, const void* Wg, const float* 
 }
 
 size_t router_stats_scratch_bytes(int T_tokens, int E) {
-  return T_tokens <= 0 ? 0 : static_cast<size_t>((T_tokens + 15) / 16) * E * sizeof(float);
+  if (T_tokens <= 0) return 0;
+  const size_t ntiles = static_cast<size_t>((T_tokens + 15) / 16);
+  const size_t nblocks = (ntiles + kStatsTilesPerBlock - 1) / kStatsTilesPerBlock;
+  return align256(ntiles * 2 * E * sizeof(float)) + nblocks * 2 * E * sizeof(float);
 }
 
-hipError_t launch_router_stats(const float* prob_sum, const int32_t* ids, int T_tokens, int E, int k,
-                               float* prob_mean, float* sel_freq, float* aux, hipStream_t stream) {
+hipError_t launch_router_stats(float* prob_sum, const int32_t* ids, int T_tokens, int E, int k, float* prob_mean,
+                               float* sel_freq, float* aux, hipStream_t stream) {
+  (void)ids;
+  (void)k;
   if (T_tokens <= 0) return hipSuccess;
-  hipLaunchKernelGGL(router_stats_kernel, dim3(1), dim3(kStatsThreads), 0, stream, prob_sum, (T_tokens + 15) / 16, ids,
-                     T_tokens, E, k, prob_mean, sel_freq, aux);
+  const int ntiles = (T_tokens + 15) / 16;
+  const int nblocks = (ntiles + kStatsTilesPerBlock - 1) / kStatsTilesPerBlock;
+  float* part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(prob_sum) +
+                                         align256(static_cast<size_t>(ntiles) * 2 * E * sizeof(float)));
+  hipLaunchKernelGGL(router_stats_partial_kernel, dim3(nblocks), dim3(kStatsThreads), 0, stream, prob_sum, ntiles, E,
+                     part);
+  hipLaunchKernelGGL(router_stats_final_kernel, dim3(1), dim3(2 * kMaxExperts), 0, stream, part, nblocks, T_tokens,
+                     E, prob_mean, sel_freq, aux);
   return hipGetLastError();
 }
 

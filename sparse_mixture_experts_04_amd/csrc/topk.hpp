@@ -74,10 +74,11 @@ __device__ __forceinline__ void argmax16(float& bv, int& bi) {
 // selected logits ("Qwen2-MoE代码解析" §3.1; the temperature: "GPT-4
 // activates 2%" article §5.2).  inv_tau = 1 gives the same bits as no
 // temperature.
-// prob_sum (may be null): row tok0/16 of a [ceil(T/16)][E] array receives,
+// prob_sum (may be null): row tok0/16 of a [ceil(T/16)][2E] array receives,
 // per expert, the sum over the tile's tokens of the full router
-// probability softmax(logits * inv_tau) -- the per-tile part of the mean
-// probability of the load-balancing statistics ("Qwen2-MoE代码解析" §3.3).
+// probability softmax(logits * inv_tau), then the number of the tile's
+// tokens that select the expert -- the per-tile parts of the load-balancing
+// statistics ("Qwen2-MoE代码解析" §3.3).
 template <int NT>
 __device__ __forceinline__ void topk_tile(f32x4_t (&acc)[NT], const float* __restrict__ bias, int E, int k,
                                           int tok0, int T_tokens, float* sel_val, int* sel_id,
@@ -93,11 +94,14 @@ __device__ __forceinline__ void topk_tile(f32x4_t (&acc)[NT], const float* __res
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[t][i] = (e < E) ? acc[t][i] + b : -INFINITY;
   }
-  if (prob_sum != nullptr && tok0 < T_tokens) {  // a tile wholly past T has no row in prob_sum
-    // Full softmax of each token row; column sums over the tile's tokens.
-    float col[NT];
+  // Load-balancing statistics of the tile (prob_sum != null): col[t] sums the
+  // full softmax probability of expert t*16+n over the tile's live tokens,
+  // cnt[t] counts the tokens that select it.
+  const bool stats = prob_sum != nullptr && tok0 < T_tokens;  // a tile wholly past T has no row
+  float col[NT], cnt[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) col[t] = 0.f;
+  for (int t = 0; t < NT; ++t) col[t] = cnt[t] = 0.f;
+  if (stats) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float m = acc[0][i];
@@ -115,13 +119,6 @@ __device__ __forceinline__ void topk_tile(f32x4_t (&acc)[NT], const float* __res
 #pragma unroll
       for (int t = 0; t < NT; ++t) col[t] += live ? z[t] / den : 0.f;
     }
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      col[t] += __shfl_xor(col[t], 16);
-      col[t] += __shfl_xor(col[t], 32);
-      const int e = t * 16 + n;
-      if (grp == 0 && e < E) prob_sum[static_cast<int64_t>(tok0 / 16) * E + e] = col[t];
-    }
   }
   for (int s = 0; s < k; ++s) {
 #pragma unroll
@@ -133,13 +130,34 @@ __device__ __forceinline__ void topk_tile(f32x4_t (&acc)[NT], const float* __res
         if (better(acc[t][i], t * 16 + n, bv, bi)) { bv = acc[t][i]; bi = t * 16 + n; }
       argmax16(bv, bi);
       if ((bi & 15) == n) {
+        const bool live = tok0 + grp * 4 + i < T_tokens;
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-          if (t == (bi >> 4)) acc[t][i] = -INFINITY;
+          if (t == (bi >> 4)) {
+            acc[t][i] = -INFINITY;
+            if (live) cnt[t] += 1.f;
+          }
       }
       if (n == 0) {
         sel_val[(grp * 4 + i) * kMaxExperts + s] = bv;
         sel_id[(grp * 4 + i) * kMaxExperts + s] = bi;
+      }
+    }
+  }
+  if (stats) {
+    // Row tok0/16 of prob_sum ([ceil(T/16)][2E]): probability sums, then counts.
+    float* row = prob_sum + static_cast<int64_t>(tok0 / 16) * 2 * E;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      float c = col[t], q = cnt[t];
+      c += __shfl_xor(c, 16);
+      c += __shfl_xor(c, 32);
+      q += __shfl_xor(q, 16);
+      q += __shfl_xor(q, 32);
+      const int e = t * 16 + n;
+      if (grp == 0 && e < E) {
+        row[e] = c;
+        row[E + e] = q;
       }
     }
   }
