@@ -45,7 +45,7 @@ import numpy as np
 __all__ = [
     "as_f64", "gelu_tanh", "router_logits", "softmax", "topk_route", "route",
     "router_stats", "RouterStats",
-    "expert_capacity_formula", "capacity_keep", "dispatch", "expert_ffn",
+    "expert_capacity_formula", "expert_capacity_from_factor", "capacity_keep", "dispatch", "expert_ffn",
     "combine", "moe_forward", "dense_bruteforce", "Routing", "Dispatch",
 ]
 
@@ -156,6 +156,22 @@ def router_stats(probs: np.ndarray, ids: np.ndarray, E: int) -> RouterStats:
 def expert_capacity_formula(T: int, E: int, k: int) -> int:
     """expert_capacity = ceil(total_tokens / num_experts) * num_experts_per_tok [P3 §2.2]."""
     return int(math.ceil(T / E)) * k
+
+
+def expert_capacity_from_factor(batch: int, seq_len: int, E: int, k: int, factor: float = 2.0) -> int:
+    """The capacity-factor form of the expert capacity [P2 §3.4]: with
+    tokens_per_expert the mean number of tokens per expert (T / E, T = batch *
+    seq_len), C = int((tokens_per_expert * k * factor) // E), at most T; the
+    factor defaults to 2.0.  Autoregressive decoding (seq_len == 1) uses
+    min(512, 2 * batch) instead [P2 §5.2, its generate-mode fix].  (The page
+    prints C = 128 for batch 1, seq_len 32768, which this reading of
+    tokens_per_expert reproduces at 32 experts and k = 2.)"""
+    if seq_len == 1:
+        return min(512, 2 * batch)
+    T = batch * seq_len
+    tokens_per_expert = T / E
+    c = int((tokens_per_expert * k * factor) // E)
+    return min(c, T)
 
 
 def capacity_keep(ids: np.ndarray, E: int, capacity: int) -> np.ndarray:

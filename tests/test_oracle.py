@@ -66,6 +66,16 @@ def test_capacity_formula_golden():
     assert workloads.capacity_of(workloads.WORKLOADS["capacity"]) == 4096
 
 
+def test_capacity_factor_golden():
+    """The capacity-factor formula and the generate-mode override: the page's
+    printed capacity (128 at batch 1, seq_len 32768) and hand computations."""
+    for c in _golden("capacity_factor_example.json")["cases"]:
+        assert oracle.expert_capacity_from_factor(c["batch"], c["seq_len"], c["E"], c["k"], c["factor"]) == c["C"]
+    # never above the number of tokens; grows with the factor
+    assert oracle.expert_capacity_from_factor(1, 8, 2, 2, 100.0) == 8
+    assert oracle.expert_capacity_from_factor(16, 1024, 8, 2, 1.0) < oracle.expert_capacity_from_factor(16, 1024, 8, 2, 3.0)
+
+
 def test_capacity_hand_case():
     g = _golden("capacity_hand_case.json")
     ids = np.array(g["ids"])
