@@ -87,6 +87,17 @@ const char* moe_status_string(moe_status status);
 /* Library build description (static string). */
 const char* moe_version(void);
 
+/* Host only: the expert capacity from a capacity factor [jsqmd §3.4]:
+ * with T = batch * seq_len and tokens_per_expert = T / E (the mean tokens per
+ * expert), C = floor(tokens_per_expert * k * capacity_factor / E), at most T;
+ * in autoregressive decoding (seq_len == 1) C = min(512, 2 * batch) instead
+ * [jsqmd §5.2].  The result goes into moe_config.expert_capacity.
+ * Errors: INVALID_ARG for batch < 0, seq_len < 0, E < 1, k outside [1, E],
+ * a factor that is not finite and > 0, a null capacity, or C beyond int32. */
+moe_status moe_capacity_from_factor(int32_t batch, int32_t seq_len, int32_t num_experts,
+                                    int32_t num_experts_per_tok, double capacity_factor,
+                                    int32_t* capacity);
+
 /* Bytes of device workspace `op` needs for `cfg` (host only, no HIP call).
  * *bytes receives the size; 0 is possible.  Errors: INVALID_ARG, UNSUPPORTED. */
 moe_status moe_workspace_size(const moe_config* cfg, int32_t op, size_t* bytes);

@@ -32,7 +32,8 @@ MOE_OP_ROUTE = 3
 MOE_OP_ROUTE_STATS = 4
 
 # Every symbol include/moe.h declares.
-EXPORTED = ("moe_status_string", "moe_version", "moe_workspace_size", "moe_route", "moe_route_stats", "moe_dispatch",
+EXPORTED = ("moe_status_string", "moe_version", "moe_workspace_size", "moe_capacity_from_factor", "moe_route",
+            "moe_route_stats", "moe_dispatch",
             "moe_expert_up", "moe_expert_up_gather", "moe_expert_up_gather_supported", "moe_expert_down",
             "moe_expert_ffn", "moe_combine", "moe_forward")
 
@@ -65,6 +66,8 @@ def _load():
         "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "moe_version": (ctypes.c_char_p, []),
         "moe_workspace_size": (ctypes.c_int, [CFG, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]),
+        "moe_capacity_from_factor": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                    ctypes.c_double, ctypes.POINTER(ctypes.c_int32)]),
         "moe_route": (ctypes.c_int, [CFG, P, P, P, P, P, P, ctypes.c_size_t, P]),
         "moe_route_stats": (ctypes.c_int, [CFG, P, P, P, ctypes.c_float, P, P, P, P, P, P, ctypes.c_size_t, P]),
         "moe_dispatch": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
@@ -139,6 +142,13 @@ def moe_workspace_size(cfg: MoeConfig, op: int) -> int:
     n = ctypes.c_size_t(0)
     _check("moe_workspace_size", LIB.moe_workspace_size(ctypes.byref(cfg), int(op), ctypes.byref(n)))
     return n.value
+
+
+def moe_capacity_from_factor(batch: int, seq_len: int, E: int, k: int, factor: float = 2.0) -> int:
+    c = ctypes.c_int32(0)
+    _check("moe_capacity_from_factor",
+           LIB.moe_capacity_from_factor(int(batch), int(seq_len), int(E), int(k), float(factor), ctypes.byref(c)))
+    return c.value
 
 
 def moe_route(cfg, X, Wg, gate_bias, topk_ids, topk_w, ws=None, ws_bytes=None, stream=None) -> None:

@@ -1,6 +1,7 @@
 // C ABI of the MoE layer (declared in include/moe.h): argument checks,
 // workspace carving and the launch sequence.  Every check runs on the host
 // before anything is enqueued.
+#include <algorithm>
 #include <cmath>
 #include "../../include/moe.h"
 
@@ -101,6 +102,24 @@ const char* moe_status_string(moe_status status) {
 }
 
 const char* moe_version(void) { return "moe-gfx950 1 (router, dispatch, grouped MFMA GEMM, combine)"; }
+
+moe_status moe_capacity_from_factor(int32_t batch, int32_t seq_len, int32_t num_experts, int32_t num_experts_per_tok,
+                                    double capacity_factor, int32_t* capacity) {
+  if (capacity == nullptr || batch < 0 || seq_len < 0 || num_experts < 1 || num_experts_per_tok < 1 ||
+      num_experts_per_tok > num_experts || !(capacity_factor > 0.0) || !std::isfinite(capacity_factor))
+    return MOE_ERR_INVALID_ARG;
+  if (seq_len == 1) {
+    *capacity = std::min(512, 2 * batch);  // 2 * batch <= 2^31 - 2
+    return MOE_OK;
+  }
+  const double tokens = static_cast<double>(batch) * seq_len;
+  const double per_expert = tokens / num_experts;
+  double c = std::floor(per_expert * num_experts_per_tok * capacity_factor / num_experts);
+  if (c > tokens) c = tokens;
+  if (c > 2147483647.0) return MOE_ERR_INVALID_ARG;
+  *capacity = static_cast<int32_t>(c);
+  return MOE_OK;
+}
 
 moe_status moe_workspace_size(const moe_config* cfg, int32_t op, size_t* bytes) {
   if (bytes == nullptr) return MOE_ERR_INVALID_ARG;

@@ -3,6 +3,7 @@ function include/moe.h declares, sizes workspaces, and rejects bad arguments
 before touching the device (every call here fails validation, so nothing is
 enqueued)."""
 import ctypes
+import json
 import os
 import re
 import subprocess
@@ -192,3 +193,21 @@ def test_route_stats_rejects_before_launch():
     assert ei.value.status == moe.MOE_ERR_WORKSPACE_TOO_SMALL
     # T = 0: nothing to do, any pointers
     moe.moe_route_stats(moe.config(0, 128, 256, 8, 2), None, None, None, 1.0, None, None, None, None, None, stream=0)
+
+
+def test_capacity_from_factor_matches_oracle():
+    import oracle
+    for c in json.load(open(os.path.join(ROOT, "tests", "golden", "capacity_factor_example.json"),
+                            encoding="utf-8"))["cases"]:
+        assert moe.moe_capacity_from_factor(c["batch"], c["seq_len"], c["E"], c["k"], c["factor"]) == c["C"]
+    for batch in (0, 1, 3, 16, 300):
+        for seq in (0, 1, 2, 7, 512, 4096):
+            for E, k in ((1, 1), (8, 2), (32, 4), (64, 8)):
+                for f in (0.5, 1.0, 1.25, 2.0, 4.0):
+                    assert moe.moe_capacity_from_factor(batch, seq, E, k, f) == \
+                        oracle.expert_capacity_from_factor(batch, seq, E, k, f), (batch, seq, E, k, f)
+    for bad in ((-1, 8, 8, 2, 2.0), (1, -1, 8, 2, 2.0), (1, 8, 0, 1, 2.0), (1, 8, 8, 9, 2.0), (1, 8, 8, 2, 0.0),
+                (1, 8, 8, 2, float("inf"))):
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_capacity_from_factor(*bad)
+        assert ei.value.status == moe.MOE_ERR_INVALID_ARG
