@@ -16,7 +16,9 @@ What the layer computes, step by step (each function below cites its step):
                                                             temperature tau: P4 §5.2]
   statistics  mean probability and selection frequency per expert, and
               E * their dot product                         [P2 §3.3]
-  capacity    C = ceil(T/E) * k; pairs beyond C per expert dropped [P3 §2.2]
+  capacity    C = ceil(T/E) * k; pairs beyond C per expert dropped [P3 §2.2],
+              or rerouted to the token's next-best expert with room
+              (drop_tokens = False)                             [P2 §3.4]
   dispatch    group (token, slot) pairs by expert              [P2 §3.1 detail 3; P4 §2.2]
   experts     per expert Linear -> GELU -> Linear              [P3 §2.2; P4 §2.2]
   combine     weighted sum of the k expert outputs per token   [P2 §3.1 detail 2]
@@ -28,7 +30,12 @@ Readings taken where the pages are silent (each also listed in the design notes)
     over the top-k before any drop and is not redone; a dropped pair adds zero;
   * expert_capacity < 0 means dropless; 0 drops every pair;
   * the dispatch order is stable by (expert, token) -- unique, since a token
-    picks an expert at most once.
+    picks an expert at most once (rerouting keeps that true);
+  * rerouting (drop_tokens = False): the capacity cut runs first, unchanged;
+    then the pairs it would drop, in the same (slot rank, token index)
+    priority, each move to the best-ranked expert of their token outside its
+    top-k that still has room and that the token does not already use; a
+    pair finding none is dropped; a moved pair keeps its renormalised weight.
 
 Every computation is float64 on the already-rounded inputs (bf16 bit patterns
 are widened exactly).  Parity of this module is pinned by tests/test_oracle.py
@@ -45,7 +52,8 @@ import numpy as np
 __all__ = [
     "as_f64", "gelu_tanh", "router_logits", "softmax", "topk_route", "route",
     "router_stats", "RouterStats",
-    "expert_capacity_formula", "expert_capacity_from_factor", "capacity_keep", "dispatch", "expert_ffn",
+    "expert_capacity_formula", "expert_capacity_from_factor", "capacity_keep", "expert_ranking",
+    "reroute_overflow", "dispatch", "expert_ffn",
     "combine", "moe_forward", "dense_bruteforce", "Routing", "Dispatch",
 ]
 
@@ -194,6 +202,67 @@ def capacity_keep(ids: np.ndarray, E: int, capacity: int) -> np.ndarray:
     return keep
 
 
+def expert_ranking(probs: np.ndarray):
+    """Each token's experts in preference order: probability descending, ties
+    to the lower expert id (the order the top-k takes its first k from)
+    [P2 §3.1].  Returns (order [T, E] int64, margin [T] float64), the margin
+    being the smallest gap between adjacent probabilities along the whole
+    order -- how close the order is to a tie anywhere (inf when E = 1)."""
+    T, E = probs.shape
+    order = np.empty((T, E), dtype=np.int64)
+    margin = np.full(T, np.inf)
+    expert = np.arange(E)
+    for t in range(T):
+        o = np.lexsort((expert, -probs[t]))
+        order[t] = o
+        if E > 1:
+            pv = probs[t, o]
+            margin[t] = np.min(pv[:-1] - pv[1:])
+    return order, margin
+
+
+def reroute_overflow(ids: np.ndarray, order: np.ndarray, keep: np.ndarray, E: int,
+                     capacity: int):
+    """Over-capacity pairs routed to the next-best expert instead of dropped
+    [P2 §3.4: with drop_tokens = False, tokens over capacity go to a
+    sub-optimal expert rather than being discarded].
+
+    Reading (the page gives the rule in one sentence): the capacity cut of
+    ``capacity_keep`` stands -- a pair it keeps is never moved.  The pairs it
+    drops are then taken in the same (slot rank, token index) priority; each
+    walks its token's order past the top-k (positions k, k+1, ..., E-1) and
+    takes the first expert that has fewer than ``capacity`` pairs and that
+    its token does not already use (an earlier slot may have moved there); if
+    there is none the pair stays dropped.  Weights are not touched.
+
+    ids, keep: [T, k]; order: [T, E] (``expert_ranking``).  Returns
+    (assigned [T, k] int64, keep [T, k] bool): the expert each pair ends at
+    (its own id when it is not moved) and whether it is computed."""
+    T, k = ids.shape
+    assigned = np.array(ids, dtype=np.int64, copy=True)
+    keep = np.array(keep, dtype=bool, copy=True)
+    if capacity < 0:
+        return assigned, keep
+    load = np.zeros(E, dtype=np.int64)
+    for t in range(T):
+        for s in range(k):
+            if keep[t, s]:
+                load[ids[t, s]] += 1
+    for s in range(k):              # the drop priority: slot rank first ...
+        for t in range(T):          # ... then token index
+            if keep[t, s]:
+                continue
+            used = set(int(assigned[t, j]) for j in range(k) if j != s)
+            for pos in range(k, E):
+                e = int(order[t, pos])
+                if load[e] < capacity and e not in used:
+                    assigned[t, s] = e
+                    keep[t, s] = True
+                    load[e] += 1
+                    break
+    return assigned, keep
+
+
 @dataclass
 class Dispatch:
     counts: np.ndarray    # [E] int64, routed pairs per expert (before any drop)
@@ -201,18 +270,26 @@ class Dispatch:
     offsets: np.ndarray   # [E+1] int64, exclusive scan of kept counts
     perm: np.ndarray      # [N] int64, pair id t*k+s of each expert-ordered row
     inv_perm: np.ndarray  # [T*k] int64, row of pair t*k+s, -1 if dropped
+    assigned: np.ndarray  # [T, k] int64, expert each pair is computed by (= ids unless rerouted)
 
 
-def dispatch(ids: np.ndarray, E: int, capacity: int = -1) -> Dispatch:
+def dispatch(ids: np.ndarray, E: int, capacity: int = -1,
+             reroute_order: Optional[np.ndarray] = None) -> Dispatch:
     """Group the kept (token, slot) pairs by expert [P2 §3.1 detail 3: tokens
     are regrouped by expert id with a sort; P4 §2.2: the dispatcher gathers each
     expert's token slices].  Rows are ordered by (expert, token); offsets are
-    the exclusive scan of the kept counts (no padding)."""
+    the exclusive scan of the kept counts (no padding).  With
+    ``reroute_order`` (the tokens' ``expert_ranking``) and a capacity, the
+    pairs over capacity are rerouted (``reroute_overflow``) rather than
+    dropped, and grouped under the expert they move to."""
     T, k = ids.shape
     counts = np.bincount(ids.reshape(-1), minlength=E).astype(np.int64)
     keep = capacity_keep(ids, E, capacity)
+    assigned = np.array(ids, dtype=np.int64, copy=True)
+    if reroute_order is not None:
+        assigned, keep = reroute_overflow(ids, reroute_order, keep, E, capacity)
     t_idx, s_idx = np.nonzero(keep)                      # kept pairs
-    e_idx = ids[t_idx, s_idx]
+    e_idx = assigned[t_idx, s_idx]
     order = np.lexsort((t_idx, e_idx))                   # sort by expert, then token
     perm = (t_idx * k + s_idx)[order]
     kept = np.bincount(e_idx, minlength=E).astype(np.int64)
@@ -220,7 +297,7 @@ def dispatch(ids: np.ndarray, E: int, capacity: int = -1) -> Dispatch:
     offsets[1:] = np.cumsum(kept)
     inv_perm = np.full(T * k, -1, dtype=np.int64)
     inv_perm[perm] = np.arange(len(perm))
-    return Dispatch(counts, keep, offsets, perm, inv_perm)
+    return Dispatch(counts, keep, offsets, perm, inv_perm, assigned)
 
 
 # --------------------------------------------------------------------------- experts
@@ -254,8 +331,9 @@ def combine(tokens: np.ndarray, d: int, weights: np.ndarray, keep: np.ndarray,
 
 # --------------------------------------------------------------------------- layer
 def moe_forward(X, Wg, bias, W1, W2, k: int, capacity: int = -1, dtype: str = "f32",
-                tokens: Optional[Sequence[int]] = None):
-    """The whole layer [P3 §3.2 steps 1-5].
+                tokens: Optional[Sequence[int]] = None, reroute: bool = False):
+    """The whole layer [P3 §3.2 steps 1-5].  ``reroute``: over-capacity pairs
+    move to the next-best expert with room instead of being dropped [P2 §3.4].
 
     Inputs are the raw arrays of a workload (bf16 bit patterns when ``dtype`` is
     "bf16").  Routing and dispatch always cover all T tokens (the capacity cut
@@ -266,13 +344,14 @@ def moe_forward(X, Wg, bias, W1, W2, k: int, capacity: int = -1, dtype: str = "f
     T, d = Xf.shape
     E = Wg.shape[1]
     r = route(Xf, as_f64(Wg, dtype), bias, k)
-    disp = dispatch(r.ids, E, capacity)
+    order = expert_ranking(r.probs)[0] if reroute else None
+    disp = dispatch(r.ids, E, capacity, order)
     toks = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
     need = {}
     for t in toks:
         for s in range(k):
             if disp.keep[t, s]:
-                need.setdefault(int(r.ids[t, s]), []).append((int(t), s))
+                need.setdefault(int(disp.assigned[t, s]), []).append((int(t), s))
     y_pairs = {}
     for e, pairs in sorted(need.items()):
         W1e = as_f64(W1[e], dtype)

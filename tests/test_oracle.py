@@ -292,6 +292,168 @@ def test_capacity_bruteforce_and_limits():
     assert (full.perm == big.perm).all() and (full.inv_perm == big.inv_perm).all()
 
 
+# ----------------------------------------------------------------- rerouting
+def _random_order_case(rng, T, E, k):
+    """Random preferences: a strict order per token; ids are its first k."""
+    order = np.stack([rng.permutation(E) for _ in range(T)])
+    return order, order[:, :k].copy()
+
+
+def test_reroute_hand_case():
+    g = _golden("reroute_hand_case.json")
+    logits = np.array(g["logits"], dtype=np.float64)
+    p = oracle.softmax(logits)
+    ids, _, _ = oracle.topk_route(p, g["k"])
+    order, _ = oracle.expert_ranking(p)
+    assert ids.tolist() == g["ids"] and order.tolist() == g["preference_order"]
+    for c in g["cases"]:
+        d = oracle.dispatch(ids, g["E"], c["capacity"], order)
+        assert d.assigned.tolist() == c["assigned"]
+        assert d.keep.tolist() == c["keep"]
+        assert d.offsets.tolist() == c["offsets"] and d.perm.tolist() == c["perm"]
+        assert d.counts.tolist() == np.bincount(ids.reshape(-1), minlength=g["E"]).tolist()
+
+
+def test_expert_ranking_matches_topk_and_margin():
+    rng = np.random.default_rng(5)
+    p = oracle.softmax(rng.standard_normal((30, 7)))
+    order, margin = oracle.expert_ranking(p)
+    for k in (1, 3, 7):
+        ids, _, _ = oracle.topk_route(p, k)
+        assert (order[:, :k] == ids).all()
+    for t in range(30):
+        assert sorted(order[t].tolist()) == list(range(7))
+        sp = np.sort(p[t])[::-1]
+        assert margin[t] == pytest.approx(np.min(sp[:-1] - sp[1:]), abs=0)
+        assert (np.diff(p[t, order[t]]) <= 0).all()
+
+
+@pytest.mark.parametrize("seed,T,E,k,cap", [(0, 60, 8, 2, 9), (1, 50, 6, 3, 20), (2, 80, 5, 1, 10),
+                                             (3, 40, 8, 4, 12), (4, 33, 4, 2, 0), (5, 70, 16, 2, 6)])
+def test_reroute_invariants(seed, T, E, k, cap):
+    """Necessary conditions of the rule, checked without its loop: the cut's
+    kept pairs stay put; loads stay within capacity; a moved pair lands past
+    its token's top-k on an expert its token uses once; every expert a moved
+    pair passed over is full at the end (room only shrinks) or used by an
+    earlier slot of its token; a pair left dropped finds every candidate so."""
+    rng = np.random.default_rng(seed)
+    order, ids = _random_order_case(rng, T, E, k)
+    base = oracle.dispatch(ids, E, cap)
+    d = oracle.dispatch(ids, E, cap, order)
+    assert (d.assigned[base.keep] == ids[base.keep]).all() and d.keep[base.keep].all()
+    load = np.bincount(d.assigned[d.keep], minlength=E)
+    assert (load <= cap).all()
+    assert (d.counts == base.counts).all()
+    pos = np.argsort(order, axis=1)                      # pos[t, e]: place of e in t's order
+    for t in range(T):
+        live = [int(d.assigned[t, s]) for s in range(k) if d.keep[t, s]]
+        assert len(set(live)) == len(live)
+        for s in range(k):
+            if base.keep[t, s]:
+                continue
+            earlier = {int(d.assigned[t, j]) for j in range(s) if d.keep[t, j]}
+            stop = pos[t, d.assigned[t, s]] if d.keep[t, s] else E
+            if d.keep[t, s]:
+                assert stop >= k
+            for q in range(k, stop):
+                e = int(order[t, q])
+                assert load[e] == cap or e in earlier
+    # bijection and (expert, token) order of the rows, as for the plain cut
+    N = int(d.keep.sum())
+    assert d.offsets[-1] == N and (d.inv_perm[d.perm] == np.arange(N)).all()
+    e_rows = d.assigned.reshape(-1)[d.perm]
+    assert (np.diff(e_rows * T + d.perm // k) > 0).all()
+
+
+def test_reroute_is_lexicographic_best_by_brute_force():
+    """Taken in priority order, the moved pairs' places in their tokens'
+    orders form the lexicographically smallest vector over every feasible
+    placement (capacity per expert, a token on an expert at most once, any
+    pair may stay dropped): enumerate all placements of tiny cases."""
+    from itertools import product
+    rng = np.random.default_rng(21)
+    checked = 0
+    for trial in range(40):
+        T, E, k = int(rng.integers(2, 6)), int(rng.integers(2, 5)), 0
+        k = int(rng.integers(1, E + 1))
+        cap = int(rng.integers(0, 3))
+        order, ids = _random_order_case(rng, T, E, k)
+        keep0 = oracle.capacity_keep(ids, E, cap)
+        dropped = [(t, s) for s in range(k) for t in range(T) if not keep0[t, s]]
+        if len(dropped) > 7:
+            continue
+        load0 = np.bincount(ids[keep0], minlength=E)
+        options = [[int(order[t, q]) for q in range(k, E)] + [None] for t, s in dropped]
+        best = None
+        for choice in product(*options):
+            load = load0.copy()
+            used = {t: set() for t in range(T)}
+            ok = True
+            for (t, s), e in zip(dropped, choice):
+                if e is None:
+                    continue
+                load[e] += 1
+                if load[e] > cap or e in used[t]:
+                    ok = False
+                    break
+                used[t].add(e)
+            if not ok:
+                continue
+            vec = tuple(E if e is None else int(np.where(order[t] == e)[0][0])
+                        for (t, s), e in zip(dropped, choice))
+            if best is None or vec < best[0]:
+                best = (vec, choice)
+        assigned, keep = oracle.reroute_overflow(ids, order, keep0, E, cap)
+        for (t, s), e in zip(dropped, best[1]):
+            assert keep[t, s] == (e is not None)
+            if e is not None:
+                assert assigned[t, s] == e
+        checked += 1
+    assert checked >= 20
+
+
+def test_reroute_limits():
+    rng = np.random.default_rng(8)
+    T, E, k = 45, 6, 2
+    order, ids = _random_order_case(rng, T, E, k)
+    full = oracle.dispatch(ids, E, -1)
+    # capacity at the largest load: nothing overflows, nothing moves
+    d = oracle.dispatch(ids, E, int(full.counts.max()), order)
+    assert (d.assigned == ids).all() and d.keep.all() and (d.perm == full.perm).all()
+    # capacity 0: nothing has room, every pair stays dropped
+    z = oracle.dispatch(ids, E, 0, order)
+    assert not z.keep.any() and len(z.perm) == 0
+    # k = E: no expert lies past the top-k, so rerouting is the plain cut
+    order_e, ids_e = _random_order_case(rng, 20, 4, 4)
+    a = oracle.dispatch(ids_e, 4, 7, order_e)
+    b = oracle.dispatch(ids_e, 4, 7)
+    assert (a.keep == b.keep).all() and (a.perm == b.perm).all()
+    # total room T*k: with k = 1 every token finds an expert (one option per place)
+    order1, ids1 = _random_order_case(rng, 40, 8, 1)
+    c = oracle.dispatch(ids1, 8, 5, order1)
+    assert c.keep.all() and (np.bincount(c.assigned[:, 0], minlength=8) == 5).all()
+
+
+def test_reroute_layer_equals_dense_mask():
+    """The rerouted layer equals every expert run on every token, masked by
+    the moved pairs' weights (computed expert by expert, independently of the
+    sparse grouping)."""
+    case = _case(13, T=30, d=16, E=5, k=2, F=24, bias_scale=1.5)
+    cap = 8
+    out, r, d = oracle.moe_forward(case.X, case.Wg, case.bias, case.W1, case.W2, 2, cap, reroute=True)
+    assert d.keep.sum() > oracle.dispatch(r.ids, 5, cap).keep.sum()  # some pairs did move
+    Xf = oracle.as_f64(case.X, "f32")
+    ref = np.zeros_like(out)
+    for e in range(5):
+        h = Xf @ oracle.as_f64(case.W1[e], "f32").T
+        h = 0.5 * h * (1 + np.tanh(math.sqrt(2 / math.pi) * (h + 0.044715 * h ** 3)))
+        ye = h @ oracle.as_f64(case.W2[e], "f32").T
+        m = np.array([sum(r.weights[t, s] for s in range(2) if d.keep[t, s] and d.assigned[t, s] == e)
+                      for t in range(30)])
+        ref += m[:, None] * ye
+    assert np.abs(out - ref).max() < 1e-12
+
+
 # ----------------------------------------------------------------- expert FFN
 def test_single_expert_is_dense_ffn():
     """E = 1, k = 1: the layer is the textbook FFN Linear-GELU-Linear."""
