@@ -78,7 +78,9 @@ typedef enum moe_op {
   MOE_OP_EXPERT_FFN = 1, /* moe_expert_ffn (holds H)                      */
   MOE_OP_FORWARD = 2,    /* moe_forward (all scratch + Xp + H + Yp)       */
   MOE_OP_ROUTE = 3,      /* moe_route (partial logits when K is split)    */
-  MOE_OP_ROUTE_STATS = 4 /* moe_route_stats (as moe_route + per-tile sums) */
+  MOE_OP_ROUTE_STATS = 4, /* moe_route_stats (as moe_route + per-tile sums) */
+  MOE_OP_DISPATCH_REROUTE = 5, /* moe_dispatch_reroute (as moe_dispatch + ids) */
+  MOE_OP_FORWARD_REROUTE = 6   /* moe_forward_reroute                         */
 } moe_op;
 
 /* Human-readable name of a status.  Static string; never NULL. */
@@ -206,6 +208,53 @@ moe_status moe_forward(const moe_config* cfg, const void* X, const void* Wg,
                        int32_t* topk_ids, float* topk_w, int32_t* expert_counts,
                        int32_t* expert_offsets, int32_t* perm, int32_t* inv_perm,
                        void* ws, size_t ws_bytes, void* stream);
+
+/* Router that also returns every token's full preference order, the list
+ * the over-capacity rerouting below walks [jsqmd §3.1 (softmax, top-k);
+ * §3.4 (drop_tokens = False)].  Same topk_ids and topk_w, bit for bit, as
+ * moe_route, and
+ *   expert_order [T, E] uint8 out: row t holds all E expert ids of token t
+ *   in descending probability, equal logits to the lower id; its first k
+ *   entries equal topk_ids[t].
+ * ws / ws_bytes: as moe_route (moe_workspace_size(cfg, MOE_OP_ROUTE)). */
+moe_status moe_route_ranked(const moe_config* cfg, const void* X, const void* Wg,
+                            const float* gate_bias, int32_t* topk_ids, float* topk_w,
+                            uint8_t* expert_order, void* ws, size_t ws_bytes, void* stream);
+
+/* Dispatch with over-capacity pairs rerouted instead of dropped [jsqmd §3.4:
+ * with drop_tokens = False a token over an expert's capacity goes to a
+ * next-best expert].  The capacity cut of moe_dispatch stands (the pairs it
+ * keeps do not move).  The pairs it drops are then taken in the same
+ * (slot, token) priority; each moves to the first expert of its token's
+ * expert_order past position k-1 that holds fewer than C pairs and that the
+ * token does not already use (an earlier slot may have moved there); a pair
+ * that finds none stays dropped.  Weights are unchanged: a moved pair still
+ * carries topk_w[t, s].
+ *   topk_ids [T, k], expert_order [T, E] (from moe_route_ranked) in.
+ *   Outputs as moe_dispatch, under the final assignment: expert_counts holds
+ *   the routed counts of topk_ids (before the cut); offsets, perm, inv_perm
+ *   and Xp group the computed pairs by the expert they end at, rows ordered
+ *   by (expert, token).  The expert of a computed pair is the e with
+ *   offsets[e] <= inv_perm[t*k+s] < offsets[e+1].
+ *   expert_capacity < 0: nothing overflows, the result is moe_dispatch's.
+ *   ws / ws_bytes: moe_workspace_size(cfg, MOE_OP_DISPATCH_REROUTE) bytes.
+ * The placement runs in one workgroup and takes time in proportion to the
+ * dropped pairs. */
+moe_status moe_dispatch_reroute(const moe_config* cfg, const int32_t* topk_ids,
+                                const uint8_t* expert_order, const void* X,
+                                int32_t* expert_counts, int32_t* expert_offsets, int32_t* perm,
+                                int32_t* inv_perm, void* Xp, void* ws, size_t ws_bytes,
+                                void* stream);
+
+/* The whole layer with over-capacity rerouting: moe_route_ranked,
+ * moe_dispatch_reroute, the expert FFN and the combine, with the
+ * intermediates in ws (moe_workspace_size(cfg, MOE_OP_FORWARD_REROUTE)).
+ * Arguments as moe_forward plus expert_order [T, E] uint8 out. */
+moe_status moe_forward_reroute(const moe_config* cfg, const void* X, const void* Wg,
+                               const float* gate_bias, const void* W1, const void* W2, void* out,
+                               int32_t* topk_ids, float* topk_w, uint8_t* expert_order,
+                               int32_t* expert_counts, int32_t* expert_offsets, int32_t* perm,
+                               int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

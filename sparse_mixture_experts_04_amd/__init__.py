@@ -8,9 +8,11 @@ missing: there is no CPU or PyTorch fallback.
 """
 from ._lib import (MOE_BF16, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED,  # noqa: F401
                    MOE_ERR_WORKSPACE_TOO_SMALL, MOE_F32, MOE_OK, MOE_OP_DISPATCH, MOE_OP_EXPERT_FFN,
-                   MOE_OP_FORWARD, MOE_OP_ROUTE, MOE_OP_ROUTE_STATS, EXPORTED, LIB, LIB_PATH, MoeConfig, MoeError,
+                   MOE_OP_FORWARD, MOE_OP_ROUTE, MOE_OP_ROUTE_STATS, MOE_OP_DISPATCH_REROUTE,
+                   MOE_OP_FORWARD_REROUTE, EXPORTED, LIB, LIB_PATH, MoeConfig, MoeError,
                    config, moe_capacity_from_factor, moe_combine, moe_dispatch, moe_expert_down, moe_expert_ffn,
                    moe_expert_up,
                    moe_expert_up_gather, moe_expert_up_gather_supported, moe_forward, moe_route, moe_route_stats,
-                   moe_workspace_size, status_string, version)
+                   moe_workspace_size, moe_route_ranked, moe_dispatch_reroute, moe_forward_reroute,
+                   status_string, version)
 from .layer import ForwardBuffers, MoELayer  # noqa: F401

@@ -30,12 +30,15 @@ MOE_OP_EXPERT_FFN = 1
 MOE_OP_FORWARD = 2
 MOE_OP_ROUTE = 3
 MOE_OP_ROUTE_STATS = 4
+MOE_OP_DISPATCH_REROUTE = 5
+MOE_OP_FORWARD_REROUTE = 6
 
 # Every symbol include/moe.h declares.
 EXPORTED = ("moe_status_string", "moe_version", "moe_workspace_size", "moe_capacity_from_factor", "moe_route",
             "moe_route_stats", "moe_dispatch",
             "moe_expert_up", "moe_expert_up_gather", "moe_expert_up_gather_supported", "moe_expert_down",
-            "moe_expert_ffn", "moe_combine", "moe_forward")
+            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_route_ranked", "moe_dispatch_reroute",
+            "moe_forward_reroute")
 
 
 class MoeConfig(ctypes.Structure):
@@ -78,6 +81,10 @@ def _load():
         "moe_expert_ffn": (ctypes.c_int, [CFG, P, P, P, P, P, P, ctypes.c_size_t, P]),
         "moe_combine": (ctypes.c_int, [CFG, P, P, P, P, P]),
         "moe_forward": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "moe_route_ranked": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "moe_dispatch_reroute": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "moe_forward_reroute": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t,
+                                               P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -219,3 +226,33 @@ def moe_forward(cfg, X, Wg, gate_bias, W1, W2, out, topk_ids, topk_w, expert_cou
                                           _ptr(out), _ptr(topk_ids), _ptr(topk_w), _ptr(expert_counts),
                                           _ptr(expert_offsets), _ptr(perm), _ptr(inv_perm), _ptr(ws), int(ws_bytes),
                                           _stream(stream)))
+
+
+def moe_route_ranked(cfg, X, Wg, gate_bias, topk_ids, topk_w, expert_order, ws=None, ws_bytes=None,
+                     stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check("moe_route_ranked", LIB.moe_route_ranked(ctypes.byref(cfg), _ptr(X), _ptr(Wg), _ptr(gate_bias),
+                                                    _ptr(topk_ids), _ptr(topk_w), _ptr(expert_order), _ptr(ws),
+                                                    int(ws_bytes), _stream(stream)))
+
+
+def moe_dispatch_reroute(cfg, topk_ids, expert_order, X, expert_counts, expert_offsets, perm, inv_perm, Xp, ws,
+                         ws_bytes=None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check("moe_dispatch_reroute", LIB.moe_dispatch_reroute(ctypes.byref(cfg), _ptr(topk_ids), _ptr(expert_order),
+                                                            _ptr(X), _ptr(expert_counts), _ptr(expert_offsets),
+                                                            _ptr(perm), _ptr(inv_perm), _ptr(Xp), _ptr(ws),
+                                                            int(ws_bytes), _stream(stream)))
+
+
+def moe_forward_reroute(cfg, X, Wg, gate_bias, W1, W2, out, topk_ids, topk_w, expert_order, expert_counts,
+                        expert_offsets, perm, inv_perm, ws, ws_bytes=None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check("moe_forward_reroute", LIB.moe_forward_reroute(ctypes.byref(cfg), _ptr(X), _ptr(Wg), _ptr(gate_bias),
+                                                          _ptr(W1), _ptr(W2), _ptr(out), _ptr(topk_ids),
+                                                          _ptr(topk_w), _ptr(expert_order), _ptr(expert_counts),
+                                                          _ptr(expert_offsets), _ptr(perm), _ptr(inv_perm), _ptr(ws),
+                                                          int(ws_bytes), _stream(stream)))

@@ -61,6 +61,10 @@ size_t route_bytes(const moe_config* c) {
 size_t dispatch_bytes(const moe_config* c) {
   return moe::dispatch_scratch_bytes(c->num_tokens, c->num_experts, c->num_experts_per_tok, capacity_mode(c));
 }
+size_t dispatch_reroute_bytes(const moe_config* c) {
+  return moe::dispatch_scratch_bytes(c->num_tokens, c->num_experts, c->num_experts_per_tok, capacity_mode(c),
+                                     /*reroute=*/true);
+}
 size_t h_bytes(const moe_config* c) { return align256(pairs_of(c) * c->intermediate_size * esize(c)); }
 size_t xp_bytes(const moe_config* c) { return align256(pairs_of(c) * c->hidden_size * esize(c)); }
 
@@ -134,6 +138,10 @@ moe_status moe_workspace_size(const moe_config* cfg, int32_t op, size_t* bytes) 
     case MOE_OP_FORWARD:
       *bytes = align256(route_bytes(cfg)) + align256(dispatch_bytes(cfg)) + 2 * xp_bytes(cfg) + h_bytes(cfg);
       return MOE_OK;
+    case MOE_OP_DISPATCH_REROUTE: *bytes = dispatch_reroute_bytes(cfg); return MOE_OK;
+    case MOE_OP_FORWARD_REROUTE:
+      *bytes = align256(route_bytes(cfg)) + align256(dispatch_reroute_bytes(cfg)) + 2 * xp_bytes(cfg) + h_bytes(cfg);
+      return MOE_OK;
     default: return MOE_ERR_INVALID_ARG;
   }
 }
@@ -149,6 +157,20 @@ moe_status moe_route(const moe_config* cfg, const void* X, const void* Wg, const
   return hip_status(moe::launch_router(cfg->dtype, X, Wg, gate_bias, cfg->num_tokens, cfg->hidden_size,
                                        cfg->num_experts, cfg->num_experts_per_tok, topk_ids, topk_w, ws,
                                        as_stream(stream)));
+}
+
+moe_status moe_route_ranked(const moe_config* cfg, const void* X, const void* Wg, const float* gate_bias,
+                            int32_t* topk_ids, float* topk_w, uint8_t* expert_order, void* ws, size_t ws_bytes,
+                            void* stream) {
+  if (moe_status s = check_cfg(cfg); s != MOE_OK) return s;
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if (!X || !Wg || !topk_ids || !topk_w || !expert_order) return MOE_ERR_INVALID_ARG;
+  const size_t need = route_bytes(cfg);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (ws == nullptr) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_router(cfg->dtype, X, Wg, gate_bias, cfg->num_tokens, cfg->hidden_size,
+                                       cfg->num_experts, cfg->num_experts_per_tok, topk_ids, topk_w, ws,
+                                       as_stream(stream), /*select=*/true, 1.f, nullptr, expert_order));
 }
 
 moe_status moe_route_stats(const moe_config* cfg, const void* X, const void* Wg, const float* gate_bias,
@@ -187,6 +209,25 @@ moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_ids, const vo
   return hip_status(moe::launch_dispatch(cfg->dtype, topk_ids, X, cfg->num_tokens, cfg->hidden_size, cfg->num_experts,
                                          cfg->num_experts_per_tok, cfg->expert_capacity, expert_counts,
                                          expert_offsets, perm, inv_perm, Xp, sc, as_stream(stream)));
+}
+
+moe_status moe_dispatch_reroute(const moe_config* cfg, const int32_t* topk_ids, const uint8_t* expert_order,
+                                const void* X, int32_t* expert_counts, int32_t* expert_offsets, int32_t* perm,
+                                int32_t* inv_perm, void* Xp, void* ws, size_t ws_bytes, void* stream) {
+  if (moe_status s = check_cfg(cfg); s != MOE_OK) return s;
+  if (!expert_counts || !expert_offsets) return MOE_ERR_INVALID_ARG;
+  if (cfg->num_tokens > 0 && (!topk_ids || !X || !perm || !inv_perm)) return MOE_ERR_INVALID_ARG;
+  if (cfg->num_tokens > 0 && capacity_mode(cfg) && !expert_order) return MOE_ERR_INVALID_ARG;
+  const size_t need = dispatch_reroute_bytes(cfg);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (need > 0 && ws == nullptr) return MOE_ERR_INVALID_ARG;
+  const moe::DispatchScratch sc = moe::carve_dispatch_scratch(ws, cfg->num_tokens, cfg->num_experts,
+                                                              cfg->num_experts_per_tok, capacity_mode(cfg),
+                                                              /*reroute=*/true);
+  return hip_status(moe::launch_dispatch_reroute(cfg->dtype, topk_ids, expert_order, X, cfg->num_tokens,
+                                                 cfg->hidden_size, cfg->num_experts, cfg->num_experts_per_tok,
+                                                 cfg->expert_capacity, expert_counts, expert_offsets, perm, inv_perm,
+                                                 Xp, sc, as_stream(stream)));
 }
 
 moe_status moe_expert_up(const moe_config* cfg, const void* Xp, const int32_t* expert_offsets, const void* W1,
@@ -304,6 +345,47 @@ moe_status moe_forward(const moe_config* cfg, const void* X, const void* Wg, con
         s != MOE_OK)
       return s;
   }
+  if (cfg->num_tokens == 0) return MOE_OK;
+  if (moe_status s = gather ? moe_expert_up_gather(cfg, X, perm, expert_offsets, W1, H, stream)
+                            : moe_expert_up(cfg, Xp, expert_offsets, W1, H, stream);
+      s != MOE_OK)
+    return s;
+  if (moe_status s = moe_expert_down(cfg, H, expert_offsets, W2, Yp, stream); s != MOE_OK) return s;
+  return moe_combine(cfg, Yp, inv_perm, topk_w, out, stream);
+}
+
+moe_status moe_forward_reroute(const moe_config* cfg, const void* X, const void* Wg, const float* gate_bias,
+                               const void* W1, const void* W2, void* out, int32_t* topk_ids, float* topk_w,
+                               uint8_t* expert_order, int32_t* expert_counts, int32_t* expert_offsets, int32_t* perm,
+                               int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream) {
+  if (moe_status s = check_cfg(cfg); s != MOE_OK) return s;
+  if (!expert_counts || !expert_offsets) return MOE_ERR_INVALID_ARG;
+  if (cfg->num_tokens > 0 &&
+      (!X || !Wg || !W1 || !W2 || !out || !topk_ids || !topk_w || !expert_order || !perm || !inv_perm))
+    return MOE_ERR_INVALID_ARG;
+  size_t need = 0;
+  moe_workspace_size(cfg, MOE_OP_FORWARD_REROUTE, &need);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (ws == nullptr) return MOE_ERR_INVALID_ARG;
+  unsigned char* p = static_cast<unsigned char*>(ws);
+  void* rws = p;
+  p += align256(route_bytes(cfg));
+  void* dws = p;
+  p += align256(dispatch_reroute_bytes(cfg));
+  void* Xp = p;
+  p += xp_bytes(cfg);
+  void* H = p;
+  p += h_bytes(cfg);
+  void* Yp = p;
+  const bool gather = gathers(cfg);
+  if (moe_status s =
+          moe_route_ranked(cfg, X, Wg, gate_bias, topk_ids, topk_w, expert_order, rws, route_bytes(cfg), stream);
+      s != MOE_OK)
+    return s;
+  if (moe_status s = moe_dispatch_reroute(cfg, topk_ids, expert_order, X, expert_counts, expert_offsets, perm,
+                                          inv_perm, gather ? nullptr : Xp, dws, dispatch_reroute_bytes(cfg), stream);
+      s != MOE_OK)
+    return s;
   if (cfg->num_tokens == 0) return MOE_OK;
   if (moe_status s = gather ? moe_expert_up_gather(cfg, X, perm, expert_offsets, W1, H, stream)
                             : moe_expert_up(cfg, Xp, expert_offsets, W1, H, stream);

@@ -158,13 +158,14 @@ __global__ __launch_bounds__(kWave) void dispatch_count_kernel(const int32_t* __
   for (int c = threadIdx.x; c < cols; c += kWave) out[c] = s_hist[c];
 }
 
-enum ScanMode { kScanDropless = 0, kScanCapacity1 = 1, kScanCapacity2 = 2 };
+enum ScanMode { kScanDropless = 0, kScanCapacity1 = 1, kScanCapacity2 = 2, kScanOffsets = 3 };
 
 // One block.  Replaces M[c][col] by its exclusive prefix over chunks c, then
 //   dropless:  counts[e] = total, offsets = exclusive scan of totals;
 //   capacity1: counts[e] = sum over slots, slot_base[s][e] = pairs of e in
 //              slots < s, offsets from min(counts, C);
-//   capacity2: nothing more (offsets were written by capacity1).
+//   capacity2: nothing more (offsets were written by capacity1);
+//   offsets:   offsets = exclusive scan of the column totals (counts kept).
 // Then perm rows >= N get -1.
 __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(int32_t* __restrict__ M, int nrows, int ncols,
                                                                      int mode, int E, int k, int capacity,
@@ -258,6 +259,14 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(int32_t* __
       }
       offsets[E] = acc;
       s_N = acc;
+    } else if (mode == kScanOffsets) {
+      int acc = 0;
+      for (int e = 0; e < E; ++e) {
+        offsets[e] = acc;
+        acc += s_tot[e];
+      }
+      offsets[E] = acc;
+      s_N = acc;
     } else {
       s_N = offsets[E];
     }
@@ -303,6 +312,147 @@ __global__ __launch_bounds__(kWave) void dispatch_keep_kernel(const int32_t* __r
   }
   __syncthreads();
   if (lane < E) chunk_kept[static_cast<int64_t>(blockIdx.x) * E + lane] = s_kept[lane];
+}
+
+// Rerouting of the pairs the capacity cut drops ("Qwen2-MoE代码解析" §3.4:
+// with drop_tokens = False a token over an expert's capacity goes to a
+// next-best expert instead of being discarded).  The cut made by
+// dispatch_keep_kernel stands.  The pairs it drops are taken in the same
+// (slot rank, token index) priority; each takes the first expert past its
+// token's top-k, in the token's preference order, that still has room and
+// that the token does not already use (an earlier slot may have moved
+// there); a pair that finds none stays dropped.  Its weight is unchanged.
+//
+// One block.  For each slot s the tokens go in batches of kRerouteThreads:
+// each thread checks one token's pair (t, s) and, if it was dropped, writes
+// its candidate list (preference positions k..E-1 minus the experts the
+// token's other slots sit on) to LDS; the dropped pairs are compacted in
+// token order.  Wave 0 then places them 64 at a time: every lane picks its
+// first candidate with room as the room stood at the start of the group.
+// That pick is the sequential rule's iff fewer earlier lanes of the group
+// picked the same expert than it had room -- the candidates before it were
+// full at the start, and room only shrinks.  The lanes before the first one
+// that fails commit and the group restarts at that lane; lane 0 never fails,
+// and the failing lane's expert is full after the commit, so each slot's
+// pass needs at most ceil(dropped / 64) + E groups.
+constexpr int kRerouteThreads = 1024;
+
+__global__ __launch_bounds__(kRerouteThreads) void dispatch_reroute_kernel(
+    const int32_t* __restrict__ ids, const uint8_t* __restrict__ order, const int32_t* __restrict__ counts, int T,
+    int E, int k, int capacity, int8_t* __restrict__ keep, int32_t* __restrict__ ids2) {
+  extern __shared__ uint8_t s_cand[];                   // [kRerouteThreads][E]
+  __shared__ uint8_t s_ncand[kRerouteThreads];
+  __shared__ int s_list[kRerouteThreads];
+  __shared__ int s_room[kMaxExperts];
+  __shared__ int s_wave_cnt[kRerouteThreads / kWave];
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
+  const int64_t pairs = static_cast<int64_t>(T) * k;
+  for (int64_t i = tid; i < pairs; i += kRerouteThreads) ids2[i] = ids[i];
+  if (tid < E) s_room[tid] = capacity - min(max(counts[tid], 0), capacity);
+  __threadfence();  // the copy is in L2 before any wave reads it back
+  __syncthreads();
+  for (int s = 0; s < k; ++s) {
+    for (int b0 = 0; b0 < T; b0 += kRerouteThreads) {
+      const int t = b0 + tid;
+      bool dropped = false;
+      if (t < T) {
+        const int64_t pr = static_cast<int64_t>(t) * k + s;
+        const int e0 = ids[pr];
+        dropped = keep[pr] == 0 && e0 >= 0 && e0 < E;
+      }
+      if (dropped) {
+        // The token's other slots: their experts as they stand (slots before
+        // s are final; ids2 is read past the L1, which other waves wrote).
+        uint64_t used = 0;
+        for (int j = 0; j < k; ++j) {
+          const int ej = __hip_atomic_load(&ids2[static_cast<int64_t>(t) * k + j], __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+          if (j != s && ej >= 0 && ej < E) used |= 1ull << ej;
+        }
+        const uint8_t* row = order + static_cast<int64_t>(t) * E;
+        uint8_t* cand = s_cand + tid * E;
+        int nc = 0;
+        for (int q = k; q < E; ++q) {
+          const int e = row[q];
+          if (e < E && !((used >> e) & 1ull)) cand[nc++] = static_cast<uint8_t>(e);
+        }
+        s_ncand[tid] = static_cast<uint8_t>(nc);
+      }
+      const uint64_t bal = __ballot(dropped);
+      if (lane == 0) s_wave_cnt[wave] = __popcll(bal);
+      __syncthreads();
+      int base = 0, m = 0;
+      for (int w = 0; w < kRerouteThreads / kWave; ++w) {
+        const int c = s_wave_cnt[w];
+        base += w < wave ? c : 0;
+        m += c;
+      }
+      if (dropped) s_list[base + __popcll(bal & ((1ull << lane) - 1ull))] = tid;
+      __syncthreads();
+      if (wave == 0) {
+        const uint64_t below = (1ull << lane) - 1ull;
+        for (int c0 = 0; c0 < m;) {
+          const int idx = c0 + lane;
+          const int slot = idx < m ? s_list[idx] : 0;
+          int pick = kNone;
+          if (idx < m) {
+            const int nc = s_ncand[slot];
+            const uint8_t* cand = s_cand + slot * E;
+            for (int j = 0; j < nc; ++j) {
+              const int e = cand[j];
+              if (s_room[e] > 0) {
+                pick = e;
+                break;
+              }
+            }
+          }
+          const Ballots B = ballots_of(pick);
+          const uint64_t same = pick != kNone ? match(B, pick) : 0ull;
+          const int rank = __popcll(same & below);
+          const bool bad = pick != kNone && rank >= s_room[pick];
+          const uint64_t badm = __ballot(bad);
+          const int f = badm != 0ull ? __builtin_ctzll(badm) : kWave;
+          const int nlive = min(f, m - c0);  // >= 1: lane 0 never fails
+          const uint64_t live = nlive >= kWave ? ~0ull : (1ull << nlive) - 1ull;
+          if (lane < nlive && pick != kNone) {
+            const int64_t pr = static_cast<int64_t>(b0 + slot) * k + s;
+            ids2[pr] = pick;
+            keep[pr] = 1;
+          }
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          // The first committing lane of each picked expert takes the room of all of them.
+          if (lane < nlive && pick != kNone && rank == 0) s_room[pick] -= __popcll(same & live);
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          c0 += nlive;
+        }
+        __threadfence();  // this batch's placements are in L2 before the next slot's pass reads them
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Kept pairs per 64-token chunk and expert, under the rerouted assignment.
+__global__ __launch_bounds__(kWave) void dispatch_count_kept_kernel(const int32_t* __restrict__ ids,
+                                                                    const int8_t* __restrict__ keep, int T, int E,
+                                                                    int k, int32_t* __restrict__ chunk_kept) {
+  __shared__ int s_hist[kMaxExperts];
+  const int lane = threadIdx.x;
+  s_hist[lane] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * kDispatchChunk + lane;
+  if (t < T)
+    for (int s = 0; s < k; ++s) {
+      const int64_t pr = static_cast<int64_t>(t) * k + s;
+      const int e = ids[pr];
+      if (keep[pr] != 0 && e >= 0 && e < E) atomicAdd(&s_hist[e], 1);
+    }
+  __syncthreads();
+  if (lane < E) chunk_kept[static_cast<int64_t>(blockIdx.x) * E + lane] = s_hist[lane];
 }
 
 // Rows of the pairs of 16 tokens, then the copy of their hidden states.
@@ -570,18 +720,19 @@ size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
 }  // namespace
 
-size_t dispatch_scratch_bytes(int T, int E, int k, bool capacity) {
+size_t dispatch_scratch_bytes(int T, int E, int k, bool capacity, bool reroute) {
   const size_t nchunks = (static_cast<size_t>(T) + kDispatchChunk - 1) / kDispatchChunk;
   size_t b = align256(nchunks * (capacity ? k * E : E) * sizeof(int32_t));
   if (capacity) {
     b += align256(nchunks * E * sizeof(int32_t));
     b += align256(static_cast<size_t>(k) * E * sizeof(int32_t));
     b += align256(static_cast<size_t>(T) * k);
+    if (reroute) b += align256(static_cast<size_t>(T) * k * sizeof(int32_t));
   }
   return b;
 }
 
-DispatchScratch carve_dispatch_scratch(void* ws, int T, int E, int k, bool capacity) {
+DispatchScratch carve_dispatch_scratch(void* ws, int T, int E, int k, bool capacity, bool reroute) {
   const size_t nchunks = (static_cast<size_t>(T) + kDispatchChunk - 1) / kDispatchChunk;
   unsigned char* p = static_cast<unsigned char*>(ws);
   DispatchScratch s{};
@@ -593,6 +744,8 @@ DispatchScratch carve_dispatch_scratch(void* ws, int T, int E, int k, bool capac
     s.slot_base = reinterpret_cast<int32_t*>(p);
     p += align256(static_cast<size_t>(k) * E * sizeof(int32_t));
     s.keep = reinterpret_cast<int8_t*>(p);
+    p += align256(static_cast<size_t>(T) * k);
+    if (reroute) s.ids2 = reinterpret_cast<int32_t*>(p);
   }
   return s;
 }
@@ -696,6 +849,46 @@ hipError_t launch_dispatch(int dtype, const int32_t* ids, const void* X, int T, 
                                     sc.keep, perm, inv_perm, static_cast<uint16_t*>(Xp), stream);
   return launch_scatter<float>(cap, nblocks, ids, static_cast<const float*>(X), T, d, E, k, row_base, offsets, sc.keep,
                                perm, inv_perm, static_cast<float*>(Xp), stream);
+}
+
+hipError_t launch_dispatch_reroute(int dtype, const int32_t* ids, const uint8_t* order, const void* X, int T, int d,
+                                   int E, int k, int capacity, int32_t* counts, int32_t* offsets, int32_t* perm,
+                                   int32_t* inv_perm, void* Xp, const DispatchScratch& sc, hipStream_t stream) {
+  // Without a capacity nothing overflows: the plain dispatch.  No tokens:
+  // every expert is empty (the plain dispatch's path).
+  if (capacity < 0 || T <= 0)
+    return launch_dispatch(dtype, ids, X, T, d, E, k, capacity, counts, offsets, perm, inv_perm, Xp, sc, stream);
+  if (order == nullptr || sc.ids2 == nullptr) return hipErrorInvalidValue;
+  const int nchunks = (T + kDispatchChunk - 1) / kDispatchChunk;
+  const int total_pairs = T * k;
+  const int cols = k * E;
+  hipLaunchKernelGGL(dispatch_count_kernel, dim3(nchunks), dim3(kWave), cols * sizeof(int), stream, ids, T, E, k, true,
+                     sc.chunk_base);
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, sc.chunk_base, nchunks, cols,
+                     static_cast<int>(kScanCapacity1), E, k, capacity, counts, offsets, sc.slot_base, perm,
+                     total_pairs);
+  hipLaunchKernelGGL(dispatch_keep_kernel, dim3(nchunks), dim3(kWave), 0, stream, ids, T, E, k, capacity,
+                     sc.chunk_base, sc.slot_base, sc.keep, sc.chunk_kept);
+  const size_t cand_lds = static_cast<size_t>(kRerouteThreads) * E;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&dispatch_reroute_kernel),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     static_cast<int>(kRerouteThreads * kMaxExperts));
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(dispatch_reroute_kernel, dim3(1), dim3(kRerouteThreads), cand_lds, stream, ids, order, counts, T,
+                     E, k, capacity, sc.keep, sc.ids2);
+  hipLaunchKernelGGL(dispatch_count_kept_kernel, dim3(nchunks), dim3(kWave), 0, stream, sc.ids2, sc.keep, T, E, k,
+                     sc.chunk_kept);
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, sc.chunk_kept, nchunks, E,
+                     static_cast<int>(kScanOffsets), E, k, capacity, counts, offsets, sc.slot_base, perm,
+                     total_pairs);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  const int nblocks = (T + kScatterTok - 1) / kScatterTok;
+  if (dtype == kDtypeBF16)
+    return launch_scatter<uint16_t>(true, nblocks, sc.ids2, static_cast<const uint16_t*>(X), T, d, E, k,
+                                    sc.chunk_kept, offsets, sc.keep, perm, inv_perm, static_cast<uint16_t*>(Xp),
+                                    stream);
+  return launch_scatter<float>(true, nblocks, sc.ids2, static_cast<const float*>(X), T, d, E, k, sc.chunk_kept,
+                               offsets, sc.keep, perm, inv_perm, static_cast<float*>(Xp), stream);
 }
 
 }  // namespace moe

@@ -20,10 +20,11 @@ struct DispatchScratch {
   int32_t* chunk_kept;   // [nchunks][E]:  kept pairs per chunk, then prefix (capacity only)
   int32_t* slot_base;    // [k][E]: pairs of expert e in slots < s (capacity only)
   int8_t* keep;          // [T*k]: keep flag per pair (capacity only)
+  int32_t* ids2;         // [T*k]: expert of each pair after rerouting (rerouting only)
 };
 
-size_t dispatch_scratch_bytes(int T, int E, int k, bool capacity);
-DispatchScratch carve_dispatch_scratch(void* ws, int T, int E, int k, bool capacity);
+size_t dispatch_scratch_bytes(int T, int E, int k, bool capacity, bool reroute = false);
+DispatchScratch carve_dispatch_scratch(void* ws, int T, int E, int k, bool capacity, bool reroute = false);
 
 // Router scratch: the transposed gate and, when T is small, the partial
 // logits of the K splits.
@@ -33,9 +34,10 @@ size_t router_scratch_bytes(int T, int d, int E, int dtype);
 // inv_tau: 1 / router temperature (weights exp((l_s - l_0) * inv_tau) / sum);
 // prob_sum (may be null): [ceil(T/16)][2E] per-16-token-tile sums of the full
 // router probabilities and selection counts, for launch_router_stats.
+// order (may be null): [T][E] bytes, every token's experts in preference order.
 hipError_t launch_router(int dtype, const void* X, const void* Wg, const float* bias, int T, int d, int E, int k,
                          int32_t* ids, float* w, void* scratch, hipStream_t stream, bool select = true,
-                         float inv_tau = 1.f, float* prob_sum = nullptr);
+                         float inv_tau = 1.f, float* prob_sum = nullptr, uint8_t* order = nullptr);
 
 // The load-balancing statistics from launch_router's prob_sum (at the start
 // of a router_stats_scratch_bytes(T, E) scratch, whose rest holds the block
@@ -56,6 +58,14 @@ RouterSplit router_split(int T, int d, int E, int dtype, void* scratch);
 hipError_t launch_dispatch(int dtype, const int32_t* ids, const void* X, int T, int d, int E, int k, int capacity,
                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* Xp,
                            const DispatchScratch& scratch, hipStream_t stream);
+
+// The capacity dispatch with the pairs over capacity rerouted to their
+// token's next-best expert with room (order: [T][E] preference order from
+// launch_router); scratch carved with reroute = true.  capacity < 0: the
+// plain dispatch.
+hipError_t launch_dispatch_reroute(int dtype, const int32_t* ids, const uint8_t* order, const void* X, int T, int d,
+                                   int E, int k, int capacity, int32_t* counts, int32_t* offsets, int32_t* perm,
+                                   int32_t* inv_perm, void* Xp, const DispatchScratch& scratch, hipStream_t stream);
 
 // Small batches (the single-block dispatch: T <= 256, k <= 8) with a K-split
 // router: one block sums the partial logits, selects the top-k (writing ids

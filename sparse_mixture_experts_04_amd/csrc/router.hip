@@ -37,6 +37,7 @@ constexpr int kRouterThreads = 256;               // 4 waves
 struct RouteExtra {
   float inv_tau;
   float* prob_sum;
+  uint8_t* order;  // [T][E] preference order of every token, or null
 };
 constexpr int kRouterTok = 32;                    // tokens per block: 2 row tiles of 16
 constexpr int kRowTiles = kRouterTok / 16;
@@ -115,7 +116,7 @@ template <typename T, int NT, bool kDirect>
 __global__ __launch_bounds__(kRouterThreads) void router_kernel(
     const T* __restrict__ X, const T* __restrict__ WgT, const T* __restrict__ Wg, const float* __restrict__ bias,
     int T_tokens, int d, int E, int k, int split_len, float* __restrict__ partial, int32_t* __restrict__ topk_ids,
-    float* __restrict__ topk_w, float inv_tau, float* __restrict__ prob_sum) {
+    float* __restrict__ topk_w, float inv_tau, float* __restrict__ prob_sum, uint8_t* __restrict__ order) {
   constexpr int kStepElems = kChunkBytes / sizeof(T);  // K per k-step (32 bf16 / 16 fp32)
   __shared__ f32x4_t red[4][kRowTiles][NT][kWave];
   __shared__ float sel_val[2][16 * kMaxExperts];
@@ -216,7 +217,8 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(
     }
     return;
   }
-  topk_tile<NT>(sum, bias, E, k, rtok0, T_tokens, sel_val[r], sel_id[r], topk_ids, topk_w, inv_tau, prob_sum);
+  topk_tile<NT>(sum, bias, E, k, rtok0, T_tokens, sel_val[r], sel_id[r], topk_ids, topk_w, inv_tau, prob_sum,
+                order);
 }
 
 // bf16 router for many tokens when the whole transposed gate fits in LDS
@@ -250,7 +252,7 @@ template <int NT, int RT>
 __global__ __launch_bounds__(kRouterThreads, 1) void router_lds_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wg, const float* __restrict__ bias, int T_tokens,
     int d, int E, int k, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, float inv_tau,
-    float* __restrict__ prob_sum) {
+    float* __restrict__ prob_sum, uint8_t* __restrict__ order) {
   constexpr int WT = RT >= 4 ? 4 : RT;  // token groups of waves
   constexpr int WK = 4 / WT;            // K splits per token group
   constexpr int RW = RT / WT;           // row tiles per wave
@@ -455,7 +457,7 @@ __global__ __launch_bounds__(kRouterThreads, 1) void router_lds_kernel(
       static_for<RW>([&](auto r_c) {
         constexpr int r = decltype(r_c)::value;
         topk_tile<NT>(acc[r], bias, E, k, cur_base + (wt * RW + r) * 16, T_tokens, sel_val, sel_id, topk_ids,
-                      topk_w, inv_tau, prob_sum);
+                      topk_w, inv_tau, prob_sum, order);
       });
     }
     if (!more) break;
@@ -471,12 +473,13 @@ __global__ __launch_bounds__(1024) void router_topk_kernel(const float* __restri
                                                            const float* __restrict__ bias, int T_tokens, int E, int k,
                                                            int32_t* __restrict__ topk_ids,
                                                            float* __restrict__ topk_w, float inv_tau,
-                                                           float* __restrict__ prob_sum) {
+                                                           float* __restrict__ prob_sum,
+                                                           uint8_t* __restrict__ order) {
   __shared__ float logit[16][kMaxExperts];
   __shared__ float sel_val[16 * kMaxExperts];
   __shared__ int sel_id[16 * kMaxExperts];
   topk_from_partials<NT>(partial, nsplit, bias, T_tokens, E, k, blockIdx.x * 16, logit, sel_val, sel_id, topk_ids,
-                         topk_w, inv_tau, prob_sum);
+                         topk_w, inv_tau, prob_sum, order);
 }
 
 // The load-balancing statistics from the per-tile sums of topk_tile
@@ -578,7 +581,7 @@ hipError_t launch_lds_rt(const uint16_t* X, const uint16_t* Wg, const float* bia
                           hipFuncAttributeMaxDynamicSharedMemorySize, kLdsRouterMaxGate * 2 + kLdsRouterScratch);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((router_lds_kernel<NT, RT>), dim3(grid), dim3(kRouterThreads), lds, stream, X, Wg, bias,
-                     T_tokens, d, E, k, ids, w, x.inv_tau, x.prob_sum);
+                     T_tokens, d, E, k, ids, w, x.inv_tau, x.prob_sum, x.order);
   return hipGetLastError();
 }
 
@@ -614,15 +617,15 @@ hipError_t launch_nt(const T* X, const T* Wg, const float* bias, int T_tokens, i
   if (nsplit > 1) {
     // few token blocks: gather from W_g directly, no transpose launch
     hipLaunchKernelGGL((router_kernel<T, NT, true>), grid, dim3(kRouterThreads), 0, stream, X, WgT, Wg, bias, T_tokens,
-                       d, E, k, split_len, partial, ids, w, x.inv_tau, x.prob_sum);
+                       d, E, k, split_len, partial, ids, w, x.inv_tau, x.prob_sum, x.order);
   } else {
     hipLaunchKernelGGL((gate_transpose_kernel<T, NT>), dim3(d / 32), dim3(256), 0, stream, Wg, d, E, WgT);
     hipLaunchKernelGGL((router_kernel<T, NT, false>), grid, dim3(kRouterThreads), 0, stream, X, WgT, Wg, bias,
-                       T_tokens, d, E, k, split_len, nullptr, ids, w, x.inv_tau, x.prob_sum);
+                       T_tokens, d, E, k, split_len, nullptr, ids, w, x.inv_tau, x.prob_sum, x.order);
   }
   if (nsplit > 1 && select)
     hipLaunchKernelGGL((router_topk_kernel<NT>), dim3((T_tokens + 15) / 16), dim3(1024), 0, stream, partial, nsplit,
-                       bias, T_tokens, E, k, ids, w, x.inv_tau, x.prob_sum);
+                       bias, T_tokens, E, k, ids, w, x.inv_tau, x.prob_sum, x.order);
   return hipGetLastError();
 }
 
@@ -662,10 +665,10 @@ RouterSplit router_split(int T_tokens, int d, int E, int dtype, void* scratch) {
 
 hipError_t launch_router(int dtype, const void* X, const void* Wg, const float* bias, int T_tokens, int d, int E,
                          int k, int32_t* ids, float* w, void* scratch, hipStream_t stream, bool select,
-                         float inv_tau, float* prob_sum) {
+                         float inv_tau, float* prob_sum, uint8_t* order) {
   if (T_tokens <= 0) return hipSuccess;
   unsigned char* sc = static_cast<unsigned char*>(scratch);
-  const RouteExtra x{inv_tau, prob_sum};
+  const RouteExtra x{inv_tau, prob_sum, order};
   if (dtype == kDtypeBF16)
     return launch_t(static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(Wg), bias, T_tokens, d, E, k, ids,
                     w, sc, select, x, stream);

@@ -79,11 +79,15 @@ __device__ __forceinline__ void argmax16(float& bv, int& bi) {
 // probability softmax(logits * inv_tau), then the number of the tile's
 // tokens that select the expert -- the per-tile parts of the load-balancing
 // statistics ("Qwen2-MoE代码解析" §3.3).
+// order (may be null): [T][E] bytes; row t receives all E experts of token t
+// in preference order (the same arg-max rounds continued past k), the list
+// the over-capacity rerouting walks ("Qwen2-MoE代码解析" §3.4).
 template <int NT>
 __device__ __forceinline__ void topk_tile(f32x4_t (&acc)[NT], const float* __restrict__ bias, int E, int k,
                                           int tok0, int T_tokens, float* sel_val, int* sel_id,
                                           int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
-                                          float inv_tau = 1.f, float* __restrict__ prob_sum = nullptr) {
+                                          float inv_tau = 1.f, float* __restrict__ prob_sum = nullptr,
+                                          uint8_t* __restrict__ order = nullptr) {
   const int lane = threadIdx.x % kWave;
   const int n = lane & 15;
   const int grp = lane >> 4;
@@ -120,7 +124,8 @@ __device__ __forceinline__ void topk_tile(f32x4_t (&acc)[NT], const float* __res
       for (int t = 0; t < NT; ++t) col[t] += live ? z[t] / den : 0.f;
     }
   }
-  for (int s = 0; s < k; ++s) {
+  const int rounds = order != nullptr ? E : k;
+  for (int s = 0; s < rounds; ++s) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float bv = acc[0][i];
@@ -129,18 +134,21 @@ __device__ __forceinline__ void topk_tile(f32x4_t (&acc)[NT], const float* __res
       for (int t = 1; t < NT; ++t)
         if (better(acc[t][i], t * 16 + n, bv, bi)) { bv = acc[t][i]; bi = t * 16 + n; }
       argmax16(bv, bi);
+      const bool live = tok0 + grp * 4 + i < T_tokens;
       if ((bi & 15) == n) {
-        const bool live = tok0 + grp * 4 + i < T_tokens;
 #pragma unroll
         for (int t = 0; t < NT; ++t)
           if (t == (bi >> 4)) {
             acc[t][i] = -INFINITY;
-            if (live) cnt[t] += 1.f;
+            if (live && s < k) cnt[t] += 1.f;
           }
       }
       if (n == 0) {
-        sel_val[(grp * 4 + i) * kMaxExperts + s] = bv;
-        sel_id[(grp * 4 + i) * kMaxExperts + s] = bi;
+        if (s < k) {
+          sel_val[(grp * 4 + i) * kMaxExperts + s] = bv;
+          sel_id[(grp * 4 + i) * kMaxExperts + s] = bi;
+        }
+        if (order != nullptr && live) order[static_cast<int64_t>(tok0 + grp * 4 + i) * E + s] = static_cast<uint8_t>(bi);
       }
     }
   }
@@ -188,7 +196,8 @@ __device__ __forceinline__ void topk_from_partials(const float* __restrict__ par
                                                    int tok0, float (*logit)[kMaxExperts], float* sel_val,
                                                    int* sel_id, int32_t* __restrict__ topk_ids,
                                                    float* __restrict__ topk_w, float inv_tau = 1.f,
-                                                   float* __restrict__ prob_sum = nullptr) {
+                                                   float* __restrict__ prob_sum = nullptr,
+                                                   uint8_t* __restrict__ order = nullptr) {
   {
     const int r = threadIdx.x / kMaxExperts;
     const int e = threadIdx.x % kMaxExperts;
@@ -219,7 +228,7 @@ __device__ __forceinline__ void topk_from_partials(const float* __restrict__ par
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[t][i] = (e < E) ? logit[grp * 4 + i][e] : 0.f;
     }
-    topk_tile<NT>(acc, bias, E, k, tok0, T_tokens, sel_val, sel_id, topk_ids, topk_w, inv_tau, prob_sum);
+    topk_tile<NT>(acc, bias, E, k, tok0, T_tokens, sel_val, sel_id, topk_ids, topk_w, inv_tau, prob_sum, order);
   }
 }
 

@@ -28,11 +28,13 @@ class ForwardBuffers:
     perm: torch.Tensor            # [T*k] int32
     inv_perm: torch.Tensor        # [T*k] int32
     ws: torch.Tensor              # uint8 workspace
+    expert_order: Optional[torch.Tensor] = None  # [T, E] uint8 (rerouting forward only)
 
     @staticmethod
-    def allocate(cfg: _lib.MoeConfig, device="cuda") -> "ForwardBuffers":
+    def allocate(cfg: _lib.MoeConfig, device="cuda", reroute: bool = False) -> "ForwardBuffers":
         T, d, E, k = cfg.num_tokens, cfg.hidden_size, cfg.num_experts, cfg.num_experts_per_tok
         i32 = dict(dtype=torch.int32, device=device)
+        op = _lib.MOE_OP_FORWARD_REROUTE if reroute else _lib.MOE_OP_FORWARD
         return ForwardBuffers(
             out=torch.empty((T, d), dtype=torch_dtype(cfg), device=device),
             topk_ids=torch.empty((T, k), **i32),
@@ -41,15 +43,18 @@ class ForwardBuffers:
             expert_offsets=torch.empty(E + 1, **i32),
             perm=torch.empty(T * k, **i32),
             inv_perm=torch.empty(T * k, **i32),
-            ws=torch.empty(max(1, _lib.moe_workspace_size(cfg, _lib.MOE_OP_FORWARD)), dtype=torch.uint8,
-                           device=device),
+            ws=torch.empty(max(1, _lib.moe_workspace_size(cfg, op)), dtype=torch.uint8, device=device),
+            expert_order=torch.empty((T, E), dtype=torch.uint8, device=device) if reroute else None,
         )
+
+    def _dispatch_op(self) -> int:
+        return _lib.MOE_OP_DISPATCH_REROUTE if self.expert_order is not None else _lib.MOE_OP_DISPATCH
 
     def scratch_view(self, cfg: _lib.MoeConfig, name: str) -> torch.Tensor:
         """The router ("route") or dispatcher ("dispatch") scratch inside the forward workspace."""
         a = lambda b: (b + 255) // 256 * 256  # noqa: E731
         r = _lib.moe_workspace_size(cfg, _lib.MOE_OP_ROUTE)
-        d = _lib.moe_workspace_size(cfg, _lib.MOE_OP_DISPATCH)
+        d = _lib.moe_workspace_size(cfg, self._dispatch_op())
         if name == "route":
             return self.ws[:max(r, 1)]
         return self.ws[a(r):a(r) + max(d, 1)]
@@ -60,7 +65,7 @@ class ForwardBuffers:
         T, d, F, k = cfg.num_tokens, cfg.hidden_size, cfg.intermediate_size, cfg.num_experts_per_tok
         es = 2 if cfg.dtype == _lib.MOE_BF16 else 4
         a = lambda b: (b + 255) // 256 * 256  # noqa: E731
-        disp = a(_lib.moe_workspace_size(cfg, _lib.MOE_OP_ROUTE)) + a(_lib.moe_workspace_size(cfg, _lib.MOE_OP_DISPATCH))
+        disp = a(_lib.moe_workspace_size(cfg, _lib.MOE_OP_ROUTE)) + a(_lib.moe_workspace_size(cfg, self._dispatch_op()))
         xp = a(T * k * d * es)
         h = a(T * k * F * es)
         start, cols = {"Xp": (disp, d), "H": (disp + xp, F), "Yp": (disp + xp + h, d)}[name]
@@ -69,16 +74,24 @@ class ForwardBuffers:
 
 
 class MoELayer:
-    """Weights of one layer resident on the GPU, plus its forward buffers."""
+    """Weights of one layer resident on the GPU, plus its forward buffers.
+    ``reroute``: over-capacity pairs move to their token's next-best expert
+    with room instead of being dropped (``moe_forward_reroute``)."""
 
     def __init__(self, cfg: _lib.MoeConfig, Wg: torch.Tensor, W1: torch.Tensor, W2: torch.Tensor,
-                 gate_bias: Optional[torch.Tensor] = None, device="cuda"):
+                 gate_bias: Optional[torch.Tensor] = None, device="cuda", reroute: bool = False):
         self.cfg = cfg
+        self.reroute = reroute
         self.Wg, self.W1, self.W2, self.gate_bias = Wg, W1, W2, gate_bias
-        self.buf = ForwardBuffers.allocate(cfg, device)
+        self.buf = ForwardBuffers.allocate(cfg, device, reroute)
 
     def forward(self, X: torch.Tensor, stream=None) -> torch.Tensor:
         b = self.buf
-        _lib.moe_forward(self.cfg, X, self.Wg, self.gate_bias, self.W1, self.W2, b.out, b.topk_ids, b.topk_w,
-                         b.expert_counts, b.expert_offsets, b.perm, b.inv_perm, b.ws, stream=stream)
+        if self.reroute:
+            _lib.moe_forward_reroute(self.cfg, X, self.Wg, self.gate_bias, self.W1, self.W2, b.out, b.topk_ids,
+                                     b.topk_w, b.expert_order, b.expert_counts, b.expert_offsets, b.perm, b.inv_perm,
+                                     b.ws, stream=stream)
+        else:
+            _lib.moe_forward(self.cfg, X, self.Wg, self.gate_bias, self.W1, self.W2, b.out, b.topk_ids, b.topk_w,
+                             b.expert_counts, b.expert_offsets, b.perm, b.inv_perm, b.ws, stream=stream)
         return b.out

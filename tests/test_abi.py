@@ -211,3 +211,33 @@ def test_capacity_from_factor_matches_oracle():
         with pytest.raises(moe.MoeError) as ei:
             moe.moe_capacity_from_factor(*bad)
         assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+
+
+def test_reroute_entry_points_reject_before_launch():
+    cfg = moe.config(300, 128, 256, 8, 2, 40, "bf16")
+    need_d = moe.moe_workspace_size(cfg, moe.MOE_OP_DISPATCH_REROUTE)
+    # the rerouted assignment (T*k int32) on top of the capacity dispatch's scratch
+    assert need_d >= moe.moe_workspace_size(cfg, moe.MOE_OP_DISPATCH) + 300 * 2 * 4
+    need_f = moe.moe_workspace_size(cfg, moe.MOE_OP_FORWARD_REROUTE)
+    assert need_f >= moe.moe_workspace_size(cfg, moe.MOE_OP_FORWARD) + 300 * 2 * 4
+    calls = [
+        lambda: moe.moe_route_ranked(cfg, 1, 1, None, 1, 1, None, 1, 1 << 30, stream=0),
+        lambda: moe.moe_route_ranked(cfg, None, 1, None, 1, 1, 1, 1, 1 << 30, stream=0),
+        lambda: moe.moe_dispatch_reroute(cfg, 1, None, 1, 1, 1, 1, 1, 1, 1, need_d, stream=0),
+        lambda: moe.moe_dispatch_reroute(cfg, None, 1, 1, 1, 1, 1, 1, 1, 1, need_d, stream=0),
+        lambda: moe.moe_dispatch_reroute(cfg, 1, 1, 1, None, 1, 1, 1, 1, 1, need_d, stream=0),
+        lambda: moe.moe_forward_reroute(cfg, 1, 1, None, 1, 1, 1, 1, 1, None, 1, 1, 1, 1, 1, need_f, stream=0),
+        lambda: moe.moe_forward_reroute(cfg, 1, 1, None, 1, 1, None, 1, 1, 1, 1, 1, 1, 1, 1, need_f, stream=0),
+    ]
+    for c in calls:
+        with pytest.raises(moe.MoeError) as ei:
+            c()
+        assert ei.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_dispatch_reroute(cfg, 1, 1, 1, 1, 1, 1, 1, 1, 1, need_d - 1, stream=0)
+    assert ei.value.status == moe.MOE_ERR_WORKSPACE_TOO_SMALL
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_forward_reroute(cfg, 1, 1, None, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, need_f - 1, stream=0)
+    assert ei.value.status == moe.MOE_ERR_WORKSPACE_TOO_SMALL
+    # T = 0: nothing to do
+    moe.moe_route_ranked(moe.config(0, 128, 256, 8, 2), None, None, None, None, None, None, stream=0)

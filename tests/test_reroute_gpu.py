@@ -1,0 +1,232 @@
+"""Parity of the over-capacity rerouting (drop_tokens = False of the
+Qwen2-MoE code analysis page, section 3.4) on the GPU, through the C ABI,
+with the CPU oracle: the router's full preference order, the rerouting
+dispatch fed with the oracle's own ids and orders (bit-exact), the rerouting
+dispatch on random preference lists with many conflicts, and the whole
+rerouted layer, up to the capacity-limited workload's full size."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_mixture_experts_04_amd as moe
+import workloads
+from gpu_util import (TIE_MARGIN, check_routing, dev_to_f64, rel_tol, row_rel_err, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+# (name, T, d, E, k, F, dtype, capacity, bias_scale)
+CASES = [
+    ("cap_k4", 1000, 512, 32, 4, 512, "bf16", 128, 0.5),
+    ("cap_tight_f32", 129, 64, 4, 2, 64, "f32", 20, 1.0),
+    ("skinny_cap", 60, 128, 8, 3, 128, "bf16", 9, 0.5),
+    ("splitk_cap_k3", 48, 1024, 16, 3, 256, "bf16", 7, 0.5),
+    ("cap_zero", 70, 128, 8, 2, 128, "bf16", 0, 0.0),
+    ("batches_e8", 5000, 128, 8, 2, 128, "bf16", 1000, 1.5),   # several 1024-token batches per slot
+    ("e64_k2", 3000, 128, 64, 2, 128, "bf16", 60, 1.0),       # 64 experts: the full candidate rows
+    ("skew_left_dropped", 2100, 128, 16, 2, 128, "bf16", 150, 3.0),
+    ("k1_exact_fit", 2048, 128, 16, 1, 128, "bf16", 128, 2.0),
+    ("dropless", 300, 128, 8, 2, 128, "bf16", -1, 0.5),
+]
+IDS = [c[0] for c in CASES]
+
+
+def make(case, seed=0):
+    name, T, d, E, k, F, dt, cap, bs = case
+    inp = workloads.random_case(seed + 31 * len(name), T, d, E, k, F, dt, cap, bs, w_scale=0.05)
+    return inp, moe.config(T, d, F, E, k, cap, dt)
+
+
+def _route_ranked(cfg, X, Wg, bias, T, E, k):
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    tw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    order = torch.full((T, E), 255, dtype=torch.uint8, device="cuda")
+    rws = torch.empty(max(1, moe.moe_workspace_size(cfg, moe.MOE_OP_ROUTE)), dtype=torch.uint8, device="cuda")
+    moe.moe_route_ranked(cfg, X, Wg, bias, ids, tw, order, rws)
+    return ids, tw, order
+
+
+def _dispatch_reroute(cfg, ids_np, order_np, X, T, E, k, d):
+    Tk = T * k
+    ids = torch.from_numpy(np.ascontiguousarray(ids_np, dtype=np.int32)).cuda()
+    order = torch.from_numpy(np.ascontiguousarray(order_np, dtype=np.uint8)).cuda()
+    counts = torch.full((E,), -7, dtype=torch.int32, device="cuda")
+    offsets = torch.full((E + 1,), -7, dtype=torch.int32, device="cuda")
+    perm = torch.full((Tk,), -7, dtype=torch.int32, device="cuda")
+    inv = torch.full((Tk,), -7, dtype=torch.int32, device="cuda")
+    Xp = torch.zeros((Tk, d), dtype=X.dtype, device="cuda")
+    ws = torch.empty(max(1, moe.moe_workspace_size(cfg, moe.MOE_OP_DISPATCH_REROUTE)), dtype=torch.uint8,
+                     device="cuda")
+    moe.moe_dispatch_reroute(cfg, ids, order, X, counts, offsets, perm, inv, Xp, ws)
+    torch.cuda.synchronize()
+    return counts.cpu().numpy(), offsets.cpu().numpy(), perm.cpu().numpy(), inv.cpu().numpy(), Xp
+
+
+def _check_exact(got, disp, Tk):
+    counts, offsets, perm, inv = got[:4]
+    assert np.array_equal(counts, disp.counts), "expert_counts differ"
+    assert np.array_equal(offsets, disp.offsets), "expert_offsets differ"
+    N = int(disp.offsets[-1])
+    assert np.array_equal(perm[:N], disp.perm), "perm differs"
+    assert (perm[N:Tk] == -1).all(), "perm rows past N must be -1"
+    assert np.array_equal(inv, disp.inv_perm), "inv_perm differs"
+
+
+@pytest.mark.parametrize("case", CASES, ids=IDS)
+def test_route_ranked(case):
+    inp, cfg = make(case)
+    w = inp.workload
+    X, Wg, bias = to_dev(inp.X, w.dtype), to_dev(inp.Wg, w.dtype), to_dev(inp.bias, "f32")
+    ids, tw, order = _route_ranked(cfg, X, Wg, bias, w.T, w.E, w.k)
+    # bitwise the same ids and weights as moe_route
+    ids0 = torch.empty_like(ids)
+    tw0 = torch.empty_like(tw)
+    rws = torch.empty(max(1, moe.moe_workspace_size(cfg, moe.MOE_OP_ROUTE)), dtype=torch.uint8, device="cuda")
+    moe.moe_route(cfg, X, Wg, bias, ids0, tw0, rws)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids0) and torch.equal(tw, tw0)
+    o = order.cpu().numpy().astype(np.int64)
+    assert (np.sort(o, axis=1) == np.arange(w.E)).all(), "each row must be a permutation of the experts"
+    assert (o[:, :w.k] == ids.cpu().numpy()).all()
+    r = oracle.route(oracle.as_f64(inp.X, w.dtype), oracle.as_f64(inp.Wg, w.dtype), inp.bias, w.k)
+    check_routing(ids.cpu().numpy(), tw.cpu().numpy(), r)
+    ref, margin = oracle.expert_ranking(r.probs)
+    diff = (o != ref).any(axis=1)
+    bad = diff & (margin >= TIE_MARGIN)
+    assert not bad.any(), f"order differs on {int(bad.sum())} tokens without a near-tie"
+
+
+@pytest.mark.parametrize("case", CASES, ids=IDS)
+def test_dispatch_reroute(case):
+    inp, cfg = make(case)
+    w = inp.workload
+    r = oracle.route(oracle.as_f64(inp.X, w.dtype), oracle.as_f64(inp.Wg, w.dtype), inp.bias, w.k)
+    order, _ = oracle.expert_ranking(r.probs)
+    disp = oracle.dispatch(r.ids, w.E, inp.expert_capacity, order if inp.expert_capacity >= 0 else None)
+    X = to_dev(inp.X, w.dtype)
+    got = _dispatch_reroute(cfg, r.ids, order, X, w.T, w.E, w.k, w.d)
+    _check_exact(got, disp, w.T * w.k)
+    N = int(disp.offsets[-1])
+    if N:
+        src = torch.from_numpy((disp.perm // w.k).astype(np.int64)).cuda()
+        assert torch.equal(got[4][:N], X[src]), "gathered rows differ"
+    if inp.expert_capacity > 0:
+        plain = oracle.dispatch(r.ids, w.E, inp.expert_capacity)
+        print(case[0], "kept", int(plain.keep.sum()), "->", int(disp.keep.sum()), "of", w.T * w.k)
+
+
+@pytest.mark.parametrize("T,E,k,cap,seed", [(4000, 16, 4, 1000, 0), (3000, 16, 2, 300, 1), (2500, 64, 3, 90, 2),
+                                            (700, 5, 2, 200, 3), (9000, 32, 2, 400, 4), (256, 8, 8, 50, 5)],
+                         ids=["exact_fit_k4", "e16_k2", "e64_k3", "e5", "t9000", "k_eq_e"])
+def test_dispatch_reroute_random_orders(T, E, k, cap, seed):
+    """Arbitrary preference lists (random permutations, skewed towards low
+    ids so experts fill and conflicts arise) against the oracle's rule."""
+    rng = np.random.default_rng(seed)
+    keys = rng.random((T, E)) + 0.6 * np.linspace(0, 1, E)[None, :] * rng.random((T, 1))
+    order = np.argsort(keys, axis=1, kind="stable")
+    ids = order[:, :k]
+    cfg = moe.config(T, 64, 64, E, k, cap, "bf16")
+    X = torch.randn((T, 64), device="cuda").to(torch.bfloat16)
+    disp = oracle.dispatch(ids, E, cap, order)
+    got = _dispatch_reroute(cfg, ids, order, X, T, E, k, 64)
+    _check_exact(got, disp, T * k)
+    plain = oracle.dispatch(ids, E, cap)
+    if E > k and not plain.keep.all():
+        assert disp.keep.sum() > plain.keep.sum()
+
+
+def _forward(inp, cfg, X_np=None):
+    w = inp.workload
+    X_np = inp.X if X_np is None else X_np
+    layer = moe.MoELayer(cfg, to_dev(inp.Wg, w.dtype), to_dev(inp.W1, w.dtype), to_dev(inp.W2, w.dtype),
+                         to_dev(inp.bias, "f32"), reroute=True)
+    out = layer.forward(to_dev(X_np, w.dtype))
+    torch.cuda.synchronize()
+    return layer, out
+
+
+@pytest.mark.parametrize("case", CASES, ids=IDS)
+def test_forward_reroute(case):
+    inp, cfg = make(case)
+    w = inp.workload
+    layer, out = _forward(inp, cfg)
+    b = layer.buf
+    out_ref, r, disp = oracle.moe_forward(inp.X, inp.Wg, inp.bias, inp.W1, inp.W2, w.k, inp.expert_capacity,
+                                          w.dtype, reroute=inp.expert_capacity >= 0)
+    ids_g = b.topk_ids.cpu().numpy()
+    diff = check_routing(ids_g, b.topk_w.cpu().numpy(), r)
+    order_g = b.expert_order.cpu().numpy().astype(np.int64)
+    got = (b.expert_counts.cpu().numpy(), b.expert_offsets.cpu().numpy(), b.perm.cpu().numpy(),
+           b.inv_perm.cpu().numpy())
+    # the dispatch is the rule applied to the GPU's own ids and orders, exactly
+    own = oracle.dispatch(ids_g.astype(np.int64), w.E, inp.expert_capacity,
+                          order_g if inp.expert_capacity >= 0 else None)
+    _check_exact(got, own, w.T * w.k)
+    ref_order, _ = oracle.expert_ranking(r.probs)
+    if not diff.any() and (order_g == ref_order).all():
+        _check_exact(got, disp, w.T * w.k)
+        toks = np.arange(w.T)
+    else:
+        # near-ties: compare the tokens whose pairs ended where the oracle's did
+        same = ((own.assigned == disp.assigned) | ~disp.keep).all(axis=1) & (own.keep == disp.keep).all(axis=1)
+        toks = np.nonzero(same & ~diff)[0]
+        assert len(toks) >= 0.9 * w.T
+    err = row_rel_err(dev_to_f64(out)[toks], out_ref[toks])
+    assert err.max() <= rel_tol(w.dtype), f"layer rel err {err.max():.3g}"
+    first = out.clone()
+    layer.forward(to_dev(inp.X, w.dtype))
+    torch.cuda.synchronize()
+    assert torch.equal(first, layer.buf.out)
+
+
+def test_forward_reroute_dropless_equals_forward():
+    """Without a capacity nothing overflows: the rerouting forward is the plain forward, bit for bit."""
+    inp, cfg = make(CASES[-1])
+    w = inp.workload
+    layer, out = _forward(inp, cfg)
+    plain = moe.MoELayer(cfg, to_dev(inp.Wg, w.dtype), to_dev(inp.W1, w.dtype), to_dev(inp.W2, w.dtype),
+                         to_dev(inp.bias, "f32"))
+    out0 = plain.forward(to_dev(inp.X, w.dtype))
+    torch.cuda.synchronize()
+    assert torch.equal(out, out0)
+    assert torch.equal(layer.buf.perm, plain.buf.perm) and torch.equal(layer.buf.inv_perm, plain.buf.inv_perm)
+
+
+def test_capacity_workload_rerouted_full_size():
+    """The capacity-limited workload (T = 32768, d = 2048, E = 32, k = 4,
+    C = 4096) with rerouting: E * C = T * k, so room exists for every pair.
+    The dispatch is checked exactly as the rule applied to the GPU's own ids
+    and orders; layer outputs on a sample of tokens."""
+    inp = workloads.generate("capacity")
+    w = inp.workload
+    cfg = moe.config(w.T, w.d, w.F, w.E, w.k, inp.expert_capacity, w.dtype)
+    layer, out = _forward(inp, cfg)
+    b = layer.buf
+    ids_g = b.topk_ids.cpu().numpy().astype(np.int64)
+    order_g = b.expert_order.cpu().numpy().astype(np.int64)
+    r = oracle.route(oracle.as_f64(inp.X, w.dtype), oracle.as_f64(inp.Wg, w.dtype), inp.bias, w.k)
+    diff = check_routing(ids_g, b.topk_w.cpu().numpy(), r)
+    own = oracle.dispatch(ids_g, w.E, inp.expert_capacity, order_g)
+    got = (b.expert_counts.cpu().numpy(), b.expert_offsets.cpu().numpy(), b.perm.cpu().numpy(),
+           b.inv_perm.cpu().numpy())
+    _check_exact(got, own, w.T * w.k)
+    plain = oracle.dispatch(ids_g, w.E, inp.expert_capacity)
+    moved = int(own.keep.sum() - plain.keep.sum())
+    print("capacity rerouted: kept", int(plain.keep.sum()), "->", int(own.keep.sum()), "moved", moved)
+    assert moved > 0
+    # sampled rows: tokens with a moved pair and tokens without, both on a few experts
+    rng = np.random.default_rng(0)
+    moved_tok = np.nonzero((own.keep & ~plain.keep).any(axis=1) & ~diff)[0]
+    other_tok = np.nonzero(~(own.keep & ~plain.keep).any(axis=1) & ~diff)[0]
+    toks = np.unique(np.concatenate([rng.choice(moved_tok, 24, replace=False), rng.choice(other_tok, 8,
+                                                                                          replace=False)]))
+    ref = np.zeros((len(toks), w.d))
+    Xf = oracle.as_f64(inp.X[toks], w.dtype)
+    for e in sorted(set(int(own.assigned[t, s]) for t in toks for s in range(w.k) if own.keep[t, s])):
+        W1e, W2e = oracle.as_f64(inp.W1[e], w.dtype), oracle.as_f64(inp.W2[e], w.dtype)
+        rows = [(i, s) for i, t in enumerate(toks) for s in range(w.k) if own.keep[t, s] and own.assigned[t, s] == e]
+        ys = oracle.expert_ffn(Xf[[i for i, _ in rows]], W1e, W2e)
+        for (i, s), y in zip(rows, ys):
+            ref[i] += r.weights[toks[i], s] * y
+    err = row_rel_err(dev_to_f64(out[torch.from_numpy(toks).cuda()]), ref)
+    assert err.max() <= rel_tol(w.dtype), f"max row rel err {err.max():.3g}"
