@@ -1,10 +1,13 @@
 """Benchmark of the sparse MoE FFN layer forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|decode|skewed|capacity|tiny]
+                    [--reroute]
 
 A step is one moe_forward (router, dispatch, expert GEMM1+GELU, GEMM2,
 combine) over one batch of seeded synthetic inputs that are resident in HBM
-before the timed region starts.  The headline times K steps captured in one
+before the timed region starts.  --reroute times moe_forward_reroute
+instead: pairs over the expert capacity move to their token's next-best
+expert with room rather than being dropped.  The headline times K steps captured in one
 HIP graph and replayed.  Each stage entry point is then timed on its own: K
 back-to-back launches between two HIP events on the stream the kernels run
 on, which gives the kernels' average duration without host gaps.  Prints one
@@ -87,6 +90,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of one HIP-graph replay of the K steps")
+    ap.add_argument("--reroute", action="store_true",
+                    help="reroute over-capacity pairs to the next-best expert (moe_forward_reroute)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (reference for HBM byte counters)")
     return ap.parse_args()
@@ -100,23 +105,24 @@ def to_dev(torch, a, dtype):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
 
 
-def stage_work(w, N, active, es, gathers):
+def stage_work(w, N, active, es, gathers, reroute=False):
     """Algorithmic FLOPs and bytes per launch of each stage (N kept pairs,
     `active` experts with rows).  With the gathered up-projection the
     dispatch moves indices only and the up-projection reads each pair's row
     of X in place of the copied row."""
     T, d, F, E, k = w.T, w.d, w.F, w.E, w.k
     rows = 0 if gathers else T * d * es + N * d * es
+    order = T * E if reroute else 0  # the preference order, written by the router, read by the dispatch
     return {
-        "route": {"flops": 2.0 * T * d * E, "bytes": T * d * es + d * E * es + T * k * 8},
-        "dispatch": {"flops": 0.0, "bytes": rows + T * k * 4 * 3},
+        "route": {"flops": 2.0 * T * d * E, "bytes": T * d * es + d * E * es + T * k * 8 + order},
+        "dispatch": {"flops": 0.0, "bytes": rows + T * k * 4 * 3 + order},
         "expert_up": {"flops": 2.0 * N * d * F, "bytes": active * F * d * es + N * d * es + N * F * es},
         "expert_down": {"flops": 2.0 * N * F * d, "bytes": active * d * F * es + N * F * es + N * d * es},
         "combine": {"flops": 0.0, "bytes": N * d * es + T * k * 8 + T * d * es},
     }
 
 
-def cpu_baseline(w, inp, sample):
+def cpu_baseline(w, inp, sample, reroute=False):
     """The oracle, as it stands, on a bounded sample of the workload."""
     import oracle
     import workloads
@@ -133,7 +139,8 @@ def cpu_baseline(w, inp, sample):
         while True:
             for s in range(n):
                 X = workloads.decode_step_inputs(w, s)
-                oracle.moe_forward(X, inp.Wg, inp.bias, inp.W1, inp.W2, w.k, inp.expert_capacity, w.dtype)
+                oracle.moe_forward(X, inp.Wg, inp.bias, inp.W1, inp.W2, w.k, inp.expert_capacity, w.dtype,
+                                   reroute=reroute)
             toks += n * w.T
             reps += 1
             elapsed = time.perf_counter() - t0
@@ -144,14 +151,14 @@ def cpu_baseline(w, inp, sample):
         n = sample or min(w.T, 8192)
         cap = (-(-n // w.E) * w.k) if inp.expert_capacity >= 0 else -1
         while True:
-            oracle.moe_forward(inp.X[:n], inp.Wg, inp.bias, inp.W1, inp.W2, w.k, cap, w.dtype)
+            oracle.moe_forward(inp.X[:n], inp.Wg, inp.bias, inp.W1, inp.W2, w.k, cap, w.dtype, reroute=reroute)
             toks += n
             reps += 1
             elapsed = time.perf_counter() - t0
             if elapsed >= 10.0 or elapsed + elapsed / reps > 30.0:
                 break
         desc = (f"{reps} x first {n} of {w.T} tokens as one batch, full weights"
-                + (f", capacity {cap}" if cap >= 0 else ""))
+                + (f", capacity {cap}" if cap >= 0 else "") + (", rerouted" if reroute and cap >= 0 else ""))
     dt = time.perf_counter() - t0
     return {"value": toks / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": desc, "seconds": round(dt, 2)}
@@ -190,7 +197,8 @@ def main():
         xs = [to_dev(torch, workloads.decode_step_inputs(w, s), dt) for s in range(w.steps)]
     else:
         xs = [to_dev(torch, inp.X, dt)]
-    layer = moe.MoELayer(cfg, Wg, W1, W2, bias)
+    reroute = bool(args.reroute)
+    layer = moe.MoELayer(cfg, Wg, W1, W2, bias, reroute=reroute)
     b = layer.buf
     stream = torch.cuda.current_stream()
 
@@ -237,7 +245,8 @@ def main():
     # to launch as they do in decoding.
     names = ["route", "dispatch", "expert_up", "expert_down", "combine"]
     rws, rbytes = b.scratch_view(cfg, "route"), moe.moe_workspace_size(cfg, moe.MOE_OP_ROUTE)
-    dws, dbytes = b.scratch_view(cfg, "dispatch"), moe.moe_workspace_size(cfg, moe.MOE_OP_DISPATCH)
+    dws = b.scratch_view(cfg, "dispatch")
+    dbytes = moe.moe_workspace_size(cfg, moe.MOE_OP_DISPATCH_REROUTE if reroute else moe.MOE_OP_DISPATCH)
     Xp_ws, H_ws, Yp_ws = b.workspace_view(cfg, "Xp"), b.workspace_view(cfg, "H"), b.workspace_view(cfg, "Yp")
     small = w.T * w.k * max(w.d, w.F) * es <= (64 << 20)
     nsets = min(4, len(xs)) if small else 1
@@ -247,6 +256,7 @@ def main():
         torch.cuda.synchronize()
         keep = (lambda t: t.clone()) if nsets > 1 else (lambda t: t)
         sets.append({"X": xs[si], "ids": keep(b.topk_ids), "w": keep(b.topk_w), "off": keep(b.expert_offsets),
+                     "order": keep(b.expert_order) if reroute else None,
                      "inv": keep(b.inv_perm), "perm": keep(b.perm), "Xp": keep(Xp_ws), "H": keep(H_ws),
                      "Yp": keep(Yp_ws)})
         off = b.expert_offsets.cpu().numpy()
@@ -264,6 +274,12 @@ def main():
         "expert_down": lambda q: moe.moe_expert_down(cfg, q["H"], q["off"], W2, q["Yp"]),
         "combine": lambda q: moe.moe_combine(cfg, q["Yp"], q["inv"], q["w"], b.out),
     }
+    if reroute:
+        stage_fn["route"] = lambda q: moe.moe_route_ranked(cfg, q["X"], Wg, bias, b.topk_ids, b.topk_w,
+                                                           b.expert_order, rws, rbytes)
+        stage_fn["dispatch"] = lambda q: moe.moe_dispatch_reroute(
+            cfg, q["ids"], q["order"], q["X"], b.expert_counts, b.expert_offsets, b.perm, b.inv_perm,
+            None if gathers else Xp_ws, dws, dbytes)
     stage_ms = {}
     for n in names:
         fn = stage_fn[n]
@@ -272,7 +288,7 @@ def main():
 
     N = float(np.mean(per_step_N))
     active = float(np.mean(per_step_active))
-    work = stage_work(w, N, active, es, gathers)
+    work = stage_work(w, N, active, es, gathers, reroute)
     stages = {}
     for n in names:
         ms = stage_ms[n]
@@ -293,14 +309,14 @@ def main():
         roof = {"bound": "mfma", "achieved": round(work[dom]["flops"] / ms / 1e9, 2), "peak": peak,
                 "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = gemm_traffic(w.name, dom)
+    roof["traffic"] = gemm_traffic(w.name + ("_reroute" if reroute else ""), dom)
     roof["algorithmic_bytes"] = round(work[dom]["bytes"])
     roof["kernel"] = gemm_kernel_name(w, inp.expert_capacity, dom, gathers)
     roof["ms"] = round(ms, 5)
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(w, inp, args.cpu_sample)
+        cpu = cpu_baseline(w, inp, args.cpu_sample, reroute)
 
     tok_per_step = w.T
     line = {
@@ -318,8 +334,10 @@ def main():
         "vs_baseline": None,
         "dtype": dt,
         "data": "synthetic (seeded; random-init weights of the stated shapes)",
-        "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "k": w.k, "F": w.F,
-                   "expert_capacity": inp.expert_capacity, "bias": w.bias, "seed": w.seed,
+        "config": {"workload": w.name + ("_rerouted" if reroute and inp.expert_capacity >= 0 else ""), "T": w.T, "d": w.d, "E": w.E, "k": w.k, "F": w.F,
+                   "expert_capacity": inp.expert_capacity,
+                   "over_capacity": ("rerouted" if reroute else "dropped") if inp.expert_capacity >= 0 else "none",
+                   "bias": w.bias, "seed": w.seed,
                    "parallelism": "single GPU, all experts resident"},
         "roofline": roof,
         "cpu_baseline": cpu,

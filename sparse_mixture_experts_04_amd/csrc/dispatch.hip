@@ -323,115 +323,181 @@ __global__ __launch_bounds__(kWave) void dispatch_keep_kernel(const int32_t* __r
 // that the token does not already use (an earlier slot may have moved
 // there); a pair that finds none stays dropped.  Its weight is unchanged.
 //
-// One block.  For each slot s the tokens go in batches of kRerouteThreads:
-// each thread checks one token's pair (t, s) and, if it was dropped, writes
-// its candidate list (preference positions k..E-1 minus the experts the
-// token's other slots sit on) to LDS; the dropped pairs are compacted in
-// token order.  Wave 0 then places them 64 at a time: every lane picks its
-// first candidate with room as the room stood at the start of the group.
-// That pick is the sequential rule's iff fewer earlier lanes of the group
-// picked the same expert than it had room -- the candidates before it were
-// full at the start, and room only shrinks.  The lanes before the first one
-// that fails commit and the group restarts at that lane; lane 0 never fails,
-// and the failing lane's expert is full after the commit, so each slot's
-// pass needs at most ceil(dropped / 64) + E groups.
+// Three steps.  (1) Per 64-token chunk, the dropped pairs of each slot are
+// counted; (2) a scan over the chunks gives each its place in one list in
+// priority order (slot-major segments); (3) per chunk, each dropped pair is
+// written to the list with a copy of its token's preference order and the
+// list index of the token's next dropped slot.  Then (4) one workgroup of
+// 1024 threads places the list, 1024 pairs at a time within one slot's
+// segment: every thread picks its pair's first candidate that is neither
+// full (as the room stood at the start of the round) nor used by its token.
+// That pick is the sequential rule's iff fewer earlier pairs of the round
+// picked the same expert than it had room: the candidates before it were
+// full at the start and room only shrinks.  The pairs before the first one
+// that fails commit, and the round restarts there.  The first pair of a round
+// never fails, and the failing pair's expert is full after the commit, so
+// the rounds number at most ceil(segment / 1024) per slot plus E in all.  A
+// pair passes the experts it used on to its token's next dropped slot.
 constexpr int kRerouteThreads = 1024;
 
+// (1) Dropped pairs per (chunk, slot); the assignment starts as a copy of ids.
+__global__ __launch_bounds__(kWave) void dispatch_drop_count_kernel(const int32_t* __restrict__ ids,
+                                                                    const int8_t* __restrict__ keep, int T, int E,
+                                                                    int k, int32_t* __restrict__ drop_hist,
+                                                                    int32_t* __restrict__ ids2) {
+  const int lane = threadIdx.x;
+  const int t = blockIdx.x * kDispatchChunk + lane;
+  for (int s = 0; s < k; ++s) {
+    bool dropped = false;
+    if (t < T) {
+      const int64_t pr = static_cast<int64_t>(t) * k + s;
+      const int e = ids[pr];
+      ids2[pr] = e;
+      dropped = keep[pr] == 0 && e >= 0 && e < E;
+    }
+    const uint64_t b = __ballot(dropped);
+    if (lane == 0) drop_hist[static_cast<int64_t>(blockIdx.x) * k + s] = __popcll(b);
+  }
+}
+
+// (3) The list: entry i holds the pair id, the token's preference order
+// (rstride = 32 or 64 bytes, padded with a copy of position 0), the list index of the token's next dropped slot (-1: none) and
+// the experts the token uses: its top-k here, plus, while placing, where
+// its earlier slots moved.
+__global__ __launch_bounds__(kWave) void dispatch_drop_list_kernel(
+    const int32_t* __restrict__ ids, const int8_t* __restrict__ keep, const uint8_t* __restrict__ order, int T,
+    int E, int k, int rstride, const int32_t* __restrict__ drop_hist, const int32_t* __restrict__ drop_seg,
+    int32_t* __restrict__ list, uint8_t* __restrict__ rows, int32_t* __restrict__ next,
+    uint64_t* __restrict__ used) {
+  const int lane = threadIdx.x;
+  const int t = blockIdx.x * kDispatchChunk + lane;
+  const uint64_t below = (1ull << lane) - 1ull;
+  int prev = -1;  // list index of this token's previous dropped slot
+  for (int s = 0; s < k; ++s) {
+    bool dropped = false;
+    if (t < T) {
+      const int64_t pr = static_cast<int64_t>(t) * k + s;
+      const int e = ids[pr];
+      dropped = keep[pr] == 0 && e >= 0 && e < E;
+    }
+    const uint64_t b = __ballot(dropped);
+    if (dropped) {
+      const int pos = drop_seg[s] + drop_hist[static_cast<int64_t>(blockIdx.x) * k + s] + __popcll(b & below);
+      list[pos] = t * k + s;
+      const uint8_t* src = order + static_cast<int64_t>(t) * E;
+      uint8_t* dst = rows + static_cast<int64_t>(pos) * rstride;
+      for (int q = 0; q < rstride; ++q) dst[q] = src[q < E ? q : 0];
+      // The token's top-k experts count as used, so a scan of the whole row
+      // skips positions below k (and the padding, a copy of position 0).
+      uint64_t topk = 0ull;
+      for (int j = 0; j < k; ++j) {
+        const int e = ids[static_cast<int64_t>(t) * k + j];
+        if (e >= 0 && e < E) topk |= 1ull << e;
+      }
+      for (int q = 0; q < k; ++q) topk |= 1ull << (src[q] & 63);
+      next[pos] = -1;
+      used[pos] = topk;
+      if (prev >= 0) next[prev] = pos;
+      prev = pos;
+    }
+  }
+}
+
+// (4) Placement, one workgroup.  NQ = 32 or 64: the row length (E <= NQ).
+template <int NQ>
 __global__ __launch_bounds__(kRerouteThreads) void dispatch_reroute_kernel(
-    const int32_t* __restrict__ ids, const uint8_t* __restrict__ order, const int32_t* __restrict__ counts, int T,
-    int E, int k, int capacity, int8_t* __restrict__ keep, int32_t* __restrict__ ids2) {
-  extern __shared__ uint8_t s_cand[];                   // [kRerouteThreads][E]
-  __shared__ uint8_t s_ncand[kRerouteThreads];
-  __shared__ int s_list[kRerouteThreads];
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ drop_seg, const int32_t* __restrict__ list,
+    const uint8_t* __restrict__ rows, const int32_t* __restrict__ next, uint64_t* __restrict__ used, int E, int k,
+    int capacity, int8_t* __restrict__ keep, int32_t* __restrict__ ids2) {
   __shared__ int s_room[kMaxExperts];
-  __shared__ int s_wave_cnt[kRerouteThreads / kWave];
+  __shared__ int s_cnt[kRerouteThreads / kWave][kMaxExperts];
+  __shared__ int s_first;
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = tid / kWave;
-  const int64_t pairs = static_cast<int64_t>(T) * k;
-  for (int64_t i = tid; i < pairs; i += kRerouteThreads) ids2[i] = ids[i];
-  if (tid < E) s_room[tid] = capacity - min(max(counts[tid], 0), capacity);
-  __threadfence();  // the copy is in L2 before any wave reads it back
+  const uint64_t below = (1ull << lane) - 1ull;
+  if (tid < kMaxExperts) s_room[tid] = tid < E ? capacity - min(max(counts[tid], 0), capacity) : 0;
+  int s = 0;
+  int seg_end = drop_seg[1];
+  const int m = drop_seg[k];
+  int c0 = 0;
+  while (c0 < m && c0 >= seg_end) seg_end = drop_seg[++s + 1];  // rounds stay inside one slot's segment
+  // The round's entries: pair id, the experts its token's earlier slots
+  // moved to (written in an earlier segment: read past the L1), and the
+  // preference order as words.
+  int pair = 0;
+  uint64_t mine = 0ull;
+  u32x4_t wv[NQ / 16];
+  auto load = [&]() {
+    const int i = c0 + tid;
+    if (i < seg_end) {
+      pair = list[i];
+      mine = __hip_atomic_load(&used[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const u32x4_t* row = reinterpret_cast<const u32x4_t*>(rows + static_cast<int64_t>(i) * NQ);
+#pragma unroll
+      for (int w = 0; w < NQ / 16; ++w) wv[w] = row[w];
+    }
+  };
+  if (c0 < m) load();
   __syncthreads();
-  for (int s = 0; s < k; ++s) {
-    for (int b0 = 0; b0 < T; b0 += kRerouteThreads) {
-      const int t = b0 + tid;
-      bool dropped = false;
-      if (t < T) {
-        const int64_t pr = static_cast<int64_t>(t) * k + s;
-        const int e0 = ids[pr];
-        dropped = keep[pr] == 0 && e0 >= 0 && e0 < E;
+  while (c0 < m) {
+    const int i = c0 + tid;
+    const bool valid = i < seg_end;
+    // Full experts (and ids past E) as they stand at the start of the round.
+    const uint64_t full = __ballot(lane >= E || s_room[lane] <= 0);
+    int pick = kNone;
+    if (valid) {
+      // Last to first, so the earliest available position wins; the top-k
+      // (and the padding, a copy of position 0) are in `mine`.
+      const uint64_t avail = ~(full | mine);
+      const uint32_t lo = static_cast<uint32_t>(avail), hi = static_cast<uint32_t>(avail >> 32);
+#pragma unroll
+      for (int q = NQ - 1; q >= 0; --q) {
+        const uint32_t e = __builtin_amdgcn_ubfe(wv[q >> 4][(q >> 2) & 3], (q & 3) * 8, 8);
+        const uint32_t ok = NQ == 32 ? __builtin_amdgcn_ubfe(lo, e, 1)
+                                     : __builtin_amdgcn_ubfe(e < 32 ? lo : hi, e & 31, 1);
+        pick = ok ? static_cast<int>(e) : pick;
       }
-      if (dropped) {
-        // The token's other slots: their experts as they stand (slots before
-        // s are final; ids2 is read past the L1, which other waves wrote).
-        uint64_t used = 0;
-        for (int j = 0; j < k; ++j) {
-          const int ej = __hip_atomic_load(&ids2[static_cast<int64_t>(t) * k + j], __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-          if (j != s && ej >= 0 && ej < E) used |= 1ull << ej;
-        }
-        const uint8_t* row = order + static_cast<int64_t>(t) * E;
-        uint8_t* cand = s_cand + tid * E;
-        int nc = 0;
-        for (int q = k; q < E; ++q) {
-          const int e = row[q];
-          if (e < E && !((used >> e) & 1ull)) cand[nc++] = static_cast<uint8_t>(e);
-        }
-        s_ncand[tid] = static_cast<uint8_t>(nc);
-      }
-      const uint64_t bal = __ballot(dropped);
-      if (lane == 0) s_wave_cnt[wave] = __popcll(bal);
-      __syncthreads();
-      int base = 0, m = 0;
+    }
+    // Rank of each pick among the round's earlier picks of the same expert.
+    const Ballots B = ballots_of(pick);
+    const int rank_w = pick != kNone ? __popcll(match(B, pick) & below) : 0;
+    if (lane < E) s_cnt[wave][lane] = __popcll(match(B, lane));
+    if (tid == 0) s_first = min(seg_end, c0 + kRerouteThreads);  // the round's end if nothing fails
+    __syncthreads();
+    if (pick != kNone) {
+      int rank = rank_w;
+#pragma unroll
       for (int w = 0; w < kRerouteThreads / kWave; ++w) {
-        const int c = s_wave_cnt[w];
-        base += w < wave ? c : 0;
-        m += c;
+        const int c = s_cnt[w][pick];
+        rank += w < wave ? c : 0;
       }
-      if (dropped) s_list[base + __popcll(bal & ((1ull << lane) - 1ull))] = tid;
-      __syncthreads();
-      if (wave == 0) {
-        const uint64_t below = (1ull << lane) - 1ull;
-        for (int c0 = 0; c0 < m;) {
-          const int idx = c0 + lane;
-          const int slot = idx < m ? s_list[idx] : 0;
-          int pick = kNone;
-          if (idx < m) {
-            const int nc = s_ncand[slot];
-            const uint8_t* cand = s_cand + slot * E;
-            for (int j = 0; j < nc; ++j) {
-              const int e = cand[j];
-              if (s_room[e] > 0) {
-                pick = e;
-                break;
-              }
-            }
-          }
-          const Ballots B = ballots_of(pick);
-          const uint64_t same = pick != kNone ? match(B, pick) : 0ull;
-          const int rank = __popcll(same & below);
-          const bool bad = pick != kNone && rank >= s_room[pick];
-          const uint64_t badm = __ballot(bad);
-          const int f = badm != 0ull ? __builtin_ctzll(badm) : kWave;
-          const int nlive = min(f, m - c0);  // >= 1: lane 0 never fails
-          const uint64_t live = nlive >= kWave ? ~0ull : (1ull << nlive) - 1ull;
-          if (lane < nlive && pick != kNone) {
-            const int64_t pr = static_cast<int64_t>(b0 + slot) * k + s;
-            ids2[pr] = pick;
-            keep[pr] = 1;
-          }
-          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          // The first committing lane of each picked expert takes the room of all of them.
-          if (lane < nlive && pick != kNone && rank == 0) s_room[pick] -= __popcll(same & live);
-          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          c0 += nlive;
-        }
-        __threadfence();  // this batch's placements are in L2 before the next slot's pass reads them
+      if (rank >= s_room[pick]) atomicMin(&s_first, i);
+    }
+    __syncthreads();
+    const int f = s_first;  // > c0: the round's first pair never fails
+    const bool commit = valid && i < f;
+    if (commit) {
+      if (pick != kNone) {
+        ids2[pair] = pick;
+        keep[pair] = 1;
       }
-      __syncthreads();
+      const int nx = next[i];
+      if (nx >= 0) used[nx] = mine | (pick != kNone ? 1ull << pick : 0ull);
+    }
+    const uint64_t live = __ballot(commit);
+    if (lane < E) {
+      const int dec = __popcll(match(B, lane) & live);
+      if (dec > 0) atomicSub(&s_room[lane], dec);
+    }
+    c0 = f;
+    const bool new_seg = c0 >= seg_end;
+    if (!new_seg) load();  // same segment: the next round's entries load across the barrier
+    else __threadfence();  // a new segment reads used[] written in this one
+    __syncthreads();
+    if (new_seg && c0 < m) {
+      while (c0 >= seg_end) seg_end = drop_seg[++s + 1];
+      load();
     }
   }
 }
@@ -727,7 +793,16 @@ size_t dispatch_scratch_bytes(int T, int E, int k, bool capacity, bool reroute) 
     b += align256(nchunks * E * sizeof(int32_t));
     b += align256(static_cast<size_t>(k) * E * sizeof(int32_t));
     b += align256(static_cast<size_t>(T) * k);
-    if (reroute) b += align256(static_cast<size_t>(T) * k * sizeof(int32_t));
+    if (reroute) {
+      const size_t pairs = static_cast<size_t>(T) * k;
+      b += align256(pairs * sizeof(int32_t));             // ids2
+      b += align256(nchunks * k * sizeof(int32_t));       // drop_hist
+      b += align256((static_cast<size_t>(k) + 1) * sizeof(int32_t));  // drop_seg
+      b += align256(pairs * sizeof(int32_t));             // drop_list
+      b += align256(pairs * sizeof(int32_t));             // drop_next
+      b += align256(pairs * sizeof(uint64_t));            // drop_used
+      b += align256(pairs * (E <= 32 ? 32 : 64));         // drop_rows (rows of 32 or 64 bytes)
+    }
   }
   return b;
 }
@@ -745,7 +820,22 @@ DispatchScratch carve_dispatch_scratch(void* ws, int T, int E, int k, bool capac
     p += align256(static_cast<size_t>(k) * E * sizeof(int32_t));
     s.keep = reinterpret_cast<int8_t*>(p);
     p += align256(static_cast<size_t>(T) * k);
-    if (reroute) s.ids2 = reinterpret_cast<int32_t*>(p);
+    if (reroute) {
+      const size_t pairs = static_cast<size_t>(T) * k;
+      s.ids2 = reinterpret_cast<int32_t*>(p);
+      p += align256(pairs * sizeof(int32_t));
+      s.drop_hist = reinterpret_cast<int32_t*>(p);
+      p += align256(nchunks * k * sizeof(int32_t));
+      s.drop_seg = reinterpret_cast<int32_t*>(p);
+      p += align256((static_cast<size_t>(k) + 1) * sizeof(int32_t));
+      s.drop_list = reinterpret_cast<int32_t*>(p);
+      p += align256(pairs * sizeof(int32_t));
+      s.drop_next = reinterpret_cast<int32_t*>(p);
+      p += align256(pairs * sizeof(int32_t));
+      s.drop_used = reinterpret_cast<uint64_t*>(p);
+      p += align256(pairs * sizeof(uint64_t));
+      s.drop_rows = reinterpret_cast<uint8_t*>(p);
+    }
   }
   return s;
 }
@@ -869,13 +959,19 @@ hipError_t launch_dispatch_reroute(int dtype, const int32_t* ids, const uint8_t*
                      total_pairs);
   hipLaunchKernelGGL(dispatch_keep_kernel, dim3(nchunks), dim3(kWave), 0, stream, ids, T, E, k, capacity,
                      sc.chunk_base, sc.slot_base, sc.keep, sc.chunk_kept);
-  const size_t cand_lds = static_cast<size_t>(kRerouteThreads) * E;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&dispatch_reroute_kernel),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     static_cast<int>(kRerouteThreads * kMaxExperts));
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(dispatch_reroute_kernel, dim3(1), dim3(kRerouteThreads), cand_lds, stream, ids, order, counts, T,
-                     E, k, capacity, sc.keep, sc.ids2);
+  hipLaunchKernelGGL(dispatch_drop_count_kernel, dim3(nchunks), dim3(kWave), 0, stream, ids, sc.keep, T, E, k,
+                     sc.drop_hist, sc.ids2);
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, sc.drop_hist, nchunks, k,
+                     static_cast<int>(kScanOffsets), k, k, capacity, nullptr, sc.drop_seg, nullptr, nullptr, 0);
+  const int rstride = E <= 32 ? 32 : 64;
+  hipLaunchKernelGGL(dispatch_drop_list_kernel, dim3(nchunks), dim3(kWave), 0, stream, ids, sc.keep, order, T, E, k,
+                     rstride, sc.drop_hist, sc.drop_seg, sc.drop_list, sc.drop_rows, sc.drop_next, sc.drop_used);
+  if (E <= 32)
+    hipLaunchKernelGGL(dispatch_reroute_kernel<32>, dim3(1), dim3(kRerouteThreads), 0, stream, counts, sc.drop_seg,
+                       sc.drop_list, sc.drop_rows, sc.drop_next, sc.drop_used, E, k, capacity, sc.keep, sc.ids2);
+  else
+    hipLaunchKernelGGL(dispatch_reroute_kernel<64>, dim3(1), dim3(kRerouteThreads), 0, stream, counts, sc.drop_seg,
+                       sc.drop_list, sc.drop_rows, sc.drop_next, sc.drop_used, E, k, capacity, sc.keep, sc.ids2);
   hipLaunchKernelGGL(dispatch_count_kept_kernel, dim3(nchunks), dim3(kWave), 0, stream, sc.ids2, sc.keep, T, E, k,
                      sc.chunk_kept);
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, sc.chunk_kept, nchunks, E,

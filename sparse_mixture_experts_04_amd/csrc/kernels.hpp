@@ -20,7 +20,14 @@ struct DispatchScratch {
   int32_t* chunk_kept;   // [nchunks][E]:  kept pairs per chunk, then prefix (capacity only)
   int32_t* slot_base;    // [k][E]: pairs of expert e in slots < s (capacity only)
   int8_t* keep;          // [T*k]: keep flag per pair (capacity only)
-  int32_t* ids2;         // [T*k]: expert of each pair after rerouting (rerouting only)
+  // Rerouting only:
+  int32_t* ids2;         // [T*k]: expert of each pair after rerouting
+  int32_t* drop_hist;    // [nchunks][k]: dropped pairs per chunk and slot, then prefix
+  int32_t* drop_seg;     // [k+1]: start of each slot's segment of the dropped-pair list
+  int32_t* drop_list;    // [T*k]: dropped pair ids in (slot, token) order
+  int32_t* drop_next;    // [T*k]: list index of the same token's next dropped slot, -1 if none
+  uint64_t* drop_used;   // [T*k]: experts the token's earlier dropped slots moved to
+  uint8_t* drop_rows;    // [T*k][32 or 64]: the token's preference order, per list entry
 };
 
 size_t dispatch_scratch_bytes(int T, int E, int k, bool capacity, bool reroute = false);

@@ -65,6 +65,23 @@ __device__ __forceinline__ void argmax16(float& bv, int& bi) {
   argmax_dpp_step<0x140>(bv, bi);
 }
 
+// Step R of the places in a 16-lane row: compare this lane's NT values with
+// those of the lane that row rotation R brings here (its lane index comes
+// along the same rotation, so the direction of the rotation does not matter).
+template <int NT, int R>
+__device__ __forceinline__ void place_steps(const f32x4_t (&acc)[NT], int i, int n, int (&place)[NT]) {
+  if constexpr (R < 16) {
+    const int n2 = R == 0 ? n : __builtin_amdgcn_update_dpp(0, n, 0x120 + R, 0xF, 0xF, false);
+#pragma unroll
+    for (int t2 = 0; t2 < NT; ++t2) {
+      const float v2 = R == 0 ? acc[t2][i] : dpp_move<0x120 + R>(acc[t2][i]);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) place[t] += better(v2, t2 * 16 + n2, acc[t][i], t * 16 + n) ? 1 : 0;
+    }
+    place_steps<NT, R + 1>(acc, i, n, place);
+  }
+}
+
 // Top-k + renormalisation for one 16-token row tile held in MFMA C layout:
 // acc[t][i] is the logit of token row (lane>>4)*4+i and expert t*16+(lane&15).
 // sel_val / sel_id: LDS scratch [16][k] of the calling wave.
@@ -80,8 +97,9 @@ __device__ __forceinline__ void argmax16(float& bv, int& bi) {
 // tokens that select the expert -- the per-tile parts of the load-balancing
 // statistics ("Qwen2-MoE代码解析" §3.3).
 // order (may be null): [T][E] bytes; row t receives all E experts of token t
-// in preference order (the same arg-max rounds continued past k), the list
-// the over-capacity rerouting walks ("Qwen2-MoE代码解析" §3.4).
+// in preference order (the order of better(), so its first k entries are
+// the selected ids), the list the over-capacity rerouting walks
+// ("Qwen2-MoE代码解析" §3.4).
 template <int NT>
 __device__ __forceinline__ void topk_tile(f32x4_t (&acc)[NT], const float* __restrict__ bias, int E, int k,
                                           int tok0, int T_tokens, float* sel_val, int* sel_id,
@@ -124,8 +142,26 @@ __device__ __forceinline__ void topk_tile(f32x4_t (&acc)[NT], const float* __res
       for (int t = 0; t < NT; ++t) col[t] += live ? z[t] / den : 0.f;
     }
   }
-  const int rounds = order != nullptr ? E : k;
-  for (int s = 0; s < rounds; ++s) {
+  if (order != nullptr) {
+    // Each expert's place in its token's order: the number of experts of
+    // the row that beat it (better() is a total order, so the places are a
+    // permutation).  The 16 lanes of a row see each other's values through
+    // the 15 row rotations (DPP row_ror), 16 steps instead of E arg-max rounds.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int place[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) place[t] = 0;
+      place_steps<NT, 0>(acc, i, n, place);
+      const int tok = tok0 + grp * 4 + i;
+      if (tok < T_tokens) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          if (t * 16 + n < E) order[static_cast<int64_t>(tok) * E + place[t]] = static_cast<uint8_t>(t * 16 + n);
+      }
+    }
+  }
+  for (int s = 0; s < k; ++s) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float bv = acc[0][i];
@@ -148,7 +184,6 @@ __device__ __forceinline__ void topk_tile(f32x4_t (&acc)[NT], const float* __res
           sel_val[(grp * 4 + i) * kMaxExperts + s] = bv;
           sel_id[(grp * 4 + i) * kMaxExperts + s] = bi;
         }
-        if (order != nullptr && live) order[static_cast<int64_t>(tok0 + grp * 4 + i) * E + s] = static_cast<uint8_t>(bi);
       }
     }
   }
