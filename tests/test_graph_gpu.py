@@ -1,6 +1,7 @@
 """The layer captured in a HIP graph (through torch.cuda.graph, on torch's
 current stream) replays bit-identically to eager execution, replay after
-replay, with eager work and synchronisations in between."""
+replay, with eager work and synchronisations in between (the plain forward
+and the forward that reroutes over-capacity pairs)."""
 import pytest
 import torch
 
@@ -11,13 +12,14 @@ from gpu_util import to_dev
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("T,d,E,k,F,cap", [(300, 256, 8, 2, 384, -1), (8, 1024, 64, 2, 256, -1),
-                                           (500, 256, 16, 4, 256, 100)])
-def test_graph_replay_matches_eager(T, d, E, k, F, cap):
+@pytest.mark.parametrize("T,d,E,k,F,cap,reroute", [(300, 256, 8, 2, 384, -1, False), (8, 1024, 64, 2, 256, -1, False),
+                                                   (500, 256, 16, 4, 256, 100, False),
+                                                   (2500, 256, 16, 4, 256, 500, True)])
+def test_graph_replay_matches_eager(T, d, E, k, F, cap, reroute):
     inp = workloads.random_case(3, T, d, E, k, F, "bf16", cap, 0.3, w_scale=0.05)
     cfg = moe.config(T, d, F, E, k, cap, "bf16")
     layer = moe.MoELayer(cfg, to_dev(inp.Wg, "bf16"), to_dev(inp.W1, "bf16"), to_dev(inp.W2, "bf16"),
-                         to_dev(inp.bias, "f32"))
+                         to_dev(inp.bias, "f32"), reroute=reroute)
     X = to_dev(inp.X, "bf16")
     X2 = torch.randn_like(X)
     ref = layer.forward(X).clone()

@@ -27,6 +27,8 @@ CASES = [
     ("skew_left_dropped", 2100, 128, 16, 2, 128, "bf16", 150, 3.0),
     ("k1_exact_fit", 2048, 128, 16, 1, 128, "bf16", 128, 2.0),
     ("dropless", 300, 128, 8, 2, 128, "bf16", -1, 0.5),
+    # a gate too large for LDS (E = 64, d = 4096): the global-memory router writes the order
+    ("e64_d4096", 700, 4096, 64, 2, 128, "bf16", 30, 1.0),
 ]
 IDS = [c[0] for c in CASES]
 
@@ -181,7 +183,7 @@ def test_forward_reroute(case):
 
 def test_forward_reroute_dropless_equals_forward():
     """Without a capacity nothing overflows: the rerouting forward is the plain forward, bit for bit."""
-    inp, cfg = make(CASES[-1])
+    inp, cfg = make(next(c for c in CASES if c[0] == "dropless"))
     w = inp.workload
     layer, out = _forward(inp, cfg)
     plain = moe.MoELayer(cfg, to_dev(inp.Wg, w.dtype), to_dev(inp.W1, w.dtype), to_dev(inp.W2, w.dtype),
