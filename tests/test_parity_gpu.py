@@ -70,12 +70,14 @@ def test_route(case):
 
 
 @pytest.mark.parametrize("T,d,E,k", [(12000, 256, 16, 2), (40000, 128, 8, 2), (9000, 128, 40, 3), (5000, 256, 5, 2),
-                                     (20000, 2048, 32, 2)],
-                         ids=["t12000_rows4", "t40000_two_passes", "e40_nt3", "e5_gathered_gate", "t20000_d2048"])
+                                     (20000, 2048, 32, 2), (17000, 2048, 64, 2), (16400, 1536, 50, 3)],
+                         ids=["t12000_rows4", "t40000_two_passes", "e40_nt3", "e5_gathered_gate", "t20000_d2048",
+                              "gate_in_l2_64tok_blocks", "gate_in_l2_e50_k3"])
 def test_route_many_tokens(T, d, E, k):
     """Router shapes where one block per CU covers 48-128 tokens per pass
     (and a second pass past 32768 tokens), with gates whose expert count is
-    or is not a multiple of 8."""
+    or is not a multiple of 8; and gates too large for LDS with enough
+    tokens for 64-token blocks (ragged last block)."""
     inp = workloads.random_case(71 + T, T, d, E, k, 64, "bf16", -1, 0.7, w_scale=0.05)
     cfg = moe.config(T, d, 64, E, k, -1, "bf16")
     X, Wg = to_dev(inp.X, "bf16"), to_dev(inp.Wg, "bf16")
