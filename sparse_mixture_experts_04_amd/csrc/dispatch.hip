@@ -422,38 +422,47 @@ __global__ __launch_bounds__(kRerouteThreads) void dispatch_reroute_kernel(
   const int m = drop_seg[k];
   int c0 = 0;
   while (c0 < m && c0 >= seg_end) seg_end = drop_seg[++s + 1];  // rounds stay inside one slot's segment
-  // The round's entries: pair id, the experts its token's earlier slots
-  // moved to (written in an earlier segment: read past the L1), and the
-  // preference order as words.
-  int pair = 0;
-  uint64_t mine = 0ull;
-  u32x4_t wv[NQ / 16];
-  auto load = [&]() {
-    const int i = c0 + tid;
+  // The round's entries: pair id, the list index of its token's next
+  // dropped slot, the experts its token uses (its top-k and where its
+  // earlier slots moved, written in an earlier segment: read past the L1),
+  // and the preference order as words.  The entries of the round after are
+  // fetched while this one runs (into the second set) when that round stays
+  // in the segment; they are used if this round commits all its entries.
+  struct Entry {
+    int pair, nx;
+    uint64_t mine;
+    u32x4_t wv[NQ / 16];
+  };
+  Entry cur{}, pre{};
+  auto load = [&](Entry& en, int base) {
+    const int i = base + tid;
     if (i < seg_end) {
-      pair = list[i];
-      mine = __hip_atomic_load(&used[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      en.pair = list[i];
+      en.nx = next[i];
+      en.mine = __hip_atomic_load(&used[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const u32x4_t* row = reinterpret_cast<const u32x4_t*>(rows + static_cast<int64_t>(i) * NQ);
 #pragma unroll
-      for (int w = 0; w < NQ / 16; ++w) wv[w] = row[w];
+      for (int w = 0; w < NQ / 16; ++w) en.wv[w] = row[w];
     }
   };
-  if (c0 < m) load();
+  if (c0 < m) load(cur, c0);
   __syncthreads();
   while (c0 < m) {
     const int i = c0 + tid;
     const bool valid = i < seg_end;
+    const bool ahead = c0 + kRerouteThreads < seg_end;  // the next round, if this one commits all, is in the segment
+    if (ahead) load(pre, c0 + kRerouteThreads);
     // Full experts (and ids past E) as they stand at the start of the round.
     const uint64_t full = __ballot(lane >= E || s_room[lane] <= 0);
     int pick = kNone;
     if (valid) {
       // Last to first, so the earliest available position wins; the top-k
       // (and the padding, a copy of position 0) are in `mine`.
-      const uint64_t avail = ~(full | mine);
+      const uint64_t avail = ~(full | cur.mine);
       const uint32_t lo = static_cast<uint32_t>(avail), hi = static_cast<uint32_t>(avail >> 32);
 #pragma unroll
       for (int q = NQ - 1; q >= 0; --q) {
-        const uint32_t e = __builtin_amdgcn_ubfe(wv[q >> 4][(q >> 2) & 3], (q & 3) * 8, 8);
+        const uint32_t e = __builtin_amdgcn_ubfe(cur.wv[q >> 4][(q >> 2) & 3], (q & 3) * 8, 8);
         const uint32_t ok = NQ == 32 ? __builtin_amdgcn_ubfe(lo, e, 1)
                                      : __builtin_amdgcn_ubfe(e < 32 ? lo : hi, e & 31, 1);
         pick = ok ? static_cast<int>(e) : pick;
@@ -479,25 +488,29 @@ __global__ __launch_bounds__(kRerouteThreads) void dispatch_reroute_kernel(
     const bool commit = valid && i < f;
     if (commit) {
       if (pick != kNone) {
-        ids2[pair] = pick;
-        keep[pair] = 1;
+        ids2[cur.pair] = pick;
+        keep[cur.pair] = 1;
       }
-      const int nx = next[i];
-      if (nx >= 0) used[nx] = mine | (pick != kNone ? 1ull << pick : 0ull);
+      if (cur.nx >= 0) used[cur.nx] = cur.mine | (pick != kNone ? 1ull << pick : 0ull);
     }
     const uint64_t live = __ballot(commit);
     if (lane < E) {
       const int dec = __popcll(match(B, lane) & live);
       if (dec > 0) atomicSub(&s_room[lane], dec);
     }
+    const bool all = f == c0 + kRerouteThreads;
     c0 = f;
     const bool new_seg = c0 >= seg_end;
-    if (!new_seg) load();  // same segment: the next round's entries load across the barrier
-    else __threadfence();  // a new segment reads used[] written in this one
+    if (!new_seg) {
+      if (all && ahead) cur = pre;  // fetched during this round
+      else load(cur, c0);           // a conflict moved the start: fetch across the barrier
+    } else {
+      __threadfence();  // a new segment reads used[] written in this one
+    }
     __syncthreads();
     if (new_seg && c0 < m) {
       while (c0 >= seg_end) seg_end = drop_seg[++s + 1];
-      load();
+      load(cur, c0);
     }
   }
 }
