@@ -37,16 +37,16 @@ METRIC = "MoE-layer tokens/sec at 1 GPU; % bf16 MFMA peak (FFN) / % HBM peak (re
 # WRITE_SIZE (KiB per dispatch), scaled by what the same counters read for a
 # plain 1 GiB device copy (FETCH_SIZE x2.0, WRITE_SIZE x1.0); valid only for
 # the GEMM source they were taken on (sha1 prefix), else reported as null.
-TRAFFIC_SOURCE_SHA1 = "902f10cb0752"
+TRAFFIC_SOURCE_SHA1 = "437a9341a2c2"
 TRAFFIC_BYTES = {  # (workload, stage) -> (fetch KiB, write KiB) per dispatch, raw counter values
-    ("prefill", "expert_up"): (477144.0, 180229.5),
-    ("prefill", "expert_down"): (795743.7, 65536.1),
-    ("capacity", "expert_up"): (842199.4, 285280.1),
-    ("capacity", "expert_down"): (717284.0, 415961.3),
-    ("skewed", "expert_up"): (7224735.2, 919327.8),
-    ("skewed", "expert_down"): (6395353.6, 262182.2),
-    ("decode", "expert_up"): (122941.2, 80.0),
-    ("decode", "expert_down"): (122812.7, 112.0),
+    ("prefill", "expert_up"): (479448.2, 180225.7),
+    ("prefill", "expert_down"): (784472.2, 65536.2),
+    ("capacity", "expert_up"): (838897.8, 285269.8),
+    ("capacity", "expert_down"): (699457.7, 415661.9),
+    ("skewed", "expert_up"): (7314474.9, 918633.2),
+    ("skewed", "expert_down"): (6472589.0, 262178.4),
+    ("decode", "expert_up"): (122940.3, 80.0),
+    ("decode", "expert_down"): (122812.5, 112.0),
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 

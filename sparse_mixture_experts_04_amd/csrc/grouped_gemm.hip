@@ -263,13 +263,14 @@ __device__ __forceinline__ int key_x(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int key_w(int r) { return ((r >> 1) & 3) | (((r >> 4) & 1) << 2); }
 
 // x * sigmoid(2u) = 0.5 x (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3),
-// with the hardware exp2 and reciprocal (about 1 ulp each).  Large |x|
-// saturates correctly: exp2 -> inf gives -0, exp2 -> 0 gives x.
+// with the hardware exp2 and reciprocal (about 1 ulp each).  -2 log2(e) u is
+// formed as x * (c + 0.044715 c x^2), c = -2 log2(e) sqrt(2/pi): five VALU
+// operations and two transcendentals per value.  Large |x| saturates
+// correctly: exp2 -> inf gives -0, exp2 -> 0 gives x.
 __device__ __forceinline__ float gelu_tanh_fast(float x) {
-  const float kSqrt2OverPi = 0.7978845608028654f;
-  const float kMinus2Log2e = -2.0f * 1.4426950408889634f;
-  const float u = kSqrt2OverPi * fmaf(0.044715f * x, x * x, x);
-  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(kMinus2Log2e * u));
+  constexpr float kC = -2.0f * 1.4426950408889634f * 0.7978845608028654f;
+  const float p = fmaf(kC * 0.044715f, x * x, kC);
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * p));
 }
 
 template <int N>
