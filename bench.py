@@ -317,6 +317,13 @@ def main():
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(w, inp, args.cpu_sample, reroute)
+        if w.name == "tiny":
+            # The tiny layer's oracle also on one core (BLAS limited to one thread).
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                one = cpu_baseline(w, inp, args.cpu_sample, reroute)
+            one["cores"] = 1
+            cpu["one_core"] = one
 
     tok_per_step = w.T
     line = {
