@@ -173,10 +173,11 @@ moe_status moe_expert_up_gather(const moe_config* cfg, const void* X, const int3
                                 const int32_t* expert_offsets, const void* W1, void* H,
                                 void* stream);
 
-/* Host only: *supported = 1 if moe_expert_up_gather runs for cfg (bf16 with
- * more than 64 pairs per expert possible, i.e. min(T, C) > 64, and T*d*2 <
- * 2^31 bytes), else 0.  moe_forward then gathers too and leaves the Xp part of
- * its workspace unwritten. */
+/* Host only: *supported = 1 if moe_expert_up_gather runs for cfg, else 0:
+ * bf16, T*d*2 < 2^31 bytes, and either more than 64 pairs per expert possible
+ * (min(T, C) > 64) or at most 16 (decode-sized batches) with d a multiple of
+ * 128 and F a multiple of 8.  moe_forward then gathers too and leaves the Xp
+ * part of its workspace unwritten. */
 moe_status moe_expert_up_gather_supported(const moe_config* cfg, int32_t* supported);
 
 /* Expert down-projection: Yp[r] = W2[e] H[r] (the second Linear).

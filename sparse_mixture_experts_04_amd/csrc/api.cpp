@@ -80,10 +80,11 @@ int rows_per_expert_bound(const moe_config* c) {
   return b;
 }
 
-// Whether the up-projection reads X through perm (the 256x256 kernel runs
-// and X fits its 32-bit buffer offsets).
+// Whether the up-projection reads X through perm (the 256x256 kernel or the
+// decode kernel runs, and X fits 32-bit buffer offsets).
 bool gathers(const moe_config* c) {
-  return moe::grouped_gemm_gathers(c->dtype, c->hidden_size, rows_per_expert_bound(c), c->num_tokens);
+  return moe::grouped_gemm_gathers(c->dtype, c->hidden_size, c->intermediate_size, rows_per_expert_bound(c),
+                                   c->num_tokens);
 }
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
@@ -258,7 +259,7 @@ moe_status moe_expert_up_gather(const moe_config* cfg, const void* X, const int3
   return hip_status(moe::launch_grouped_gemm_gather(true, X, cfg->num_tokens, perm, cfg->num_experts_per_tok, W1,
                                                     H, expert_offsets, cfg->num_experts, cfg->intermediate_size,
                                                     cfg->hidden_size, static_cast<int>(pairs_of(cfg)),
-                                                    as_stream(stream)));
+                                                    rows_per_expert_bound(cfg), as_stream(stream)));
 }
 
 moe_status moe_expert_down(const moe_config* cfg, const void* H, const int32_t* expert_offsets, const void* W2,

@@ -856,18 +856,22 @@ __global__ __launch_bounds__(kWave) void grouped_gemm_bf16_skinny(const uint16_t
 // waves owns 32 rows of one active expert.  A pass covers kTG groups of 4
 // token rows; token groups past the expert's row count are skipped (uniform
 // per wave), and an expert with more rows than one pass holds gets further
-// passes, so any row count is computed.
+// passes, so any row count is computed.  kGather: token row r of the
+// expert-ordered operand is row gidx[r] / gdiv of A (src_rows rows), as in the
+// 256x256 kernel; an index naming no row of A gives a zero row.
 constexpr int kGvGroups = 2;        // 4-row weight groups per wave
 constexpr int kGvWaves = 4;
 constexpr int kGvRows = kGvWaves * kGvGroups * 4;  // weight rows per block
 constexpr int kGvMaxTok = 16;       // token rows per expert this kernel handles
 
-template <bool kGelu, int kTG>
+template <bool kGelu, int kTG, bool kGather>
 __global__ __launch_bounds__(kGvWaves * kWave) void grouped_gemm_bf16_gemv(const uint16_t* __restrict__ A,
                                                                           const uint16_t* __restrict__ B,
                                                                           uint16_t* __restrict__ C,
                                                                           const int32_t* __restrict__ offsets,
-                                                                          int E, int N, int K, int max_rows) {
+                                                                          int E, int N, int K, int max_rows,
+                                                                          const int32_t* __restrict__ gidx, int gdiv,
+                                                                          int src_rows) {
   __shared__ int s_tile_base[kMaxExperts + 1];
   __shared__ int s_seg0[kMaxExperts];
   __shared__ int s_seg1[kMaxExperts];
@@ -923,10 +927,23 @@ __global__ __launch_bounds__(kGvWaves * kWave) void grouped_gemm_bf16_gemv(const
     const int ntok = min(rows - tok0, kTG * 4);
     const int ntg = (ntok + 3) / 4;
     const unsigned char* xp[kTG];
+    bool xok[kTG];  // the row names a row of A (always, without a gather)
 #pragma unroll
-    for (int tg = 0; tg < kTG; ++tg)
-      xp[tg] = reinterpret_cast<const unsigned char*>(A) +
-               static_cast<int64_t>(seg0 + tok0 + min(tg * 4 + (i16 >> 2), ntok - 1)) * row_bytes + lane_off;
+    for (int tg = 0; tg < kTG; ++tg) {
+      const int r = seg0 + tok0 + min(tg * 4 + (i16 >> 2), ntok - 1);
+      int64_t src = r;
+      xok[tg] = true;
+      if constexpr (kGather) {
+        const unsigned u = static_cast<unsigned>(gidx[r]) / static_cast<unsigned>(gdiv);
+        xok[tg] = u < static_cast<unsigned>(src_rows);
+        src = xok[tg] ? u : 0;
+      }
+      xp[tg] = reinterpret_cast<const unsigned char*>(A) + src * row_bytes + lane_off;
+    }
+    auto ldx = [&](int tg, int64_t off) {
+      const u32x4_t x = ld16(xp[tg] + off);
+      return xok[tg] ? x : u32x4_t{0u, 0u, 0u, 0u};
+    };
 
     f32x4_t acc[kGvGroups][kTG];
 #pragma unroll
@@ -943,7 +960,7 @@ __global__ __launch_bounds__(kGvWaves * kWave) void grouped_gemm_bf16_gemv(const
         for (int rg = 0; rg < kGvGroups; ++rg) wa[buf][u][rg] = ld16_nt(wp[rg] + off);
 #pragma unroll
         for (int tg = 0; tg < kTG; ++tg)
-          if (tg < ntg) xa[buf][u][tg] = ld16(xp[tg] + off);
+          if (tg < ntg) xa[buf][u][tg] = ldx(tg, off);
       }
     };
     auto mma = [&](int buf) {
@@ -976,7 +993,7 @@ __global__ __launch_bounds__(kGvWaves * kWave) void grouped_gemm_bf16_gemv(const
 #pragma unroll
       for (int tg = 0; tg < kTG; ++tg)
         if (tg < ntg) {
-          const u32x4_t x = ld16(xp[tg] + off);
+          const u32x4_t x = ldx(tg, off);
 #pragma unroll
           for (int rg = 0; rg < kGvGroups; ++rg)
             acc[rg][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w[rg]),
@@ -1005,13 +1022,15 @@ __global__ __launch_bounds__(kGvWaves * kWave) void grouped_gemm_bf16_gemv(const
   }
 }
 
-template <bool kGelu, int kTG>
+template <bool kGelu, int kTG, bool kGather = false>
 hipError_t launch_gemv(const uint16_t* A, const uint16_t* B, uint16_t* C, const int32_t* offsets, int E, int N, int K,
-                       int max_rows, hipStream_t stream) {
+                       int max_rows, hipStream_t stream, const int32_t* gidx = nullptr, int gdiv = 1,
+                       int src_rows = 0) {
+  if (kGather && (gidx == nullptr || gdiv < 1 || src_rows < 0)) return hipErrorInvalidValue;
   const int active = max_rows < E ? max_rows : E;
   const int64_t blocks = static_cast<int64_t>(active) * ((N + kGvRows - 1) / kGvRows);
-  hipLaunchKernelGGL((grouped_gemm_bf16_gemv<kGelu, kTG>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(kGvWaves * kWave), 0, stream, A, B, C, offsets, E, N, K, max_rows);
+  hipLaunchKernelGGL((grouped_gemm_bf16_gemv<kGelu, kTG, kGather>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(kGvWaves * kWave), 0, stream, A, B, C, offsets, E, N, K, max_rows, gidx, gdiv, src_rows);
   return hipGetLastError();
 }
 
@@ -1083,18 +1102,36 @@ hipError_t launch_grouped_gemm(int dtype, bool gelu, const void* A, const void* 
                                          static_cast<float*>(C), offsets, E, N, K, max_rows, stream);
 }
 
-bool grouped_gemm_gathers(int dtype, int K, int max_tokens_per_expert, int src_rows) {
-  return dtype == kDtypeBF16 && max_tokens_per_expert > kSkinnyMaxTok &&
+namespace {
+// The decode kernel runs (launch_grouped_gemm's rule) for this shape.
+bool gemv_runs(int K, int N, int max_tokens_per_expert) {
+  return K % 128 == 0 && N % (kGvGroups * 4) == 0 && max_tokens_per_expert <= kGvMaxTok;
+}
+}  // namespace
+
+bool grouped_gemm_gathers(int dtype, int K, int N, int max_tokens_per_expert, int src_rows) {
+  return dtype == kDtypeBF16 && (max_tokens_per_expert > kSkinnyMaxTok || gemv_runs(K, N, max_tokens_per_expert)) &&
          static_cast<int64_t>(src_rows) * K * 2 < (int64_t{1} << 31);
 }
 
 hipError_t launch_grouped_gemm_gather(bool gelu, const void* X, int src_rows, const int32_t* gidx, int gdiv,
                                       const void* B, void* C, const int32_t* offsets, int E, int N, int K,
-                                      int max_rows, hipStream_t stream) {
+                                      int max_rows, int max_tokens_per_expert, hipStream_t stream) {
   if (max_rows <= 0) return hipSuccess;
   const uint16_t* a = static_cast<const uint16_t*>(X);
   const uint16_t* b = static_cast<const uint16_t*>(B);
   uint16_t* c = static_cast<uint16_t*>(C);
+  if (gemv_runs(K, N, max_tokens_per_expert)) {
+    if (max_tokens_per_expert <= 4)
+      return gelu ? launch_gemv<true, 1, true>(a, b, c, offsets, E, N, K, max_rows, stream, gidx, gdiv, src_rows)
+                  : launch_gemv<false, 1, true>(a, b, c, offsets, E, N, K, max_rows, stream, gidx, gdiv, src_rows);
+    if (max_tokens_per_expert <= 8)
+      return gelu ? launch_gemv<true, 2, true>(a, b, c, offsets, E, N, K, max_rows, stream, gidx, gdiv, src_rows)
+                  : launch_gemv<false, 2, true>(a, b, c, offsets, E, N, K, max_rows, stream, gidx, gdiv, src_rows);
+    return gelu ? launch_gemv<true, 4, true>(a, b, c, offsets, E, N, K, max_rows, stream, gidx, gdiv, src_rows)
+                : launch_gemv<false, 4, true>(a, b, c, offsets, E, N, K, max_rows, stream, gidx, gdiv, src_rows);
+  }
+  if (max_tokens_per_expert <= kSkinnyMaxTok) return hipErrorInvalidValue;  // no gathering kernel for this shape
   return gelu ? launch_big<true, true>(a, b, c, offsets, E, N, K, max_rows, gidx, gdiv, src_rows, stream)
               : launch_big<false, true>(a, b, c, offsets, E, N, K, max_rows, gidx, gdiv, src_rows, stream);
 }

@@ -143,14 +143,19 @@ def test_workspace_sizes():
 
 
 def test_gathered_up_projection_support():
-    # bf16 with experts that may hold more than 64 pairs (min(T, C) > 64)
+    # bf16 with experts that may hold more than 64 pairs (min(T, C) > 64): the 256x256 kernel
     assert moe.moe_expert_up_gather_supported(moe.config(8192, 2048, 5632, 32, 2, -1, "bf16"))
     assert moe.moe_expert_up_gather_supported(moe.config(65, 128, 128, 8, 2, -1, "bf16"))
     assert moe.moe_expert_up_gather_supported(moe.config(32768, 2048, 1408, 32, 4, 4096, "bf16"))
     assert not moe.moe_expert_up_gather_supported(moe.config(64, 128, 128, 8, 2, -1, "bf16"))
     assert not moe.moe_expert_up_gather_supported(moe.config(8192, 2048, 5632, 32, 2, 64, "bf16"))
     assert not moe.moe_expert_up_gather_supported(moe.config(8192, 2048, 5632, 32, 2, -1, "f32"))
-    assert not moe.moe_expert_up_gather_supported(moe.config(8, 3584, 2560, 64, 2, -1, "bf16"))
+    # decode-sized batches (at most 16 pairs per expert) gather too, where the decode kernel runs
+    assert moe.moe_expert_up_gather_supported(moe.config(8, 3584, 2560, 64, 2, -1, "bf16"))
+    assert moe.moe_expert_up_gather_supported(moe.config(300, 1024, 256, 16, 2, 16, "bf16"))
+    assert not moe.moe_expert_up_gather_supported(moe.config(300, 1024, 256, 16, 2, 17, "bf16"))  # 17-64: no
+    assert not moe.moe_expert_up_gather_supported(moe.config(8, 3520, 2560, 64, 2, -1, "bf16"))  # d % 128 != 0
+    assert not moe.moe_expert_up_gather_supported(moe.config(8, 3584, 2560, 64, 2, -1, "f32"))
     # X must fit 32-bit buffer offsets: T * d * 2 < 2^31
     assert moe.moe_expert_up_gather_supported(moe.config((1 << 31) // 8192 - 1, 4096, 128, 8, 2, -1, "bf16"))
     assert not moe.moe_expert_up_gather_supported(moe.config((1 << 31) // 8192, 4096, 128, 8, 2, -1, "bf16"))

@@ -268,18 +268,21 @@ def test_expert_up_gather(case):
         assert eh.max() <= rel_tol(w.dtype), f"H rel err {eh.max():.3g}"
 
 
-def test_expert_up_gather_bad_perm_entries():
+@pytest.mark.parametrize("T,d,F,E,k,bad,offsets", [
+    (130, 128, 192, 2, 2, [0, 5, 100, 200, 259], [0, 150, 260]),      # 256x256 kernel
+    (8, 256, 128, 4, 2, [0, 6, 9, 15, 12], [0, 5, 9, 16, 16]),         # decode kernel (<= 16 rows per expert)
+], ids=["tiles256", "decode"])
+def test_expert_up_gather_bad_perm_entries(T, d, F, E, k, bad, offsets):
     """perm entries inside a segment that name no token (negative, or
     token >= T) read zero rows: H = gelu(0) = 0 there; the rest is exact."""
-    T, d, F, E, k = 130, 128, 192, 2, 2
     inp = workloads.random_case(23, T, d, E, k, F, "bf16", -1, 0.0, w_scale=0.05)
     cfg = moe.config(T, d, F, E, k, -1, "bf16")
     assert moe.moe_expert_up_gather_supported(cfg)
     Tk = T * k
     perm_np = np.random.default_rng(3).permutation(Tk).astype(np.int32)
-    bad = np.array([0, 5, 100, 200, 259])
+    bad = np.array(bad)
     perm_np[bad] = np.array([-1, T * k, T * k + 7, -(1 << 30), 2 ** 31 - 1], dtype=np.int64).astype(np.int32)
-    offsets_np = np.array([0, 150, Tk], dtype=np.int32)
+    offsets_np = np.array(offsets, dtype=np.int32)
     X = to_dev(inp.X, "bf16")
     W1 = to_dev(inp.W1, "bf16")
     H = torch.full((Tk, F), 3.0, dtype=torch.bfloat16, device="cuda")
