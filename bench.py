@@ -37,16 +37,16 @@ METRIC = "MoE-layer tokens/sec at 1 GPU; % bf16 MFMA peak (FFN) / % HBM peak (re
 # WRITE_SIZE (KiB per dispatch), scaled by what the same counters read for a
 # plain 1 GiB device copy (FETCH_SIZE x2.0, WRITE_SIZE x1.0); valid only for
 # the GEMM source they were taken on (sha1 prefix), else reported as null.
-TRAFFIC_SOURCE_SHA1 = "437a9341a2c2"
+TRAFFIC_SOURCE_SHA1 = "99bae6925e6f"
 TRAFFIC_BYTES = {  # (workload, stage) -> (fetch KiB, write KiB) per dispatch, raw counter values
-    ("prefill", "expert_up"): (479448.2, 180225.7),
-    ("prefill", "expert_down"): (784472.2, 65536.2),
-    ("capacity", "expert_up"): (838897.8, 285269.8),
-    ("capacity", "expert_down"): (699457.7, 415661.9),
-    ("skewed", "expert_up"): (7314474.9, 918633.2),
-    ("skewed", "expert_down"): (6472589.0, 262178.4),
-    ("decode", "expert_up"): (122940.3, 80.0),
-    ("decode", "expert_down"): (122812.5, 112.0),
+    ("prefill", "expert_up"): (476088.9, 180226.3),
+    ("prefill", "expert_down"): (802335.4, 65536.2),
+    ("capacity", "expert_up"): (830483.9, 285269.4),
+    ("capacity", "expert_down"): (717762.6, 415605.1),
+    ("skewed", "expert_up"): (7229923.1, 918933.6),
+    ("skewed", "expert_down"): (6423522.8, 262171.6),
+    ("decode", "expert_up"): (122723.7, 80.0),
+    ("decode", "expert_down"): (122812.6, 112.0),
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 
@@ -65,8 +65,8 @@ def gemm_traffic(workload, stage):
 def gemm_kernel_name(w, capacity, stage, gathers):
     """The expert-GEMM kernel the library runs for this shape (its selection
     rule: bf16 with at most min(T, C) rows per expert picks the few-rows
-    kernels; the up-projection of the 256x256 kernel gathers X through perm
-    where moe_expert_up_gather_supported says so)."""
+    kernels; the up-projection of the 256x256 and decode kernels gathers X
+    through perm where moe_expert_up_gather_supported says so)."""
     gelu = "true" if stage == "expert_up" else "false"
     K = w.d if stage == "expert_up" else w.F
     N = w.F if stage == "expert_up" else w.d
@@ -74,7 +74,8 @@ def gemm_kernel_name(w, capacity, stage, gathers):
         return f"grouped_gemm_kernel<float, 64, 64, 2, 2, {gelu}>"
     bound = w.T if capacity < 0 else min(w.T, capacity)
     if K % 128 == 0 and N % 8 == 0 and bound <= 16:
-        return f"grouped_gemm_bf16_gemv<{gelu}, {1 if bound <= 4 else 2 if bound <= 8 else 4}>"
+        g = 1 if bound <= 4 else 2 if bound <= 8 else 4
+        return f"grouped_gemm_bf16_gemv<{gelu}, {g}, {'true' if gathers and stage == 'expert_up' else 'false'}>"
     if bound <= 64:
         return f"grouped_gemm_bf16_skinny<{gelu}, {1 if bound <= 16 else 2 if bound <= 32 else 4}>"
     return f"grouped_gemm_bf16_256<{gelu}, {'true' if gathers and stage == 'expert_up' else 'false'}>"
