@@ -37,6 +37,10 @@ CASES = [
     # (an n-tile of 64 valid weight rows), experts of a few hundred rows
     ("big_d64_f64", 700, 64, 4, 2, 64, "bf16", -1, 0.0),
     ("big_e1_k1", 300, 128, 1, 1, 192, "bf16", -1, 0.0),
+    # more than 8 slots per token (the general dispatch's wide-k path), up to k = E = 64
+    ("k16_e32", 400, 128, 32, 16, 128, "bf16", -1, 0.3),
+    ("k12_cap", 300, 128, 24, 12, 128, "bf16", 100, 0.5),
+    ("k64_e64", 40, 128, 64, 64, 64, "bf16", -1, 0.0),
 ]
 IDS = [c[0] for c in CASES]
 
@@ -92,7 +96,8 @@ def test_route_many_tokens(T, d, E, k):
 
 
 STATS_CASES = [c for c in CASES if c[0] in ("tiny_like", "ragged_bf16", "e64_tail", "cap_k4", "f32_e5_k3", "bf16_e3_k1",
-                                            "decode_like_splitk", "splitk_e24_f32", "single_token")]
+                                            "decode_like_splitk", "splitk_e24_f32", "single_token", "k16_e32",
+                                            "k64_e64")]
 
 
 def _route_stats_dev(cfg, X, Wg, bias, tau, T, E, k):

@@ -29,6 +29,9 @@ CASES = [
     ("dropless", 300, 128, 8, 2, 128, "bf16", -1, 0.5),
     # a gate too large for LDS (E = 64, d = 4096): the global-memory router writes the order
     ("e64_d4096", 700, 4096, 64, 2, 128, "bf16", 30, 1.0),
+    # more than 8 slots per token: 12 of 24 experts, and 16 of 64 with a tight capacity
+    ("k12_e24", 300, 128, 24, 12, 128, "bf16", 100, 0.5),
+    ("k16_e64", 400, 128, 64, 16, 128, "bf16", 60, 1.0),
 ]
 IDS = [c[0] for c in CASES]
 
