@@ -501,6 +501,27 @@ def test_forward(case):
     assert torch.equal(first, layer.buf.out)
 
 
+@pytest.mark.parametrize("T,d,E,k,F", [(300, 128, 8, 2, 128), (8, 1024, 16, 2, 256)], ids=["tiles256", "decode"])
+def test_layer_with_saturating_gelu(T, d, E, k, F):
+    """Hidden states 40x larger than the workloads': the pre-activations
+    reach |h| of 20 and more, where the GELU's exponential overflows or
+    underflows (the tanh form's limits x and -0); the layer still matches the
+    oracle, and no output is inf or NaN."""
+    inp = workloads.random_case(91 + T, T, d, E, k, F, "bf16", -1, 0.0, x_scale=40.0, w_scale=0.05)
+    cfg = moe.config(T, d, F, E, k, -1, "bf16")
+    out_ref, r, _ = oracle_all(inp)
+    layer = moe.MoELayer(cfg, to_dev(inp.Wg, "bf16"), to_dev(inp.W1, "bf16"), to_dev(inp.W2, "bf16"))
+    out = layer.forward(to_dev(inp.X, "bf16"))
+    torch.cuda.synchronize()
+    got = dev_to_f64(out)
+    assert np.isfinite(got).all()
+    pre = oracle.as_f64(inp.X, "bf16") @ oracle.as_f64(inp.W1[0], "bf16").T
+    assert np.abs(pre).max() > 20.0  # the saturating range is exercised
+    diff = check_routing(layer.buf.topk_ids.cpu().numpy(), layer.buf.topk_w.cpu().numpy(), r)
+    err = row_rel_err(got, out_ref)
+    assert err[~diff].max() <= rel_tol("bf16"), f"layer rel err {err[~diff].max():.3g}"
+
+
 def test_empty_input():
     cfg = moe.config(0, 128, 128, 8, 2, -1, "bf16")
     E = 8
