@@ -73,6 +73,45 @@ def test_route(case):
     assert np.max(np.abs(tw.cpu().numpy().sum(1) - 1)) < 1e-5
 
 
+@pytest.mark.parametrize("T,d,E,k,dt", [(500, 256, 16, 3, "bf16"), (8, 1024, 64, 2, "bf16"), (200, 128, 40, 4, "f32"),
+                                        (20000, 2048, 64, 2, "bf16")],
+                         ids=["lds_router", "splitk", "f32", "gate_in_l2"])
+def test_route_exact_ties_go_to_lower_id(T, d, E, k, dt):
+    """Experts 3 and 5 (and 7) get the same gate column, so their logits are
+    equal bit for bit on every token: the tie rule (lower id first) must
+    decide, and the slot order must follow it, on each router path."""
+    inp = workloads.random_case(5 + T, T, d, E, k, 64, dt, -1, 0.0, w_scale=0.05)
+    Wg = np.array(inp.Wg, copy=True)
+    if dt == "bf16":  # the shared column, 4x stronger so it often leads (bf16: scale the widened values)
+        col = oracle.as_f64(Wg[:, 3:4], dt).astype(np.float32) * 4.0
+        Wg[:, 3] = (col.view(np.uint32)[:, 0] >> 16).astype(np.uint16)  # exact: a power-of-two scale
+    else:
+        Wg[:, 3] *= 4.0
+    Wg[:, 5] = Wg[:, 3]
+    Wg[:, 7] = Wg[:, 3]
+    cfg = moe.config(T, d, 64, E, k, -1, dt)
+    X, Wgd = to_dev(inp.X, dt), to_dev(Wg, dt)
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    tw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    rws = torch.empty(max(1, moe.moe_workspace_size(cfg, moe.MOE_OP_ROUTE)), dtype=torch.uint8, device="cuda")
+    moe.moe_route(cfg, X, Wgd, None, ids, tw, rws)
+    torch.cuda.synchronize()
+    got = ids.cpu().numpy()
+    tied = 0
+    for t in range(T):
+        row = list(got[t])
+        for hi in (5, 7):
+            if hi in row:
+                tied += 1
+                assert 3 in row and row.index(3) < row.index(hi), f"token {t}: {row}"
+        if 7 in row:
+            assert 5 in row and row.index(5) < row.index(7), f"token {t}: {row}"
+    assert tied > 0  # the tie was reached on some tokens
+    # and away from the tie the ids are the oracle's
+    r = oracle.route(oracle.as_f64(inp.X, dt), oracle.as_f64(Wg, dt), None, k)
+    check_routing(got, tw.cpu().numpy(), r)
+
+
 @pytest.mark.parametrize("T,d,E,k", [(12000, 256, 16, 2), (40000, 128, 8, 2), (9000, 128, 40, 3), (5000, 256, 5, 2),
                                      (20000, 2048, 32, 2), (17000, 2048, 64, 2), (16400, 1536, 50, 3)],
                          ids=["t12000_rows4", "t40000_two_passes", "e40_nt3", "e5_gathered_gate", "t20000_d2048",
