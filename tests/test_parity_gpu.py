@@ -107,6 +107,14 @@ def test_route_exact_ties_go_to_lower_id(T, d, E, k, dt):
         if 7 in row:
             assert 5 in row and row.index(5) < row.index(7), f"token {t}: {row}"
     assert tied > 0  # the tie was reached on some tokens
+    # the full preference order puts the three tied experts next to each other, lower id first
+    order = torch.empty((T, E), dtype=torch.uint8, device="cuda")
+    ids2, tw2 = torch.empty_like(ids), torch.empty_like(tw)
+    moe.moe_route_ranked(cfg, X, Wgd, None, ids2, tw2, order, rws)
+    torch.cuda.synchronize()
+    assert torch.equal(ids2, ids) and torch.equal(tw2, tw)
+    pos = np.argsort(order.cpu().numpy().astype(np.int64), axis=1)  # pos[t, e]: place of expert e
+    assert ((pos[:, 5] == pos[:, 3] + 1) & (pos[:, 7] == pos[:, 3] + 2)).all()
     # and away from the tie the ids are the oracle's
     r = oracle.route(oracle.as_f64(inp.X, dt), oracle.as_f64(Wg, dt), None, k)
     check_routing(got, tw.cpu().numpy(), r)
