@@ -569,6 +569,25 @@ def test_layer_with_saturating_gelu(T, d, E, k, F):
     assert err[~diff].max() <= rel_tol("bf16"), f"layer rel err {err[~diff].max():.3g}"
 
 
+@pytest.mark.parametrize("T,d,E,k,F", [(600, 128, 8, 2, 192), (40, 1024, 16, 3, 256)], ids=["tiles256", "few_rows"])
+def test_capacity_above_every_load_is_dropless(T, d, E, k, F):
+    """A capacity no expert reaches (C = T) drops nothing: the capacity
+    dispatch, with or without rerouting, gives the dropless layer's rows and
+    output bit for bit."""
+    inp = workloads.random_case(61 + T, T, d, E, k, F, "bf16", -1, 0.5, w_scale=0.05)
+    dev = dict(Wg=to_dev(inp.Wg, "bf16"), W1=to_dev(inp.W1, "bf16"), W2=to_dev(inp.W2, "bf16"),
+               gate_bias=to_dev(inp.bias, "f32"))
+    X = to_dev(inp.X, "bf16")
+    outs = []
+    for cap, reroute in ((-1, False), (T, False), (T, True)):
+        layer = moe.MoELayer(moe.config(T, d, F, E, k, cap, "bf16"), reroute=reroute, **dev)
+        outs.append((layer.forward(X).clone(), layer.buf.perm.clone(), layer.buf.expert_offsets.clone()))
+    torch.cuda.synchronize()
+    for o, p, off in outs[1:]:
+        assert torch.equal(off, outs[0][2]) and torch.equal(p, outs[0][1])
+        assert torch.equal(o, outs[0][0])
+
+
 def test_empty_input():
     cfg = moe.config(0, 128, 128, 8, 2, -1, "bf16")
     E = 8
