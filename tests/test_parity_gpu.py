@@ -588,6 +588,25 @@ def test_capacity_above_every_load_is_dropless(T, d, E, k, F):
         assert torch.equal(o, outs[0][0])
 
 
+@pytest.mark.parametrize("T,d,E,k,F,cap", [(700, 256, 16, 2, 320, -1), (8, 1024, 64, 2, 256, -1),
+                                           (500, 128, 8, 4, 192, -1)], ids=["tiles256", "decode", "k4"])
+def test_token_permutation_equivariance(T, d, E, k, F, cap):
+    """Dropless, every token's output depends on that token alone, and each
+    row's arithmetic (its K order, its tile's kernel) does not depend on where
+    the token sits: permuting the tokens permutes the outputs bit for bit."""
+    inp = workloads.random_case(71 + T, T, d, E, k, F, "bf16", cap, 0.3, w_scale=0.05)
+    layer = moe.MoELayer(moe.config(T, d, F, E, k, cap, "bf16"), to_dev(inp.Wg, "bf16"), to_dev(inp.W1, "bf16"),
+                         to_dev(inp.W2, "bf16"), to_dev(inp.bias, "f32"))
+    X = to_dev(inp.X, "bf16")
+    out = layer.forward(X).clone()
+    ids = layer.buf.topk_ids.clone()
+    p = torch.from_numpy(np.random.default_rng(4).permutation(T)).cuda()
+    out_p = layer.forward(X[p].contiguous()).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(layer.buf.topk_ids, ids[p])
+    assert torch.equal(out_p, out[p])
+
+
 def test_empty_input():
     cfg = moe.config(0, 128, 128, 8, 2, -1, "bf16")
     E = 8
