@@ -607,6 +607,30 @@ def test_token_permutation_equivariance(T, d, E, k, F, cap):
     assert torch.equal(out_p, out[p])
 
 
+@pytest.mark.parametrize("T,d,E,k,F,cap", [(700, 256, 16, 2, 320, -1), (8, 1024, 64, 2, 256, -1),
+                                           (900, 128, 8, 2, 192, 150)], ids=["tiles256", "decode", "capacity"])
+def test_expert_relabelling_equivariance(T, d, E, k, F, cap):
+    """Relabelling the experts (gate columns, bias and expert weights by one
+    permutation) relabels the selected ids and leaves the output unchanged,
+    bit for bit (no ties in random logits; a row's arithmetic does not depend
+    on its expert's index)."""
+    inp = workloads.random_case(81 + T, T, d, E, k, F, "bf16", cap, 0.3, w_scale=0.05)
+    q = np.random.default_rng(6).permutation(E)  # new expert j is old expert q[j]
+    cfg = moe.config(T, d, F, E, k, cap, "bf16")
+    X = to_dev(inp.X, "bf16")
+    a = moe.MoELayer(cfg, to_dev(inp.Wg, "bf16"), to_dev(inp.W1, "bf16"), to_dev(inp.W2, "bf16"),
+                     to_dev(inp.bias, "f32"))
+    b = moe.MoELayer(cfg, to_dev(np.ascontiguousarray(inp.Wg[:, q]), "bf16"),
+                     to_dev(np.ascontiguousarray(inp.W1[q]), "bf16"), to_dev(np.ascontiguousarray(inp.W2[q]), "bf16"),
+                     to_dev(np.ascontiguousarray(inp.bias[q]), "f32"))
+    out_a = a.forward(X).clone()
+    out_b = b.forward(X).clone()
+    torch.cuda.synchronize()
+    inv = np.argsort(q)  # old expert e is new expert inv[e]
+    assert (b.buf.topk_ids.cpu().numpy() == inv[a.buf.topk_ids.cpu().numpy()]).all()
+    assert torch.equal(out_a, out_b)
+
+
 def test_empty_input():
     cfg = moe.config(0, 128, 128, 8, 2, -1, "bf16")
     E = 8
