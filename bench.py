@@ -1,11 +1,15 @@
 """Benchmark of the sparse MoE FFN layer forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|decode|skewed|capacity|tiny]
-                    [--reroute]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload skewed|prefill|decode|capacity|tiny]
+                    [--reroute] [--no-others]
 
 A step is one moe_forward (router, dispatch, expert GEMM1+GELU, GEMM2,
 combine) over one batch of seeded synthetic inputs that are resident in HBM
-before the timed region starts.  --reroute times moe_forward_reroute
+before the timed region starts.  The default workload is the largest one a
+single GPU holds: T = 16384 tokens, d = 4096, E = 64, k = 2, F = 14336 with a
+Zipf-skewed router bias.  Unless --no-others is given, the prefill,
+capacity-limited and decode workloads are then measured the same way (without
+the CPU baseline) and reported under "other_workloads".  --reroute times moe_forward_reroute
 instead: pairs over the expert capacity move to their token's next-best
 expert with room rather than being dropped.  The headline times K steps captured in one
 HIP graph and replayed.  Each stage entry point is then timed on its own: K
@@ -84,9 +88,11 @@ def gemm_kernel_name(w, capacity, stage, gathers):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 20; decode-sized workloads: their step count, 100)")
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="prefill")
+    ap.add_argument("--workload", default="skewed")
+    ap.add_argument("--no-others", action="store_true", help="measure only --workload")
     ap.add_argument("--cpu-sample", type=int, default=None, help="tokens (prefill-like) or steps (decode) for the oracle")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--eager", action="store_true",
@@ -123,8 +129,23 @@ def stage_work(w, N, active, es, gathers, reroute=False):
     }
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, inp, sample, reroute=False):
-    """The oracle, as it stands, on a bounded sample of the workload."""
+    """The oracle, as it stands, on a bounded sample of the workload: the
+    first `sample` tokens as one batch with the full expert weights (a
+    prefill-like workload; default 512 tokens), or `sample` decode steps
+    (default 4).  The sample is repeated until at least 10 s (at most about
+    30 s) of CPU work has been timed."""
     import oracle
     import workloads
     try:
@@ -132,7 +153,6 @@ def cpu_baseline(w, inp, sample, reroute=False):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    # Repeat the sample until at least 10 s of CPU work (at most 30 s) is timed.
     t0 = time.perf_counter()
     toks, reps = 0, 0
     if w.steps > 1:
@@ -149,7 +169,7 @@ def cpu_baseline(w, inp, sample, reroute=False):
                 break
         desc = f"{reps} x {n} decode steps of {w.T} tokens, full weights"
     else:
-        n = sample or min(w.T, 8192)
+        n = min(sample or 512, w.T)
         cap = (-(-n // w.E) * w.k) if inp.expert_capacity >= 0 else -1
         while True:
             oracle.moe_forward(inp.X[:n], inp.Wg, inp.bias, inp.W1, inp.W2, w.k, cap, w.dtype, reroute=reroute)
@@ -158,114 +178,116 @@ def cpu_baseline(w, inp, sample, reroute=False):
             elapsed = time.perf_counter() - t0
             if elapsed >= 10.0 or elapsed + elapsed / reps > 30.0:
                 break
-        desc = (f"{reps} x first {n} of {w.T} tokens as one batch, full weights"
+        desc = (f"{reps} x first {n} of {w.T} tokens as one batch, full expert weights"
                 + (f", capacity {cap}" if cap >= 0 else "") + (", rerouted" if reroute and cap >= 0 else ""))
     dt = time.perf_counter() - t0
     return {"value": toks / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": desc, "seconds": round(dt, 2)}
+            "sample": desc, "seconds": round(dt, 2), "cpu_model": cpu_model(),
+            "host_cpus": os.cpu_count()}
 
 
-def main():
-    args = parse()
-    if args.calibrate_copy:
-        import torch
-        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes": src.numel() * 4, "copies": 5}))
-        return
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus N>1 is not supported",
-                          "n_gpus": args.gpus}))
-        sys.exit(2)
-    import torch
+def rotation_sets(w, T, d, F, k, es):
+    """How many input sets the per-stage timings rotate over: enough that
+    the smallest per-set input of a stage (the hidden states X, read by the
+    router) summed over the sets exceeds 1 GiB, four times the 256 MB
+    last-level (MALL) cache, so no stage time is served from it; at least 4,
+    at most 32."""
+    per_set = T * d * es
+    return int(min(32, max(4, -(-(1 << 30) // max(per_set, 1)))))
 
-    import sparse_mixture_experts_04_amd as moe
-    import workloads
 
-    w = workloads.WORKLOADS[args.workload]
+def measure(torch, moe, workloads, name, steps, warmup, eager=False, reroute=False, with_cpu=False,
+            cpu_sample=None):
+    """Measure one workload: the whole-layer step rate, the per-stage kernel
+    times and the roofline of the dominant expert GEMM."""
+    w = workloads.WORKLOADS[name]
     t_gen = time.perf_counter()
     inp = workloads.generate(w)
     gen_s = time.perf_counter() - t_gen
     dt = w.dtype
     es = 2 if dt == "bf16" else 4
+    if steps is None:
+        steps = w.steps if w.steps > 1 else 20
     cfg = moe.config(w.T, w.d, w.F, w.E, w.k, inp.expert_capacity, dt)
     Wg, W1, W2 = to_dev(torch, inp.Wg, dt), to_dev(torch, inp.W1, dt), to_dev(torch, inp.W2, dt)
     bias = to_dev(torch, inp.bias, "f32")
     if w.steps > 1:
         xs = [to_dev(torch, workloads.decode_step_inputs(w, s), dt) for s in range(w.steps)]
     else:
-        xs = [to_dev(torch, inp.X, dt)]
-    reroute = bool(args.reroute)
+        # Rotated copies of the one batch: the same tokens in another order
+        # (the layer is equivariant under token permutations, so each copy
+        # does the same work) at other addresses, for the stage timings.
+        X0 = to_dev(torch, inp.X, dt)
+        nrot = rotation_sets(w, w.T, w.d, w.F, w.k, es)
+        xs = [X0] + [torch.roll(X0, shifts=(i * w.T) // nrot, dims=0).contiguous() for i in range(1, nrot)]
+    reroute = bool(reroute)
     layer = moe.MoELayer(cfg, Wg, W1, W2, bias, reroute=reroute)
     b = layer.buf
     stream = torch.cuda.current_stream()
 
-    for i in range(args.warmup):
-        layer.forward(xs[i % len(xs)])
+    # Whole-layer steps step through the decode steps' fresh hidden states;
+    # a prefill-like layer repeats its one batch.
+    step_x = xs if w.steps > 1 else xs[:1]
+    for i in range(warmup):
+        layer.forward(step_x[i % len(step_x)])
     torch.cuda.synchronize()
 
-    # ---- headline: K whole-layer steps.  Eager: K moe_forward calls.  Graph
-    # (default): the same K calls captured once into a HIP graph and replayed,
-    # so host launch overhead is off the GPU's critical path.
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
-    def timed(run):
+    def timed(run, n):
         torch.cuda.synchronize()
         w0 = time.perf_counter()
         ev0.record(stream)
         run()
         ev1.record(stream)
         torch.cuda.synchronize()
-        return ev0.elapsed_time(ev1) / args.steps, time.perf_counter() - w0
+        return ev0.elapsed_time(ev1) / n, time.perf_counter() - w0
 
     def eager_steps():
-        for i in range(args.steps):
-            layer.forward(xs[i % len(xs)])
+        for i in range(steps):
+            layer.forward(step_x[i % len(step_x)])
 
-    eager_ms, eager_wall = timed(eager_steps)
+    eager_ms, eager_wall = timed(eager_steps, steps)
     graph_ms = None
-    if not args.eager:
+    if not eager:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             eager_steps()
         graph.replay()  # untimed replay
         torch.cuda.synchronize()
-        graph_ms, graph_wall = timed(graph.replay)
+        graph_ms, graph_wall = timed(graph.replay, steps)
         stream = torch.cuda.current_stream()
+        del graph
     ms_step, wall = (eager_ms, eager_wall) if graph_ms is None else (graph_ms, graph_wall)
 
     # ---- per-stage kernel times: each stage entry point is launched K times
     # back to back between two HIP events on the launch stream, so the queue
     # stays full and the interval is the kernels' own time (no host gaps).
-    # Inputs come from forwards of the benchmark's own batches; for
-    # decode-sized layers the stages rotate over up to 4 routings of
-    # consecutive batches, so the expert weights streamed change from launch
-    # to launch as they do in decoding.
+    # The launches rotate over several input sets prepared by forwards of the
+    # benchmark's own batches (decode: consecutive steps, so the expert
+    # weights streamed change from launch to launch; prefill-like: the
+    # rotated copies, so activations are not served from the last-level
+    # cache).
     names = ["route", "dispatch", "expert_up", "expert_down", "combine"]
     rws, rbytes = b.scratch_view(cfg, "route"), moe.moe_workspace_size(cfg, moe.MOE_OP_ROUTE)
     dws = b.scratch_view(cfg, "dispatch")
     dbytes = moe.moe_workspace_size(cfg, moe.MOE_OP_DISPATCH_REROUTE if reroute else moe.MOE_OP_DISPATCH)
     Xp_ws, H_ws, Yp_ws = b.workspace_view(cfg, "Xp"), b.workspace_view(cfg, "H"), b.workspace_view(cfg, "Yp")
-    small = w.T * w.k * max(w.d, w.F) * es <= (64 << 20)
-    nsets = min(4, len(xs)) if small else 1
+    nsets = min(len(xs), 4) if w.steps > 1 else len(xs)
+    gathers = moe.moe_expert_up_gather_supported(cfg)
     sets, per_step_N, per_step_active = [], [], []
     for si in range(nsets):
         layer.forward(xs[si])
         torch.cuda.synchronize()
-        keep = (lambda t: t.clone()) if nsets > 1 else (lambda t: t)
-        sets.append({"X": xs[si], "ids": keep(b.topk_ids), "w": keep(b.topk_w), "off": keep(b.expert_offsets),
-                     "order": keep(b.expert_order) if reroute else None,
-                     "inv": keep(b.inv_perm), "perm": keep(b.perm), "Xp": keep(Xp_ws), "H": keep(H_ws),
-                     "Yp": keep(Yp_ws)})
+        sets.append({"X": xs[si], "ids": b.topk_ids.clone(), "w": b.topk_w.clone(), "off": b.expert_offsets.clone(),
+                     "order": b.expert_order.clone() if reroute else None,
+                     "inv": b.inv_perm.clone(), "perm": b.perm.clone(),
+                     "Xp": None if gathers else Xp_ws.clone(), "H": H_ws.clone(), "Yp": Yp_ws.clone()})
         off = b.expert_offsets.cpu().numpy()
         per_step_N.append(int(off[-1]))
         per_step_active.append(int((np.diff(off) > 0).sum()))
     # The stages as moe_forward runs them: where the up-projection gathers X
     # through perm, the dispatch writes indices only.
-    gathers = moe.moe_expert_up_gather_supported(cfg)
     stage_fn = {
         "route": lambda q: moe.moe_route(cfg, q["X"], Wg, bias, b.topk_ids, b.topk_w, rws, rbytes),
         "dispatch": lambda q: moe.moe_dispatch(cfg, q["ids"], q["X"], b.expert_counts, b.expert_offsets, b.perm,
@@ -282,10 +304,11 @@ def main():
             cfg, q["ids"], q["order"], q["X"], b.expert_counts, b.expert_offsets, b.perm, b.inv_perm,
             None if gathers else Xp_ws, dws, dbytes)
     stage_ms = {}
+    nst = max(steps, nsets)
     for n in names:
         fn = stage_fn[n]
         fn(sets[0])  # untimed
-        stage_ms[n], _ = timed(lambda: [fn(sets[i % nsets]) for i in range(args.steps)])
+        stage_ms[n], _ = timed(lambda: [fn(sets[i % nsets]) for i in range(nst)], nst)
 
     N = float(np.mean(per_step_N))
     active = float(np.mean(per_step_active))
@@ -316,46 +339,105 @@ def main():
     roof["ms"] = round(ms, 5)
 
     cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline(w, inp, args.cpu_sample, reroute)
+    if with_cpu:
+        cpu = cpu_baseline(w, inp, cpu_sample, reroute)
         if w.name == "tiny":
             # The tiny layer's oracle also on one core (BLAS limited to one thread).
             from threadpoolctl import threadpool_limits
             with threadpool_limits(limits=1):
-                one = cpu_baseline(w, inp, args.cpu_sample, reroute)
+                one = cpu_baseline(w, inp, cpu_sample, reroute)
             one["cores"] = 1
             cpu["one_core"] = one
 
-    tok_per_step = w.T
-    line = {
-        "metric": METRIC,
-        "value": round(tok_per_step / (ms_step / 1e3), 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+    res = {
+        "value": round(w.T / (ms_step / 1e3), 1),
+        "steps": steps,
         "ms_per_step": round(ms_step, 5),
         "timing": "hip-graph replay of the K steps" if graph_ms is not None else "eager launches",
         "eager_ms_per_step": round(eager_ms, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": dt,
-        "data": "synthetic (seeded; random-init weights of the stated shapes)",
-        "config": {"workload": w.name + ("_rerouted" if reroute and inp.expert_capacity >= 0 else ""), "T": w.T, "d": w.d, "E": w.E, "k": w.k, "F": w.F,
-                   "expert_capacity": inp.expert_capacity,
+        "config": {"workload": w.name + ("_rerouted" if reroute and inp.expert_capacity >= 0 else ""), "T": w.T,
+                   "d": w.d, "E": w.E, "k": w.k, "F": w.F, "expert_capacity": inp.expert_capacity,
                    "over_capacity": ("rerouted" if reroute else "dropped") if inp.expert_capacity >= 0 else "none",
-                   "bias": w.bias, "seed": w.seed,
-                   "parallelism": "single GPU, all experts resident"},
+                   "bias": w.bias, "seed": w.seed, "parallelism": "single GPU, all experts resident"},
+        "dtype": dt,
         "roofline": roof,
         "cpu_baseline": cpu,
         "stages": stages,
+        "stage_input_sets": nsets,
         "kept_pairs": N,
         "active_experts": active,
         "wall_s_timed_region": round(wall, 4),
         "input_gen_s": round(gen_s, 2),
     }
-    print(json.dumps(line))
+    del layer, sets, xs, W1, W2
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse()
+    if args.calibrate_copy:
+        import torch
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": src.numel() * 4, "copies": 5}))
+        return
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus N>1 is not supported",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import sparse_mixture_experts_04_amd as moe
+    import workloads
+
+    head = measure(torch, moe, workloads, args.workload, args.steps, args.warmup, eager=args.eager,
+                   reroute=args.reroute, with_cpu=not args.no_cpu, cpu_sample=args.cpu_sample)
+    print(f"[bench] {head['config']['workload']}: {head['value']:.1f} tokens/s, "
+          f"{head['roofline']['kernel']} at {head['roofline']['frac']:.4f} of peak", file=sys.stderr, flush=True)
+    others = {}
+    if not args.no_others and not args.reroute and args.workload == "skewed":
+        for name in ("prefill", "capacity", "decode"):
+            r = measure(torch, moe, workloads, name, None, args.warmup, eager=args.eager)
+            others[name] = {k: r[k] for k in ("value", "ms_per_step", "steps", "roofline", "stages", "kept_pairs",
+                                              "active_experts", "stage_input_sets")}
+            others[name]["unit"] = "tokens/s"
+            others[name]["config"] = r["config"]
+            print(f"[bench] {name}: {r['value']:.1f} tokens/s, {r['roofline']['kernel']} at "
+                  f"{r['roofline']['frac']:.4f} of peak", file=sys.stderr, flush=True)
+
+    line = {
+        "metric": METRIC,
+        "value": head["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": head["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "timing": head["timing"],
+        "eager_ms_per_step": head["eager_ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head["dtype"],
+        "data": "synthetic (seeded; random-init weights of the stated shapes)",
+        "config": head["config"],
+        "roofline": head["roofline"],
+        "cpu_baseline": head["cpu_baseline"],
+        "stages": head["stages"],
+        "stage_input_sets": head["stage_input_sets"],
+        "kept_pairs": head["kept_pairs"],
+        "active_experts": head["active_experts"],
+        "wall_s_timed_region": head["wall_s_timed_region"],
+        "input_gen_s": head["input_gen_s"],
+    }
+    if others:
+        line["other_workloads"] = others
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

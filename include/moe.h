@@ -109,7 +109,8 @@ moe_status moe_workspace_size(const moe_config* cfg, int32_t op, size_t* bytes);
  *   X [T, d], Wg [d, E] (dtype), gate_bias [E] float or NULL (a per-expert
  *   logit bias, the domain bias of mlqm §6).
  *   topk_ids [T, k] int32 out: slot 0 holds the most probable expert; slots in
- *   descending probability; equal logits go to the lower expert id.
+ *   descending probability; equal logits go to the lower expert id.  A NaN
+ *   logit ranks as -inf, so the k ids are always distinct experts.
  *   topk_w [T, k] float out: p_s / sum_j p_j over the k selected experts.
  *   ws / ws_bytes: workspace of moe_workspace_size(cfg, MOE_OP_ROUTE) bytes:
  *   the gate transposed to [16*ceil(E/16), d] and, when T is small (the gate
@@ -180,13 +181,19 @@ moe_status moe_expert_up_gather(const moe_config* cfg, const void* X, const int3
  * part of its workspace unwritten. */
 moe_status moe_expert_up_gather_supported(const moe_config* cfg, int32_t* supported);
 
-/* Expert down-projection: Yp[r] = W2[e] H[r] (the second Linear).
- * H [T*k, F], W2 [E, d, F] in; Yp [T*k, d] out (rows >= N untouched). */
+/* Expert down-projection: Yp[r] = W2[e] H[r] for every row r of expert e's
+ * segment [offsets[e], offsets[e+1]): the second Linear of each expert's
+ * Linear -> GELU -> Linear FFN [mlqm §2.2: every expert is a standard FFN;
+ * wmrh §2.2: Linear-GELU-Linear], run only on the rows dispatched to it
+ * [mlqm §3.2 step 4].  H [T*k, F], W2 [E, d, F] in; Yp [T*k, d] out (rows
+ * >= N untouched).  expert_offsets [E+1] is read on the device. */
 moe_status moe_expert_down(const moe_config* cfg, const void* H, const int32_t* expert_offsets,
                            const void* W2, void* Yp, void* stream);
 
-/* Both expert projections: Yp[r] = W2[e] gelu(W1[e] Xp[r]); H lives in ws
- * (moe_workspace_size(cfg, MOE_OP_EXPERT_FFN)). */
+/* Both expert projections: Yp[r] = W2[e] gelu(W1[e] Xp[r]), the whole
+ * expert FFN of every dispatched row [mlqm §2.2; wmrh §2.2: Linear-GELU-
+ * Linear; mlqm §3.2 step 4: each expert runs on its own tokens].  H lives in
+ * ws (moe_workspace_size(cfg, MOE_OP_EXPERT_FFN)). */
 moe_status moe_expert_ffn(const moe_config* cfg, const void* Xp, const int32_t* expert_offsets,
                           const void* W1, const void* W2, void* Yp, void* ws, size_t ws_bytes,
                           void* stream);
@@ -231,7 +238,10 @@ moe_status moe_route_ranked(const moe_config* cfg, const void* X, const void* Wg
  * token does not already use (an earlier slot may have moved there); a pair
  * that finds none stays dropped.  Weights are unchanged: a moved pair still
  * carries topk_w[t, s].
- *   topk_ids [T, k], expert_order [T, E] (from moe_route_ranked) in.
+ *   topk_ids [T, k], expert_order [T, E] (from moe_route_ranked) in.  Each
+ *   row of expert_order must be a permutation of [0, E) whose first k
+ *   entries are the token's ids; a byte >= E is never taken as a
+ *   destination.
  *   Outputs as moe_dispatch, under the final assignment: expert_counts holds
  *   the routed counts of topk_ids (before the cut); offsets, perm, inv_perm
  *   and Xp group the computed pairs by the expert they end at, rows ordered

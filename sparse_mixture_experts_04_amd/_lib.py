@@ -127,6 +127,36 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+def _layer_dtype(cfg) -> torch.dtype:
+    return torch.bfloat16 if cfg.dtype == MOE_BF16 else torch.float32
+
+
+def _arg(fn: str, name: str, t, dtype, numel: int) -> None:
+    """Check one buffer before its pointer goes to the library, which
+    cannot see sizes: a tensor must live on the GPU, be contiguous, have the
+    element type moe.h documents and hold at least the elements it
+    documents.  None (checked by the library) and raw integer pointers (the
+    caller's responsibility) pass unchanged, as does any buffer of a call
+    that reads or writes nothing (numel 0)."""
+    if t is None or isinstance(t, int) or numel <= 0:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{fn}: {name} must be a torch.Tensor, an int pointer or None, not {type(t).__name__}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{fn}: {name} must be a GPU tensor, got device {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{fn}: {name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{fn}: {name} must have dtype {dtype}, got {t.dtype}")
+    if t.numel() < numel:
+        raise ValueError(f"{fn}: {name} holds {t.numel()} elements, needs {numel}")
+
+
+def _dims(cfg):
+    T, k = max(cfg.num_tokens, 0), cfg.num_experts_per_tok
+    return T, cfg.hidden_size, cfg.intermediate_size, cfg.num_experts, k, T * k
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         try:
@@ -136,6 +166,37 @@ def _stream(stream) -> Optional[int]:
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
+
+
+def _route_args(fn, cfg, X, Wg, gate_bias, topk_ids, topk_w):
+    T, d, F, E, k, Tk = _dims(cfg)
+    dt = _layer_dtype(cfg)
+    for name, t, ty, n in (("X", X, dt, T * d), ("Wg", Wg, dt, d * E * (T > 0)),
+                           ("gate_bias", gate_bias, torch.float32, E * (T > 0)),
+                           ("topk_ids", topk_ids, torch.int32, Tk), ("topk_w", topk_w, torch.float32, Tk)):
+        _arg(fn, name, t, ty, n)
+
+
+def _dispatch_args(fn, cfg, topk_ids, X, expert_counts, expert_offsets, perm, inv_perm, Xp):
+    T, d, F, E, k, Tk = _dims(cfg)
+    dt = _layer_dtype(cfg)
+    for name, t, ty, n in (("topk_ids", topk_ids, torch.int32, Tk), ("X", X, dt, T * d),
+                           ("expert_counts", expert_counts, torch.int32, E),
+                           ("expert_offsets", expert_offsets, torch.int32, E + 1),
+                           ("perm", perm, torch.int32, Tk), ("inv_perm", inv_perm, torch.int32, Tk),
+                           ("Xp", Xp, dt, Tk * d)):
+        _arg(fn, name, t, ty, n)
+
+
+def _forward_args(fn, cfg, X, Wg, gate_bias, W1, W2, out, topk_ids, topk_w, expert_counts, expert_offsets, perm,
+                  inv_perm):
+    T, d, F, E, k, Tk = _dims(cfg)
+    dt = _layer_dtype(cfg)
+    _route_args(fn, cfg, X, Wg, gate_bias, topk_ids, topk_w)
+    _dispatch_args(fn, cfg, topk_ids, X, expert_counts, expert_offsets, perm, inv_perm, None)
+    for name, t, ty, n in (("W1", W1, dt, E * F * d * (T > 0)), ("W2", W2, dt, E * d * F * (T > 0)),
+                           ("out", out, dt, T * d)):
+        _arg(fn, name, t, ty, n)
 
 
 def config(T: int, d: int, F: int, E: int, k: int, capacity: int = -1, dtype: str = "bf16") -> MoeConfig:
@@ -159,6 +220,7 @@ def moe_capacity_from_factor(batch: int, seq_len: int, E: int, k: int, factor: f
 
 
 def moe_route(cfg, X, Wg, gate_bias, topk_ids, topk_w, ws=None, ws_bytes=None, stream=None) -> None:
+    _route_args("moe_route", cfg, X, Wg, gate_bias, topk_ids, topk_w)
     if ws_bytes is None:
         ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check("moe_route", LIB.moe_route(ctypes.byref(cfg), _ptr(X), _ptr(Wg), _ptr(gate_bias), _ptr(topk_ids),
@@ -167,6 +229,10 @@ def moe_route(cfg, X, Wg, gate_bias, topk_ids, topk_w, ws=None, ws_bytes=None, s
 
 def moe_route_stats(cfg, X, Wg, gate_bias, temperature, topk_ids, topk_w, prob_mean, sel_freq, aux, ws=None,
                     ws_bytes=None, stream=None) -> None:
+    _route_args("moe_route_stats", cfg, X, Wg, gate_bias, topk_ids, topk_w)
+    E = cfg.num_experts if cfg.num_tokens > 0 else 0
+    for name, t, n in (("prob_mean", prob_mean, E), ("sel_freq", sel_freq, E), ("aux", aux, 1 if E else 0)):
+        _arg("moe_route_stats", name, t, torch.float32, n)
     if ws_bytes is None:
         ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check("moe_route_stats", LIB.moe_route_stats(ctypes.byref(cfg), _ptr(X), _ptr(Wg), _ptr(gate_bias),
@@ -177,6 +243,7 @@ def moe_route_stats(cfg, X, Wg, gate_bias, temperature, topk_ids, topk_w, prob_m
 
 def moe_dispatch(cfg, topk_ids, X, expert_counts, expert_offsets, perm, inv_perm, Xp, ws, ws_bytes=None,
                  stream=None) -> None:
+    _dispatch_args("moe_dispatch", cfg, topk_ids, X, expert_counts, expert_offsets, perm, inv_perm, Xp)
     if ws_bytes is None:
         ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check("moe_dispatch", LIB.moe_dispatch(ctypes.byref(cfg), _ptr(topk_ids), _ptr(X), _ptr(expert_counts),
@@ -185,11 +252,22 @@ def moe_dispatch(cfg, topk_ids, X, expert_counts, expert_offsets, perm, inv_perm
 
 
 def moe_expert_up(cfg, Xp, expert_offsets, W1, H, stream=None) -> None:
+    T, d, F, E, k, Tk = _dims(cfg)
+    dt = _layer_dtype(cfg)
+    for name, t, ty, n in (("Xp", Xp, dt, Tk * d), ("expert_offsets", expert_offsets, torch.int32, (E + 1) * (T > 0)),
+                           ("W1", W1, dt, E * F * d * (T > 0)), ("H", H, dt, Tk * F)):
+        _arg("moe_expert_up", name, t, ty, n)
     _check("moe_expert_up", LIB.moe_expert_up(ctypes.byref(cfg), _ptr(Xp), _ptr(expert_offsets), _ptr(W1), _ptr(H),
                                               _stream(stream)))
 
 
 def moe_expert_up_gather(cfg, X, perm, expert_offsets, W1, H, stream=None) -> None:
+    T, d, F, E, k, Tk = _dims(cfg)
+    dt = _layer_dtype(cfg)
+    for name, t, ty, n in (("X", X, dt, T * d), ("perm", perm, torch.int32, Tk),
+                           ("expert_offsets", expert_offsets, torch.int32, (E + 1) * (T > 0)),
+                           ("W1", W1, dt, E * F * d * (T > 0)), ("H", H, dt, Tk * F)):
+        _arg("moe_expert_up_gather", name, t, ty, n)
     _check("moe_expert_up_gather", LIB.moe_expert_up_gather(ctypes.byref(cfg), _ptr(X), _ptr(perm),
                                                             _ptr(expert_offsets), _ptr(W1), _ptr(H),
                                                             _stream(stream)))
@@ -202,11 +280,22 @@ def moe_expert_up_gather_supported(cfg) -> bool:
 
 
 def moe_expert_down(cfg, H, expert_offsets, W2, Yp, stream=None) -> None:
+    T, d, F, E, k, Tk = _dims(cfg)
+    dt = _layer_dtype(cfg)
+    for name, t, ty, n in (("H", H, dt, Tk * F), ("expert_offsets", expert_offsets, torch.int32, (E + 1) * (T > 0)),
+                           ("W2", W2, dt, E * d * F * (T > 0)), ("Yp", Yp, dt, Tk * d)):
+        _arg("moe_expert_down", name, t, ty, n)
     _check("moe_expert_down", LIB.moe_expert_down(ctypes.byref(cfg), _ptr(H), _ptr(expert_offsets), _ptr(W2),
                                                   _ptr(Yp), _stream(stream)))
 
 
 def moe_expert_ffn(cfg, Xp, expert_offsets, W1, W2, Yp, ws, ws_bytes=None, stream=None) -> None:
+    T, d, F, E, k, Tk = _dims(cfg)
+    dt = _layer_dtype(cfg)
+    for name, t, ty, n in (("Xp", Xp, dt, Tk * d), ("expert_offsets", expert_offsets, torch.int32, (E + 1) * (T > 0)),
+                           ("W1", W1, dt, E * F * d * (T > 0)), ("W2", W2, dt, E * d * F * (T > 0)),
+                           ("Yp", Yp, dt, Tk * d)):
+        _arg("moe_expert_ffn", name, t, ty, n)
     if ws_bytes is None:
         ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check("moe_expert_ffn", LIB.moe_expert_ffn(ctypes.byref(cfg), _ptr(Xp), _ptr(expert_offsets), _ptr(W1),
@@ -214,12 +303,19 @@ def moe_expert_ffn(cfg, Xp, expert_offsets, W1, W2, Yp, ws, ws_bytes=None, strea
 
 
 def moe_combine(cfg, Yp, inv_perm, topk_w, out, stream=None) -> None:
+    T, d, F, E, k, Tk = _dims(cfg)
+    dt = _layer_dtype(cfg)
+    for name, t, ty, n in (("Yp", Yp, dt, Tk * d), ("inv_perm", inv_perm, torch.int32, Tk),
+                           ("topk_w", topk_w, torch.float32, Tk), ("out", out, dt, T * d)):
+        _arg("moe_combine", name, t, ty, n)
     _check("moe_combine", LIB.moe_combine(ctypes.byref(cfg), _ptr(Yp), _ptr(inv_perm), _ptr(topk_w), _ptr(out),
                                           _stream(stream)))
 
 
 def moe_forward(cfg, X, Wg, gate_bias, W1, W2, out, topk_ids, topk_w, expert_counts, expert_offsets, perm,
                 inv_perm, ws, ws_bytes=None, stream=None) -> None:
+    _forward_args("moe_forward", cfg, X, Wg, gate_bias, W1, W2, out, topk_ids, topk_w, expert_counts,
+                  expert_offsets, perm, inv_perm)
     if ws_bytes is None:
         ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check("moe_forward", LIB.moe_forward(ctypes.byref(cfg), _ptr(X), _ptr(Wg), _ptr(gate_bias), _ptr(W1), _ptr(W2),
@@ -230,6 +326,8 @@ def moe_forward(cfg, X, Wg, gate_bias, W1, W2, out, topk_ids, topk_w, expert_cou
 
 def moe_route_ranked(cfg, X, Wg, gate_bias, topk_ids, topk_w, expert_order, ws=None, ws_bytes=None,
                      stream=None) -> None:
+    _route_args("moe_route_ranked", cfg, X, Wg, gate_bias, topk_ids, topk_w)
+    _arg("moe_route_ranked", "expert_order", expert_order, torch.uint8, max(cfg.num_tokens, 0) * cfg.num_experts)
     if ws_bytes is None:
         ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check("moe_route_ranked", LIB.moe_route_ranked(ctypes.byref(cfg), _ptr(X), _ptr(Wg), _ptr(gate_bias),
@@ -239,6 +337,8 @@ def moe_route_ranked(cfg, X, Wg, gate_bias, topk_ids, topk_w, expert_order, ws=N
 
 def moe_dispatch_reroute(cfg, topk_ids, expert_order, X, expert_counts, expert_offsets, perm, inv_perm, Xp, ws,
                          ws_bytes=None, stream=None) -> None:
+    _dispatch_args("moe_dispatch_reroute", cfg, topk_ids, X, expert_counts, expert_offsets, perm, inv_perm, Xp)
+    _arg("moe_dispatch_reroute", "expert_order", expert_order, torch.uint8, max(cfg.num_tokens, 0) * cfg.num_experts)
     if ws_bytes is None:
         ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check("moe_dispatch_reroute", LIB.moe_dispatch_reroute(ctypes.byref(cfg), _ptr(topk_ids), _ptr(expert_order),
@@ -249,6 +349,9 @@ def moe_dispatch_reroute(cfg, topk_ids, expert_order, X, expert_counts, expert_o
 
 def moe_forward_reroute(cfg, X, Wg, gate_bias, W1, W2, out, topk_ids, topk_w, expert_order, expert_counts,
                         expert_offsets, perm, inv_perm, ws, ws_bytes=None, stream=None) -> None:
+    _forward_args("moe_forward_reroute", cfg, X, Wg, gate_bias, W1, W2, out, topk_ids, topk_w, expert_counts,
+                  expert_offsets, perm, inv_perm)
+    _arg("moe_forward_reroute", "expert_order", expert_order, torch.uint8, max(cfg.num_tokens, 0) * cfg.num_experts)
     if ws_bytes is None:
         ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check("moe_forward_reroute", LIB.moe_forward_reroute(ctypes.byref(cfg), _ptr(X), _ptr(Wg), _ptr(gate_bias),

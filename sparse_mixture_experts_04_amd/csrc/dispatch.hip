@@ -457,14 +457,17 @@ __global__ __launch_bounds__(kRerouteThreads) void dispatch_reroute_kernel(
     int pick = kNone;
     if (valid) {
       // Last to first, so the earliest available position wins; the top-k
-      // (and the padding, a copy of position 0) are in `mine`.
+      // (and the padding, a copy of position 0) are in `mine`.  A byte of
+      // the order that names no expert (>= E: a caller's malformed order) is
+      // never available, so every pick indexes the per-expert tables in range.
       const uint64_t avail = ~(full | cur.mine);
       const uint32_t lo = static_cast<uint32_t>(avail), hi = static_cast<uint32_t>(avail >> 32);
 #pragma unroll
       for (int q = NQ - 1; q >= 0; --q) {
         const uint32_t e = __builtin_amdgcn_ubfe(cur.wv[q >> 4][(q >> 2) & 3], (q & 3) * 8, 8);
-        const uint32_t ok = NQ == 32 ? __builtin_amdgcn_ubfe(lo, e, 1)
-                                     : __builtin_amdgcn_ubfe(e < 32 ? lo : hi, e & 31, 1);
+        const uint32_t bit = NQ == 32 ? __builtin_amdgcn_ubfe(lo, e & 31, 1)
+                                      : __builtin_amdgcn_ubfe(e < 32 ? lo : hi, e & 31, 1);
+        const bool ok = bit != 0 && e < static_cast<uint32_t>(E);
         pick = ok ? static_cast<int>(e) : pick;
       }
     }

@@ -113,8 +113,14 @@ __device__ __forceinline__ void topk_tile(f32x4_t (&acc)[NT], const float* __res
   for (int t = 0; t < NT; ++t) {
     const int e = t * 16 + n;
     const float b = (e < E && bias != nullptr) ? bias[e] : 0.f;
+    // A NaN logit ranks as -inf: better() is then a total order on every
+    // input, so the selection is k distinct experts and the preference order
+    // a permutation of the E experts even for non-finite hidden states.
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[t][i] = (e < E) ? acc[t][i] + b : -INFINITY;
+    for (int i = 0; i < 4; ++i) {
+      const float v = acc[t][i] + b;
+      acc[t][i] = (e < E && !__builtin_isnan(v)) ? v : -INFINITY;
+    }
   }
   // Load-balancing statistics of the tile (prob_sum != null): col[t] sums the
   // full softmax probability of expert t*16+n over the tile's live tokens,

@@ -246,3 +246,59 @@ def test_reroute_entry_points_reject_before_launch():
     assert ei.value.status == moe.MOE_ERR_WORKSPACE_TOO_SMALL
     # T = 0: nothing to do
     moe.moe_route_ranked(moe.config(0, 128, 256, 8, 2), None, None, None, None, None, None, stream=0)
+
+
+def test_binding_rejects_bad_tensors_before_the_library():
+    """The library cannot see buffer sizes, so the binding checks every
+    tensor against moe.h's documented device, dtype, contiguity and size
+    before passing its pointer (no call reaches the library here)."""
+    import torch
+    cfg = moe.config(16, 128, 256, 8, 2, -1, "bf16")
+    ok = dict(X=torch.empty(16, 128, dtype=torch.bfloat16), Wg=torch.empty(128, 8, dtype=torch.bfloat16))
+    # a CPU tensor is refused (it is not device memory)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        moe.moe_route(cfg, ok["X"], ok["Wg"], None, 1, 1, 1, 1 << 20, stream=0)
+    meta = lambda shape, dt: torch.empty(shape, dtype=dt, device="meta")  # noqa: E731
+    with pytest.raises(ValueError, match="GPU tensor"):
+        moe.moe_combine(cfg, meta((32, 128), torch.bfloat16), 1, 1, 1, stream=0)
+    # int pointers pass through unchecked: the library then validates nulls
+    with pytest.raises(moe.MoeError):
+        moe.moe_combine(cfg, 1, None, 1, 1, stream=0)
+
+
+def test_binding_arg_checks():
+    """The per-buffer check itself: dtype, contiguity and size are enforced
+    for tensors; None, int pointers and empty requirements pass."""
+    import torch
+    from sparse_mixture_experts_04_amd import _lib
+
+    class FakeCuda:  # stands in for a device tensor (no GPU here)
+        def __init__(self, t):
+            self.t = t
+            self.device = torch.device("cuda", 0)
+            self.dtype = t.dtype
+
+        def is_contiguous(self):
+            return self.t.is_contiguous()
+
+        def numel(self):
+            return self.t.numel()
+
+    orig = _lib.torch.Tensor
+    try:
+        _lib.torch.Tensor = FakeCuda  # isinstance checks accept the stand-in
+        good = FakeCuda(torch.empty(4, 8, dtype=torch.int32))
+        _lib._arg("f", "a", good, torch.int32, 32)
+        _lib._arg("f", "a", None, torch.int32, 32)
+        _lib._arg("f", "a", 1234, torch.int32, 32)
+        _lib._arg("f", "a", good, torch.float32, 0)
+        with pytest.raises(TypeError, match="dtype"):
+            _lib._arg("f", "a", good, torch.float32, 32)
+        with pytest.raises(ValueError, match="needs 33"):
+            _lib._arg("f", "a", good, torch.int32, 33)
+        with pytest.raises(ValueError, match="contiguous"):
+            _lib._arg("f", "a", FakeCuda(torch.empty(8, 4, dtype=torch.int32).t()), torch.int32, 32)
+        with pytest.raises(TypeError):
+            _lib._arg("f", "a", "not a tensor", torch.int32, 32)
+    finally:
+        _lib.torch.Tensor = orig

@@ -10,7 +10,8 @@ import torch
 import oracle
 import sparse_mixture_experts_04_amd as moe
 import workloads
-from gpu_util import (check_dispatch_exact, check_routing, dev_to_f64, rel_tol, round_to, row_rel_err, to_dev)
+from gpu_util import (assert_close, check_dispatch_exact, check_dispatch_valid, check_routing, dev_to_f64, round_to,
+                      to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -258,19 +259,15 @@ def test_expert_up_down(case):
     ws = torch.empty(max(1, moe.moe_workspace_size(cfg, moe.MOE_OP_EXPERT_FFN)), dtype=torch.uint8, device="cuda")
     moe.moe_expert_ffn(cfg, Xp, offsets, W1, W2, Yp2, ws)
     torch.cuda.synchronize()
-    tol = rel_tol(w.dtype)
     if N:
-        eh = row_rel_err(dev_to_f64(H[:N]), H_ref[:N])
-        assert eh.max() <= tol, f"H rel err {eh.max():.3g}"
-        ey = row_rel_err(dev_to_f64(Yp[:N]), Y_ref[:N])
-        assert ey.max() <= tol, f"Yp rel err {ey.max():.3g}"
+        assert_close(dev_to_f64(H[:N]), H_ref[:N], w.dtype, "H")
+        assert_close(dev_to_f64(Yp[:N]), Y_ref[:N], w.dtype, "Yp")
         Y_full = np.zeros((N, w.d))
         for e, a, b in _segments(disp, w.E):
             if b > a:
                 Y_full[a:b] = oracle.expert_ffn(Xp64[a:b], oracle.as_f64(inp.W1[e], w.dtype),
                                                 oracle.as_f64(inp.W2[e], w.dtype))
-        ef = row_rel_err(dev_to_f64(Yp2[:N]), Y_full)
-        assert ef.max() <= tol, f"expert FFN rel err {ef.max():.3g}"
+        assert_close(dev_to_f64(Yp2[:N]), Y_full, w.dtype, "expert FFN")
     # rows past N are never written
     assert (H[N:] == 0).all() and (Yp[N:] == 0).all()
 
@@ -316,8 +313,7 @@ def test_expert_up_gather(case):
         if b > a:
             H_ref[a:b] = oracle.gelu_tanh(Xf[disp.perm[a:b] // w.k] @ oracle.as_f64(inp.W1[e], w.dtype).T)
     if N:
-        eh = row_rel_err(dev_to_f64(H[:N]), H_ref)
-        assert eh.max() <= rel_tol(w.dtype), f"H rel err {eh.max():.3g}"
+        assert_close(dev_to_f64(H[:N]), H_ref, w.dtype, "H")
 
 
 @pytest.mark.parametrize("T,d,F,E,k,bad,offsets", [
@@ -350,8 +346,7 @@ def test_expert_up_gather_bad_perm_entries(T, d, F, E, k, bad, offsets):
         rows = np.arange(a, b)
         rows = rows[np.isin(rows, good)]
         ref[rows] = oracle.gelu_tanh(Xf[perm_np[rows] // k] @ oracle.as_f64(inp.W1[e], "bf16").T)
-    err = row_rel_err(got[good], ref[good])
-    assert err.max() <= rel_tol("bf16"), f"H rel err {err.max():.3g}"
+    assert_close(got[good], ref[good], "bf16", "H")
 
 
 @pytest.mark.parametrize("case", GATHER_CASES, ids=[c[0] for c in GATHER_CASES])
@@ -444,8 +439,7 @@ def test_expert_gemm_tile_heights(rows):
     moe.moe_expert_up_gather(cfg, X, torch.from_numpy(perm_np).cuda(), offsets, W1, Hg)
     torch.cuda.synchronize()
     assert torch.equal(H, Hg)
-    eh = row_rel_err(dev_to_f64(H), H_ref)
-    assert eh.max() <= rel_tol("bf16"), f"H rel err {eh.max():.3g} (worst row {int(eh.argmax())})"
+    assert_close(dev_to_f64(H), H_ref, "bf16", "H")
 
 
 @pytest.mark.parametrize("d,F,cap", [(256, 384, 4), (256, 384, 8), (256, 384, 16), (192, 320, 16)],
@@ -483,10 +477,8 @@ def test_expert_rows_beyond_the_bound(d, F, cap):
     Yp = torch.zeros((Tk, d), dtype=torch.bfloat16, device="cuda")
     moe.moe_expert_down(cfg, torch.from_numpy(H_in).to(torch.bfloat16).cuda(), offsets, to_dev(inp.W2, "bf16"), Yp)
     torch.cuda.synchronize()
-    eh = row_rel_err(dev_to_f64(H), H_ref)
-    assert eh.max() <= rel_tol("bf16"), f"H rel err {eh.max():.3g} (worst row {int(eh.argmax())})"
-    ey = row_rel_err(dev_to_f64(Yp), Y_ref)
-    assert ey.max() <= rel_tol("bf16"), f"Yp rel err {ey.max():.3g} (worst row {int(ey.argmax())})"
+    assert_close(dev_to_f64(H), H_ref, "bf16", "H")
+    assert_close(dev_to_f64(Yp), Y_ref, "bf16", "Yp")
 
 
 @pytest.mark.parametrize("case", CASES, ids=IDS)
@@ -515,8 +507,7 @@ def test_combine(case):
     moe.moe_combine(cfg, Yp, inv, tw, out)
     torch.cuda.synchronize()
     got = dev_to_f64(out)
-    err = row_rel_err(got, ref)
-    assert err.max() <= rel_tol(w.dtype), f"combine rel err {err.max():.3g}"
+    assert_close(got, ref, w.dtype, "combine")
     dropped = ~disp.keep.any(axis=1)
     assert (got[dropped] == 0).all()
     del N
@@ -534,13 +525,20 @@ def test_forward(case):
     out = layer.forward(X)
     torch.cuda.synchronize()
     b = layer.buf
-    diff = check_routing(b.topk_ids.cpu().numpy(), b.topk_w.cpu().numpy(), r)
+    ids_g = b.topk_ids.cpu().numpy()
+    diff = check_routing(ids_g, b.topk_w.cpu().numpy(), r)
+    inv = b.inv_perm.cpu().numpy()
     if not diff.any():
         check_dispatch_exact(b.expert_counts.cpu().numpy(), b.expert_offsets.cpu().numpy(), b.perm.cpu().numpy(),
-                             b.inv_perm.cpu().numpy(), disp, w.T * w.k)
-    err = row_rel_err(dev_to_f64(out), out_ref)
-    ok = ~diff
-    assert err[ok].max() <= rel_tol(w.dtype), f"layer rel err {err[ok].max():.3g}"
+                             inv, disp, w.T * w.k)
+        ok = np.ones(w.T, dtype=bool)
+    else:
+        # a near-tie flipped an id: the dispatch must be a correct one of the
+        # GPU's own ids; outputs are compared where ids and kept slots agree
+        check_dispatch_valid(ids_g, b.expert_counts.cpu().numpy(), b.expert_offsets.cpu().numpy(),
+                             b.perm.cpu().numpy(), inv, w.E, inp.expert_capacity)
+        ok = ~diff & ((inv >= 0).reshape(-1, w.k) == disp.keep).all(axis=1)
+    assert_close(dev_to_f64(out)[ok], out_ref[ok], w.dtype, "layer")
     # determinism: a second run gives bitwise the same output
     first = out.clone()
     layer.forward(X)
@@ -565,8 +563,7 @@ def test_layer_with_saturating_gelu(T, d, E, k, F):
     pre = oracle.as_f64(inp.X, "bf16") @ oracle.as_f64(inp.W1[0], "bf16").T
     assert np.abs(pre).max() > 20.0  # the saturating range is exercised
     diff = check_routing(layer.buf.topk_ids.cpu().numpy(), layer.buf.topk_w.cpu().numpy(), r)
-    err = row_rel_err(got, out_ref)
-    assert err[~diff].max() <= rel_tol("bf16"), f"layer rel err {err[~diff].max():.3g}"
+    assert_close(got[~diff], out_ref[~diff], "bf16", "layer")
 
 
 @pytest.mark.parametrize("T,d,E,k,F", [(600, 128, 8, 2, 192), (40, 1024, 16, 3, 256)], ids=["tiles256", "few_rows"])
@@ -656,6 +653,4 @@ def test_tiny_workload_full():
     assert not diff.any()
     check_dispatch_exact(b.expert_counts.cpu().numpy(), b.expert_offsets.cpu().numpy(), b.perm.cpu().numpy(),
                          b.inv_perm.cpu().numpy(), disp, w.T * w.k)
-    err = row_rel_err(dev_to_f64(out), out_ref)
-    assert err.max() <= rel_tol(w.dtype)
-    assert math.isfinite(err.max())
+    assert_close(dev_to_f64(out), out_ref, w.dtype, "layer")
