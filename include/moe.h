@@ -110,7 +110,8 @@ moe_status moe_workspace_size(const moe_config* cfg, int32_t op, size_t* bytes);
  *   logit bias, the domain bias of mlqm §6).
  *   topk_ids [T, k] int32 out: slot 0 holds the most probable expert; slots in
  *   descending probability; equal logits go to the lower expert id.  A NaN
- *   logit ranks as -inf, so the k ids are always distinct experts.
+ *   or -inf logit ranks as the lowest finite value, so the k ids are always
+ *   distinct experts.
  *   topk_w [T, k] float out: p_s / sum_j p_j over the k selected experts.
  *   ws / ws_bytes: workspace of moe_workspace_size(cfg, MOE_OP_ROUTE) bytes:
  *   the gate transposed to [16*ceil(E/16), d] and, when T is small (the gate

@@ -113,13 +113,16 @@ __device__ __forceinline__ void topk_tile(f32x4_t (&acc)[NT], const float* __res
   for (int t = 0; t < NT; ++t) {
     const int e = t * 16 + n;
     const float b = (e < E && bias != nullptr) ? bias[e] : 0.f;
-    // A NaN logit ranks as -inf: better() is then a total order on every
-    // input, so the selection is k distinct experts and the preference order
-    // a permutation of the E experts even for non-finite hidden states.
+    // Live experts hold values in [-FLT_MAX, +inf]: a NaN or -inf logit
+    // becomes -FLT_MAX.  -inf then marks only the padding lanes (e >= E)
+    // and the experts the selection below has taken, so better() is a total
+    // order on every input and each round takes a new expert: the k ids are
+    // distinct and the preference order is a permutation of the E experts
+    // even for non-finite hidden states.  Finite logits are unchanged.
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float v = acc[t][i] + b;
-      acc[t][i] = (e < E && !__builtin_isnan(v)) ? v : -INFINITY;
+      acc[t][i] = (e < E) ? (__builtin_isnan(v) ? -3.402823466e38f : fmaxf(v, -3.402823466e38f)) : -INFINITY;
     }
   }
   // Load-balancing statistics of the tile (prob_sum != null): col[t] sums the
