@@ -268,6 +268,29 @@ moe_status moe_forward_reroute(const moe_config* cfg, const void* X, const void*
                                int32_t* expert_counts, int32_t* expert_offsets, int32_t* perm,
                                int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of the device array moe_forward_noalloc uses as its workspace (per GPU). */
+#define MOE_NOALLOC_MAX_WORKSPACE_BYTES ((size_t)64 << 20)
+
+/* moe_forward without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments, results and bits as moe_forward
+ * minus ws / ws_bytes: the workspace is a device array inside the library,
+ * MOE_NOALLOC_MAX_WORKSPACE_BYTES (64 MiB) on every GPU the library runs on,
+ * held until the process ends.  The call allocates nothing (no hipMalloc,
+ * no allocating library routine); its first call on a device looks up that
+ * device's copy of the array.
+ * Limit: moe_workspace_size(cfg, MOE_OP_FORWARD) must be at most
+ * MOE_NOALLOC_MAX_WORKSPACE_BYTES (decode-sized batches and small prefills),
+ * else MOE_ERR_WORKSPACE_TOO_SMALL and nothing is enqueued.
+ * Every call on one GPU shares that GPU's array and leaves its contents to
+ * the next call: calls that overlap on one GPU (different streams or host
+ * threads without ordering between them) race. */
+moe_status moe_forward_noalloc(const moe_config* cfg, const void* X, const void* Wg,
+                               const float* gate_bias, const void* W1, const void* W2, void* out,
+                               int32_t* topk_ids, float* topk_w, int32_t* expert_counts,
+                               int32_t* expert_offsets, int32_t* perm, int32_t* inv_perm,
+                               void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -13,6 +13,6 @@ from ._lib import (MOE_BF16, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORT
                    config, moe_capacity_from_factor, moe_combine, moe_dispatch, moe_expert_down, moe_expert_ffn,
                    moe_expert_up,
                    moe_expert_up_gather, moe_expert_up_gather_supported, moe_forward, moe_route, moe_route_stats,
-                   moe_workspace_size, moe_route_ranked, moe_dispatch_reroute, moe_forward_reroute,
+                   moe_workspace_size, moe_route_ranked, moe_dispatch_reroute, moe_forward_reroute, moe_forward_noalloc, NOALLOC_MAX_WORKSPACE_BYTES,
                    status_string, version)
 from .layer import ForwardBuffers, MoELayer  # noqa: F401

@@ -33,12 +33,14 @@ MOE_OP_ROUTE_STATS = 4
 MOE_OP_DISPATCH_REROUTE = 5
 MOE_OP_FORWARD_REROUTE = 6
 
+NOALLOC_MAX_WORKSPACE_BYTES = 64 << 20  # MOE_NOALLOC_MAX_WORKSPACE_BYTES of include/moe.h
+
 # Every symbol include/moe.h declares.
 EXPORTED = ("moe_status_string", "moe_version", "moe_workspace_size", "moe_capacity_from_factor", "moe_route",
             "moe_route_stats", "moe_dispatch",
             "moe_expert_up", "moe_expert_up_gather", "moe_expert_up_gather_supported", "moe_expert_down",
             "moe_expert_ffn", "moe_combine", "moe_forward", "moe_route_ranked", "moe_dispatch_reroute",
-            "moe_forward_reroute")
+            "moe_forward_reroute", "moe_forward_noalloc")
 
 
 class MoeConfig(ctypes.Structure):
@@ -85,6 +87,7 @@ def _load():
         "moe_dispatch_reroute": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
         "moe_forward_reroute": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t,
                                                P]),
+        "moe_forward_noalloc": (ctypes.c_int, [CFG, P, P, P, P, P, P, P, P, P, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -359,3 +362,14 @@ def moe_forward_reroute(cfg, X, Wg, gate_bias, W1, W2, out, topk_ids, topk_w, ex
                                                           _ptr(topk_w), _ptr(expert_order), _ptr(expert_counts),
                                                           _ptr(expert_offsets), _ptr(perm), _ptr(inv_perm), _ptr(ws),
                                                           int(ws_bytes), _stream(stream)))
+
+
+def moe_forward_noalloc(cfg, X, Wg, gate_bias, W1, W2, out, topk_ids, topk_w, expert_counts, expert_offsets, perm,
+                        inv_perm, stream=None) -> None:
+    """moe_forward with the library's own per-GPU workspace array (no workspace argument)."""
+    _forward_args("moe_forward_noalloc", cfg, X, Wg, gate_bias, W1, W2, out, topk_ids, topk_w, expert_counts,
+                  expert_offsets, perm, inv_perm)
+    _check("moe_forward_noalloc", LIB.moe_forward_noalloc(ctypes.byref(cfg), _ptr(X), _ptr(Wg), _ptr(gate_bias),
+                                                          _ptr(W1), _ptr(W2), _ptr(out), _ptr(topk_ids),
+                                                          _ptr(topk_w), _ptr(expert_counts), _ptr(expert_offsets),
+                                                          _ptr(perm), _ptr(inv_perm), _stream(stream)))
