@@ -225,8 +225,9 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_kernel(const T* 
 }
 
 // ---------------------------------------------------------------------------
-// bf16 main kernel: 256x256 tiles, 4 waves of 128x128, 32x32x16 MFMAs, fed by
-// direct buffer->LDS loads through a ring of LDS units.
+// bf16 main kernel: 256x256 tiles, 8 waves of 128 token rows x 64 weight
+// rows (or 4 waves of 128x128), 32x32x16 MFMAs, fed by direct buffer->LDS
+// loads through a ring of LDS units.
 //
 // * A unit is 64 K-elements (128 bytes: one full cache line per row) of the
 //   256 rows of one operand, 32 KB.  A stage is one weight unit and one token
@@ -248,7 +249,15 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_kernel(const T* 
 //   columns: two 16-byte stores.
 // * One barrier per stage (four 16-element k-steps).
 constexpr int kBig = 256;                                 // BM = BN
-constexpr int kBigThreads = 256;                          // 4 waves, 2 x 2
+// Waves per block of the 256x256 kernel: 8, two per SIMD, each computing 128
+// token rows x 64 weight rows (128 accumulator registers), so one wave's
+// waits on loads, LDS reads or the barrier are covered by the other wave's
+// MFMAs.  The kernel also builds with 4 waves (one per SIMD, 128 x 128 each,
+// 256 accumulator registers); the results are bitwise the same (same
+// fragments, same K order per output), and on MI355X 8 waves measured
+// 1.5-5% faster on every expert GEMM of the prefill, capacity and skewed
+// layers.
+constexpr int kBigWaves = 8;
 constexpr int kUnitRow = 128;                             // K bytes per row per unit
 constexpr int kUnitBytes = kBig * kUnitRow;               // 32 KB
 constexpr int kSlots = 5;
@@ -291,8 +300,8 @@ struct TileCoord {
 // expert-ordered operand is row gidx[r] / gdiv of A, which then has src_rows
 // rows: the dispatch permutation (entries token*k + slot) read with gdiv = k
 // gathers each token's hidden state straight from the layer input.
-template <bool kGelu, bool kGather>
-__global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const uint16_t* __restrict__ A,
+template <bool kGelu, bool kGather, int kWaves>
+__global__ __launch_bounds__(kWaves * kWave) void grouped_gemm_bf16_256(const uint16_t* __restrict__ A,
                                                                         const uint16_t* __restrict__ B,
                                                                         uint16_t* __restrict__ C,
                                                                         const int32_t* __restrict__ offsets, int E,
@@ -300,12 +309,19 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
                                                                         const int32_t* __restrict__ gidx, int gdiv,
                                                                         int src_rows) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  static_assert(kWaves == 4 || kWaves == 8, "4 waves (one per SIMD) or 8 (two per SIMD)");
+  // Waves split the tile into 2 token halves x kWN weight parts; a wave
+  // holds kWF 32-row weight fragments and fills kRowsW rows of each unit.
+  constexpr int kWN = kWaves / 2;
+  constexpr int kWF = 8 / kWN;
+  constexpr int kRowsW = kBig / kWaves;
+  constexpr int kLd = kRowsW / 8;  // 16-byte loads per lane per unit
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: LDS bases stay scalar
-  const int wm = wave >> 1;   // token half of the tile
-  const int wn = wave & 1;    // weight half of the tile
+  const int wm = wave / kWN;  // token half of the tile
+  const int wn = wave % kWN;  // weight part of the tile
 
   // Expert table, held by every wave in registers: lane e has expert e's row
   // segment [seg0, seg1) (clamped to [0, max_rows]: offsets come from device
@@ -397,12 +413,12 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
   };
 
   // ---- producers: one stream of weight units and one of token units.
-  // Instruction i of this wave fills rows wave*64 + i*8 .. +7 of a unit (1 KB
-  // of LDS); lane p fills row wave*64 + i*8 + p/8, physical chunk p%8.
-  int vw[8], vx[8];
+  // Instruction i of this wave fills rows wave*kRowsW + i*8 .. +7 of a unit
+  // (1 KB of LDS); lane p fills row wave*kRowsW + i*8 + p/8, physical chunk p%8.
+  int vw[kLd], vx[kLd];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = wave * 64 + i * 8 + (lane >> 3);
+  for (int i = 0; i < kLd; ++i) {
+    const int r = wave * kRowsW + i * 8 + (lane >> 3);
     vw[i] = r * row_stride + (((lane & 7) ^ key_w(r)) << 4);
     vx[i] = r * row_stride + (((lane & 7) ^ key_x(r)) << 4);
   }
@@ -425,23 +441,23 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
     }
   };
   // Gathered token rows: the token stream's per-lane offsets change with the
-  // tile.  g[i] receives the gather index of row wave*64 + i*8 + lane/8 of a
-  // tile; the stage loop loads them at the start of the stage whose token
+  // tile.  g[i] receives the gather index of row wave*kRowsW + i*8 + lane/8 of
+  // a tile; the stage loop loads them at the start of the stage whose token
   // unit is the stream's last of its tile, before that stage's weight unit,
   // so the stage wait (which leaves only that weight unit in flight) covers
   // them and the offsets are formed at the stream's tile switch without a
   // wait of their own.
-  auto load_gidx = [&](int (&g)[8], int tile) {
+  auto load_gidx = [&](int* g, int tile) {
     if (tile < total) {
       const TileCoord t = coord(tile);
       const __amdgpu_buffer_rsrc_t grsrc = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<int32_t*>(gidx) + t.m0, 0, t.rows * 4, kRsrcWord3);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        g[i] = __builtin_amdgcn_raw_buffer_load_b32(grsrc, (wave * 64 + i * 8 + (lane >> 3)) * 4, 0, 0);
+      for (int i = 0; i < kLd; ++i)
+        g[i] = __builtin_amdgcn_raw_buffer_load_b32(grsrc, (wave * kRowsW + i * 8 + (lane >> 3)) * 4, 0, 0);
     }
   };
-  auto setup_x = [&](Stream& s, const int (&g)[8]) {
+  auto setup_x = [&](Stream& s, const int* g) {
     if (s.tile < total) {
       const TileCoord t = coord(s.tile);
       if constexpr (kGather) {
@@ -450,8 +466,8 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
         s.base = Ab;
         s.rows = src_rows;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int r = wave * 64 + i * 8 + (lane >> 3);
+        for (int i = 0; i < kLd; ++i) {
+          const int r = wave * kRowsW + i * 8 + (lane >> 3);
           const unsigned src = static_cast<unsigned>(g[i]) / static_cast<unsigned>(gdiv);
           vx[i] = r < t.rows && src < static_cast<unsigned>(src_rows)
                       ? static_cast<int>(src) * row_stride + (((lane & 7) ^ key_x(r)) << 4)
@@ -465,16 +481,17 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
       s.rows = 0;
     }
   };
-  // Issue one unit (8 loads of 1 KB per wave).  Past the last tile the range
-  // is empty: the loads return zeros into a free slot without touching memory.
-  auto issue = [&](const Stream& s, const int (&voff)[8]) {
+  // Issue one unit (kLd loads of 1 KB per wave).  Past the last tile the
+  // range is empty: the loads return zeros into a free slot without touching
+  // memory.
+  auto issue = [&](const Stream& s, const int* voff) {
     const int koff = s.ks * kUnitRow;
     const int nrec = max(s.rows * row_stride - koff, 0);
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(s.base) + koff, 0, nrec, kRsrcWord3);
-    unsigned char* dst = smem + s.slot * kUnitBytes + wave * 64 * kUnitRow;
+    unsigned char* dst = smem + s.slot * kUnitBytes + wave * kRowsW * kUnitRow;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < kLd; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(dst + i * 8 * kUnitRow), 16, voff[i], 0, 0, 0);
   };
   auto advance_w = [&](Stream& s) {
@@ -487,7 +504,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
   };
   // g: the gather indices of tile s.tile + G (used only when the stream
   // moves there).
-  auto advance_x = [&](Stream& s, const int (&g)[8]) {
+  auto advance_x = [&](Stream& s, const int* g) {
     s.slot = s.slot + 2 >= kSlots ? s.slot + 2 - kSlots : s.slot + 2;
     if (++s.ks == kstages) {
       s.ks = 0;
@@ -497,7 +514,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
   };
 
   setup_w(ws);
-  int gp[8];
+  int gp[kLd];
   if constexpr (kGather) load_gidx(gp, first);
   setup_x(xs, gp);
   // Prologue: stages 0 and 1 (units 0..3).
@@ -518,45 +535,46 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
   const int kw = key_w(wrow);  // = key_w of every weight row this lane reads
   int c_wslot = 0, c_xslot = 1;
 
-  // Fragments of one 16-element k-step: 4 weight and up to 4 token
+  // Fragments of one 16-element k-step: kWF weight and up to 4 token
   // fragments.  Token fragment j of this wave covers tile rows
   // (2j + wm)*32 .. +31: the two token-half waves interleave, so a tile of R
   // rows has ceil(R/32) fragments with rows and each wave runs
   // nj = ceil(ceil(R/32)/2) of them (both waves the same count, so the
   // per-stage barrier costs no idle MFMA time).
-  u32x4_t wf0[4], xf0[4], wf1[4], xf1[4];
+  u32x4_t wf0[kWF], xf0[4], wf1[kWF], xf1[4];
   auto frag_addr_w = [&](int kk, int i) {
-    return smem + c_wslot * kUnitBytes + (wn * 128 + i * 32 + wrow) * kUnitRow + (((kk * 2 + fhalf) ^ kw) << 4);
+    return smem + c_wslot * kUnitBytes + (wn * (kWF * 32) + i * 32 + wrow) * kUnitRow +
+           (((kk * 2 + fhalf) ^ kw) << 4);
   };
   auto frag_addr_x = [&](int kk, int j) {
     return smem + c_xslot * kUnitBytes + ((2 * j + wm) * 32 + frow) * kUnitRow + (((kk * 2 + fhalf) ^ kx) << 4);
   };
-  auto read_frags = [&](auto nj_c, int kk, u32x4_t (&wf)[4], u32x4_t (&xf)[4]) {
+  auto read_frags = [&](auto nj_c, int kk, u32x4_t (&wf)[kWF], u32x4_t (&xf)[4]) {
     constexpr int NJ = decltype(nj_c)::value;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wf[i] = *reinterpret_cast<const u32x4_t*>(frag_addr_w(kk, i));
+    for (int i = 0; i < kWF; ++i) wf[i] = *reinterpret_cast<const u32x4_t*>(frag_addr_w(kk, i));
 #pragma unroll
     for (int j = 0; j < NJ; ++j) xf[j] = *reinterpret_cast<const u32x4_t*>(frag_addr_x(kk, j));
   };
-  // One k-step block, in a fixed issue order: its 4*NJ MFMAs, with the 4+NJ
-  // fragment reads of k-step `kk_next` (into wn/xn) spread over the first
-  // half of them and, if `s` is given, a unit's 8 buffer->LDS loads spread
-  // over the first 8, so neither the LDS nor the load queue holds up the
-  // MFMA stream.
-  auto block = [&](auto nj_c, f32x16_t (&acc)[4][4], const u32x4_t (&wa)[4], const u32x4_t (&xa)[4], int kk_next,
-                   u32x4_t (&wn_)[4], u32x4_t (&xn_)[4], const Stream* s, const int* voff) {
+  // One k-step block, in a fixed issue order: its kWF*NJ MFMAs, with the
+  // kWF+NJ fragment reads of k-step `kk_next` (into wn/xn) spread over the
+  // first half of them and, if `s` is given, a unit's kLd buffer->LDS loads
+  // spread over the first kLd, so neither the LDS nor the load queue holds up
+  // the MFMA stream.
+  auto block = [&](auto nj_c, f32x16_t (&acc)[kWF][4], const u32x4_t (&wa)[kWF], const u32x4_t (&xa)[4],
+                   int kk_next, u32x4_t (&wn_)[kWF], u32x4_t (&xn_)[4], const Stream* s, const int* voff) {
     constexpr int NJ = decltype(nj_c)::value;
-    constexpr int kM = 4 * NJ;
-    constexpr int kR = 4 + NJ;
-    constexpr int kRq = kM / 2;
-    constexpr int kLq = kM < 8 ? kM : 8;
+    constexpr int kM = kWF * NJ;
+    constexpr int kR = kWF + NJ;
+    constexpr int kRq = (kM + 1) / 2;
+    constexpr int kLq = kM < kLd ? kM : kLd;
     __amdgpu_buffer_rsrc_t rsrc;
     unsigned char* dst = smem;
     if (s != nullptr) {
       const int koff = s->ks * kUnitRow;
       const int nrec = max(s->rows * row_stride - koff, 0);
       rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(s->base) + koff, 0, nrec, kRsrcWord3);
-      dst = smem + s->slot * kUnitBytes + wave * 64 * kUnitRow;
+      dst = smem + s->slot * kUnitBytes + wave * kRowsW * kUnitRow;
     }
 #pragma unroll
     for (int q = 0; q < kM; ++q) {
@@ -565,13 +583,13 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
       if (kk_next >= 0 && q < kRq) {
 #pragma unroll
         for (int r = q * kR / kRq; r < (q + 1) * kR / kRq; ++r) {
-          if (r < 4) wn_[r] = *reinterpret_cast<const u32x4_t*>(frag_addr_w(kk_next, r));
-          else xn_[r - 4] = *reinterpret_cast<const u32x4_t*>(frag_addr_x(kk_next, r - 4));
+          if (r < kWF) wn_[r] = *reinterpret_cast<const u32x4_t*>(frag_addr_w(kk_next, r));
+          else xn_[r - kWF] = *reinterpret_cast<const u32x4_t*>(frag_addr_x(kk_next, r - kWF));
         }
       }
       if (s != nullptr && q < kLq) {
 #pragma unroll
-        for (int l = q * 8 / kLq; l < (q + 1) * 8 / kLq; ++l)
+        for (int l = q * kLd / kLq; l < (q + 1) * kLd / kLq; ++l)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(dst + l * 8 * kUnitRow), 16, voff[l], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -584,8 +602,8 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
   };
 
   // Stage 0 must be resident before its first fragments are read (stage 1,
-  // 16 loads, may still be in flight).
-  wait_vmcnt<16>();
+  // 2*kLd loads, may still be in flight).
+  wait_vmcnt<2 * kLd>();
   barrier();
   bool after_epilogue = false;
 
@@ -594,9 +612,9 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
   // tile's last block read it with that tile's nj).
   auto run_tile = [&](auto nj_c, const TileCoord& tc) {
     constexpr int NJ = decltype(nj_c)::value;
-    f32x16_t acc[4][4];
+    f32x16_t acc[kWF][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kWF; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -604,7 +622,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
     read_frags(nj_c, 0, wf0, xf0);
 
     for (int ks = 0; ks < kstages; ++ks) {
-      int gn[8];
+      int gn[kLd];
       if constexpr (kGather) {
         if (xs.ks == kstages - 1) load_gidx(gn, xs.tile + G);
         __builtin_amdgcn_sched_barrier(0);
@@ -619,7 +637,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
       // in flight (right after an epilogue its stores are outstanding too:
       // drain).  lgkmcnt(0): this wave's reads of this stage are complete, so
       // after the barrier its two units are free.
-      wait_vmcnt_lgkm0<8>();
+      wait_vmcnt_lgkm0<kLd>();
       if (after_epilogue) wait_vmcnt<0>();
       after_epilogue = false;
       barrier();
@@ -634,7 +652,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
     }
     after_epilogue = true;
 
-    // acc[i][j][q]: token row m0 + (2j + wm)*32 + frow, column n0 + wn*128 + i*32 + 16*fhalf + q.
+    // acc[i][j][q]: token row m0 + (2j + wm)*32 + frow, column n0 + wn*kWF*32 + i*32 + 16*fhalf + q.
     // Stores go through a buffer resource over the tile's rows of C; a
     // column past N gets an offset beyond the range.  The hardware drops
     // out-of-range stores, so the epilogue has no branches and each group of
@@ -645,8 +663,8 @@ __global__ __launch_bounds__(kBigThreads, 1) void grouped_gemm_bf16_256(const ui
     for (int j = 0; j < NJ; ++j) {
       const int roff = ((2 * j + wm) * 32 + frow) * N * 2;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int col = tc.n0 + wn * 128 + i * 32 + 16 * fhalf;
+      for (int i = 0; i < kWF; ++i) {
+        const int col = tc.n0 + wn * (kWF * 32) + i * 32 + 16 * fhalf;
         const int off = col < N ? roff + col * 2 : static_cast<int>(0x80000000u);
         // Redefine the group's accumulators here (an empty asm on their
         // registers), after the previous group's stores: otherwise the
@@ -684,7 +702,7 @@ template <bool kGelu, bool kGather>
 hipError_t launch_big(const uint16_t* A, const uint16_t* B, uint16_t* C, const int32_t* offsets, int E, int N, int K,
                       int max_rows, const int32_t* gidx, int gdiv, int src_rows, hipStream_t stream) {
   static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_bf16_256<kGelu, kGather>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_bf16_256<kGelu, kGather, kBigWaves>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kBigLds));
   if (attr != hipSuccess) return attr;
   // 32-bit buffer offsets: 256 rows of K (operands) or N (results) bf16, and
@@ -701,8 +719,9 @@ hipError_t launch_big(const uint16_t* A, const uint16_t* B, uint16_t* C, const i
   int64_t grid = device_cu_count();
   if (upper < grid) grid = upper;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL((grouped_gemm_bf16_256<kGelu, kGather>), dim3(static_cast<unsigned>(grid)), dim3(kBigThreads),
-                     kBigLds, stream, A, B, C, offsets, E, N, K, max_rows, gidx, gdiv, src_rows);
+  hipLaunchKernelGGL((grouped_gemm_bf16_256<kGelu, kGather, kBigWaves>), dim3(static_cast<unsigned>(grid)),
+                     dim3(kBigWaves * kWave), kBigLds, stream, A, B, C, offsets, E, N, K, max_rows, gidx, gdiv,
+                     src_rows);
   return hipGetLastError();
 }
 
