@@ -248,19 +248,30 @@ __device__ __forceinline__ void static_for(F&& f) {
 constexpr int kLdsRouterScratch = 4 * 2 * 16 * kMaxExperts * 4;  // per-wave top-k scratch, 32 KB
 constexpr int kLdsRouterMaxGate = 64 * 1024;                      // gate elements that fit beside it
 
-template <int NT, int RT>
+// With kSplit the gate does not fit in LDS whole: K is cut into gridDim.y
+// slices of dlen, block (x, y) keeps slice y of the gate in LDS, streams
+// that slice of its tokens' rows and writes the slice's partial logits to
+// partial[y][token][e]; router_topk_kernel then sums the slices in order and
+// selects.  Without kSplit, dlen = d and the block selects itself.
+// With kSplit the gate comes from WgT ([16*NT][d], written by
+// gate_transpose_kernel): the block copies its slice into LDS with direct
+// buffer->LDS loads, the chunk swizzle applied to the global offsets.
+template <int NT, int RT, bool kSplit>
 __global__ __launch_bounds__(kRouterThreads, 1) void router_lds_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wg, const float* __restrict__ bias, int T_tokens,
-    int d, int E, int k, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, float inv_tau,
-    float* __restrict__ prob_sum, uint8_t* __restrict__ order) {
+    int d, int dlen, int E, int k, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, float inv_tau,
+    float* __restrict__ prob_sum, uint8_t* __restrict__ order, float* __restrict__ partial,
+    const uint16_t* __restrict__ WgT) {
   constexpr int WT = RT >= 4 ? 4 : RT;  // token groups of waves
   constexpr int WK = 4 / WT;            // K splits per token group
   constexpr int RW = RT / WT;           // row tiles per wave
   constexpr int kU = RW == 1 ? 8 : 4;   // double steps in flight per batch (16 loads per lane)
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   unsigned char* const gate = smem;
-  const int row_bytes = d * 2;
+  const int row_bytes = dlen * 2;
   unsigned char* const scratch = smem + static_cast<size_t>(16 * NT) * row_bytes;
+  const int kbeg = kSplit ? static_cast<int>(blockIdx.y) * dlen : 0;  // this block's K slice [kbeg, kbeg + dlen)
+  const uint16_t* const Wg_s = Wg + static_cast<int64_t>(kbeg) * E;
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -270,7 +281,7 @@ __global__ __launch_bounds__(kRouterThreads, 1) void router_lds_kernel(
 
   const int wt = wave / WK;
   const int wk = wave % WK;
-  const int nds = d / 64;
+  const int nds = dlen / 64;
   float* const sel_val = reinterpret_cast<float*>(scratch + wave * (2 * 16 * kMaxExperts * 4));
   int* const sel_id = reinterpret_cast<int*>(scratch + wave * (2 * 16 * kMaxExperts * 4) + 16 * kMaxExperts * 4);
   f32x4_t* const red = reinterpret_cast<f32x4_t*>(scratch);  // [4 waves][RW][NT][64 lanes], aliases the top-k scratch
@@ -282,7 +293,7 @@ __global__ __launch_bounds__(kRouterThreads, 1) void router_lds_kernel(
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
       const int tok = min(tok_base + (wt * RW + r) * 16 + n, T_tokens - 1);  // rows past T repeat the last token
-      xrow[r] = reinterpret_cast<const unsigned char*>(X + static_cast<int64_t>(tok) * d) + grp * 32;
+      xrow[r] = reinterpret_cast<const unsigned char*>(X + static_cast<int64_t>(tok) * d + kbeg) + grp * 32;
     }
   };
   const int nsteps = (nds - wk + WK - 1) / WK;
@@ -306,19 +317,41 @@ __global__ __launch_bounds__(kRouterThreads, 1) void router_lds_kernel(
   int tok_base = blockIdx.x * 16 * RT;  // < T_tokens: the grid has no block without tokens
   set_rows(tok_base);
 
+  if constexpr (kSplit) {
+    // Slice rows e = 0 .. 16*NT-1 of WgT, 2*dlen bytes each: instruction j
+    // of this wave fills LDS bytes [1024 (4j + wave), +1024), lane l its
+    // chunk p = 64 (4j + wave) % (row chunks) + l of row e, which holds the
+    // slice's chunk p ^ (e & 15) (XOR within runs of 16 chunks, so one
+    // instruction reads one contiguous 1 KB run of WgT).
+    const __amdgpu_buffer_rsrc_t grsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(WgT), 0, 16 * NT * d * 2, 0x00020000);
+    const int row_chunks = dlen / 8;
+    const int n_instr = 16 * NT * row_chunks / kWave;
+    for (int j = wave; j < n_instr; j += kRouterThreads / kWave) {
+      const int p_lin = j * kWave + lane;
+      const int e = p_lin / row_chunks;
+      const int p = p_lin % row_chunks;
+      const int goff = (e * d + kbeg + ((p ^ (e & 15)) << 3)) * 2;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(grsrc, (__attribute__((address_space(3))) void*)(gate + j * 1024), 16,
+                                               goff, 0, 0, 0);
+    }
+    load_batch(0, bufA);
+    if (nbatch > 1) load_batch(1, bufB);
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));  // vmcnt(0): the slice (and the first batches) landed
+  } else {
   // ---- W_g^T into LDS: unit (kb, eg) = 8 consecutive k x 8 experts, read as
   // 8 rows of 16 bytes (W_g is [d, E], experts contiguous) and written as 8
   // rows-of-W_g^T chunks of 16 bytes.
-  {
     constexpr int kBatch = 4;  // units per thread with their loads in flight together
     const int egs = 2 * NT;    // 8-expert groups, padding included
-    const int units = (d / 8) * egs;
-    // Vector loads go through a buffer resource over W_g (d*E*2 < 2^31
-    // bytes, as d*16*NT <= 64K): padding experts and units past the end take
-    // an offset beyond the range and read zeros, so no load sits behind a
-    // branch.  E not a multiple of 8 (rows not 16-byte aligned): 2-byte loads.
+    const int units = (dlen / 8) * egs;
+    // Vector loads go through a buffer resource over the slice of W_g
+    // (dlen*E*2 < 2^31 bytes, as dlen*16*NT <= 64K): padding experts and
+    // units past the end take an offset beyond the range and read zeros, so
+    // no load sits behind a branch.  E not a multiple of 8 (rows not 16-byte
+    // aligned): 2-byte loads.
     const __amdgpu_buffer_rsrc_t wrsrc =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Wg), 0, d * E * 2, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Wg_s), 0, dlen * E * 2, 0x00020000);
     // One batch of units; the first also issues the first two batches of
     // token loads right after its gate loads, so all are in flight together.
     auto do_batch = [&](int u0, auto vec_c, auto first_c) {
@@ -343,8 +376,8 @@ __global__ __launch_bounds__(kRouterThreads, 1) void router_lds_kernel(
               for (int q = 0; q < 4; ++q) {
                 const int e0 = eg * 8 + 2 * q;
                 const int o = (kb * 8 + j) * E + e0;
-                const uint32_t lo = u < units && e0 < E ? Wg[o] : 0u;
-                const uint32_t hi = u < units && e0 + 1 < E ? Wg[o + 1] : 0u;
+                const uint32_t lo = u < units && e0 < E ? Wg_s[o] : 0u;
+                const uint32_t hi = u < units && e0 + 1 < E ? Wg_s[o + 1] : 0u;
                 in[b][j][q] = lo | (hi << 16);
               }
             }
@@ -456,8 +489,22 @@ __global__ __launch_bounds__(kRouterThreads, 1) void router_lds_kernel(
       // index acc dynamically, and the compiler would move acc to memory.
       static_for<RW>([&](auto r_c) {
         constexpr int r = decltype(r_c)::value;
-        topk_tile<NT>(acc[r], bias, E, k, cur_base + (wt * RW + r) * 16, T_tokens, sel_val, sel_id, topk_ids,
-                      topk_w, inv_tau, prob_sum, order);
+        const int rtok0 = cur_base + (wt * RW + r) * 16;
+        if constexpr (kSplit) {
+          // Partial logits in fragment order, [slice][tile][t][lane] of
+          // f32x4 (lane (n, grp), element i: token 16*tile + 4grp + i,
+          // expert 16t + n), so each store and each load of
+          // router_topk_frag_kernel moves whole 1 KB rows.
+          f32x4_t* out = reinterpret_cast<f32x4_t*>(partial) +
+                         (static_cast<int64_t>(blockIdx.y) * ((T_tokens + 15) / 16) + rtok0 / 16) * NT * kWave;
+          if (rtok0 < T_tokens) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) out[t * kWave + lane] = acc[r][t];
+          }
+        } else {
+          topk_tile<NT>(acc[r], bias, E, k, rtok0, T_tokens, sel_val, sel_id, topk_ids, topk_w, inv_tau, prob_sum,
+                        order);
+        }
       });
     }
     if (!more) break;
@@ -480,6 +527,42 @@ __global__ __launch_bounds__(1024) void router_topk_kernel(const float* __restri
   __shared__ int sel_id[16 * kMaxExperts];
   topk_from_partials<NT>(partial, nsplit, bias, T_tokens, E, k, blockIdx.x * 16, logit, sel_val, sel_id, topk_ids,
                          topk_w, inv_tau, prob_sum, order);
+}
+
+// Sum the K-slice partial logits of router_lds_kernel<..., true> (fragment
+// order, see there) in slice order, then top-k: each wave owns one 16-token
+// tile and loads its nslices x NT fragments (1 KB each) with all loads in
+// flight.  The sums run in the same order as router_topk_kernel's, so the
+// logits are the same bits.
+template <int NT>
+__global__ __launch_bounds__(kRouterThreads) void router_topk_frag_kernel(
+    const f32x4_t* __restrict__ partial, int nslices, const float* __restrict__ bias, int T_tokens, int E, int k,
+    int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, float inv_tau, float* __restrict__ prob_sum,
+    uint8_t* __restrict__ order) {
+  constexpr int kMaxSlices = 8;
+  __shared__ float sel_val[kRouterThreads / kWave][16 * kMaxExperts];
+  __shared__ int sel_id[kRouterThreads / kWave][16 * kMaxExperts];
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int ntiles = (T_tokens + 15) / 16;
+  const int tile = blockIdx.x * (kRouterThreads / kWave) + wave;
+  if (tile >= ntiles) return;
+  f32x4_t v[kMaxSlices][NT];
+#pragma unroll
+  for (int sl = 0; sl < kMaxSlices; ++sl)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      if (sl < nslices) v[sl][t] = partial[(static_cast<int64_t>(sl) * ntiles + tile) * NT * kWave + t * kWave + lane];
+  f32x4_t acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sl = 0; sl < kMaxSlices; ++sl)
+      if (sl < nslices) acc[t] += v[sl][t];  // slice order
+  }
+  topk_tile<NT>(acc, bias, E, k, tile * 16, T_tokens, sel_val[wave], sel_id[wave], topk_ids, topk_w, inv_tau,
+                prob_sum, order);
 }
 
 // The load-balancing statistics from the per-tile sums of topk_tile
@@ -572,34 +655,75 @@ bool lds_router(int dtype, int T_tokens, int d, int E) {
          (E + 15) / 16 * 16 * d <= kLdsRouterMaxGate;
 }
 
-template <int NT, int RT>
-hipError_t launch_lds_rt(const uint16_t* X, const uint16_t* Wg, const float* bias, int T_tokens, int d, int E, int k,
-                         int32_t* ids, float* w, int grid, const RouteExtra& x, hipStream_t stream) {
-  const size_t lds = static_cast<size_t>(16 * NT) * d * 2 + kLdsRouterScratch;
+// K slices of the split LDS router, or 0 where it does not run: bf16, many
+// tokens (no small-batch K split), a gate too large for LDS whole, and d
+// cut into 2..8 equal slices that are multiples of 128 and fit in LDS
+// (d = 4096 with 64 experts: 4 slices of 1024).
+int lds_router_slices(int dtype, int T_tokens, int d, int E) {
+  if (dtype != kDtypeBF16 || split_len_of(T_tokens, d) != d || d % 128 != 0) return 0;
+  const int rows = (E + 15) / 16 * 16;
+  if (rows * d <= kLdsRouterMaxGate) return 0;
+  for (int n = 2; n <= 8; ++n)
+    if (d % (n * 128) == 0 && rows * (d / n) <= kLdsRouterMaxGate) return n;
+  return 0;
+}
+
+template <int NT, int RT, bool kSplit>
+hipError_t launch_lds_rt(const uint16_t* X, const uint16_t* Wg, const float* bias, int T_tokens, int d, int dlen,
+                         int E, int k, int32_t* ids, float* w, dim3 grid, const RouteExtra& x, float* partial,
+                         const uint16_t* WgT, hipStream_t stream) {
+  const size_t lds = static_cast<size_t>(16 * NT) * dlen * 2 + kLdsRouterScratch;
   static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&router_lds_kernel<NT, RT>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&router_lds_kernel<NT, RT, kSplit>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, kLdsRouterMaxGate * 2 + kLdsRouterScratch);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((router_lds_kernel<NT, RT>), dim3(grid), dim3(kRouterThreads), lds, stream, X, Wg, bias,
-                     T_tokens, d, E, k, ids, w, x.inv_tau, x.prob_sum, x.order);
+  hipLaunchKernelGGL((router_lds_kernel<NT, RT, kSplit>), grid, dim3(kRouterThreads), lds, stream, X, Wg, bias,
+                     T_tokens, d, dlen, E, k, ids, w, x.inv_tau, x.prob_sum, x.order, partial, WgT);
   return hipGetLastError();
 }
 
+// nslices = 1: the whole gate in LDS, every block selects.  nslices > 1:
+// the K slices, partial logits into `partial`, then router_topk_kernel.
 template <int NT>
 hipError_t launch_lds(const uint16_t* X, const uint16_t* Wg, const float* bias, int T_tokens, int d, int E, int k,
-                      int32_t* ids, float* w, const RouteExtra& x, hipStream_t stream) {
+                      int32_t* ids, float* w, const RouteExtra& x, int nslices, float* partial, uint16_t* WgT,
+                      hipStream_t stream) {
   // One block per CU (fewer if there are fewer 16-token tiles), each with a
-  // contiguous range of 16*RT tokens per pass.
-  // The grid then shrinks to the blocks that have tokens in their first pass.
+  // contiguous range of 16*RT tokens per pass; with slices, the CUs are
+  // shared out among the slices.  The grid then shrinks to the blocks that
+  // have tokens in their first pass.
   const int tiles = (T_tokens + 15) / 16;
-  const int cus = std::max(1, std::min(device_cu_count(), tiles));
+  const int cus = std::max(1, std::min(device_cu_count() / nslices, tiles));
   const int per = (tiles + cus - 1) / cus;
   const int rt = per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : 8;
-  const int grid = std::min(cus, (tiles + rt - 1) / rt);
-  if (rt == 1) return launch_lds_rt<NT, 1>(X, Wg, bias, T_tokens, d, E, k, ids, w, grid, x, stream);
-  if (rt == 2) return launch_lds_rt<NT, 2>(X, Wg, bias, T_tokens, d, E, k, ids, w, grid, x, stream);
-  if (rt == 4) return launch_lds_rt<NT, 4>(X, Wg, bias, T_tokens, d, E, k, ids, w, grid, x, stream);
-  return launch_lds_rt<NT, 8>(X, Wg, bias, T_tokens, d, E, k, ids, w, grid, x, stream);
+  const dim3 grid(std::min(cus, (tiles + rt - 1) / rt), nslices);
+  const int dlen = d / nslices;
+  hipError_t e;
+  if (nslices == 1) {
+    if (rt == 1)
+      return launch_lds_rt<NT, 1, false>(X, Wg, bias, T_tokens, d, d, E, k, ids, w, grid, x, nullptr, nullptr, stream);
+    if (rt == 2)
+      return launch_lds_rt<NT, 2, false>(X, Wg, bias, T_tokens, d, d, E, k, ids, w, grid, x, nullptr, nullptr, stream);
+    if (rt == 4)
+      return launch_lds_rt<NT, 4, false>(X, Wg, bias, T_tokens, d, d, E, k, ids, w, grid, x, nullptr, nullptr, stream);
+    return launch_lds_rt<NT, 8, false>(X, Wg, bias, T_tokens, d, d, E, k, ids, w, grid, x, nullptr, nullptr, stream);
+  }
+  // The gate transposed once into the workspace, then copied slice by slice.
+  hipLaunchKernelGGL((gate_transpose_kernel<uint16_t, NT>), dim3(d / 32), dim3(256), 0, stream, Wg, d, E, WgT);
+  if (rt == 1)
+    e = launch_lds_rt<NT, 1, true>(X, Wg, bias, T_tokens, d, dlen, E, k, ids, w, grid, x, partial, WgT, stream);
+  else if (rt == 2)
+    e = launch_lds_rt<NT, 2, true>(X, Wg, bias, T_tokens, d, dlen, E, k, ids, w, grid, x, partial, WgT, stream);
+  else if (rt == 4)
+    e = launch_lds_rt<NT, 4, true>(X, Wg, bias, T_tokens, d, dlen, E, k, ids, w, grid, x, partial, WgT, stream);
+  else
+    e = launch_lds_rt<NT, 8, true>(X, Wg, bias, T_tokens, d, dlen, E, k, ids, w, grid, x, partial, WgT, stream);
+  if (e != hipSuccess) return e;
+  const int waves = kRouterThreads / kWave;
+  hipLaunchKernelGGL((router_topk_frag_kernel<NT>), dim3((tiles + waves - 1) / waves), dim3(kRouterThreads), 0, stream,
+                     reinterpret_cast<const f32x4_t*>(partial), nslices, bias, T_tokens, E, k, ids, w, x.inv_tau,
+                     x.prob_sum, x.order);
+  return hipGetLastError();
 }
 
 template <typename T, int NT>
@@ -607,7 +731,11 @@ hipError_t launch_nt(const T* X, const T* Wg, const float* bias, int T_tokens, i
                      float* w, unsigned char* scratch, bool select, const RouteExtra& x, hipStream_t stream) {
   if constexpr (std::is_same<T, uint16_t>::value) {
     if (lds_router(kDtypeBF16, T_tokens, d, E))
-      return launch_lds<NT>(X, Wg, bias, T_tokens, d, E, k, ids, w, x, stream);
+      return launch_lds<NT>(X, Wg, bias, T_tokens, d, E, k, ids, w, x, 1, nullptr, nullptr, stream);
+    if (const int ns = lds_router_slices(kDtypeBF16, T_tokens, d, E); ns > 1)
+      return launch_lds<NT>(X, Wg, bias, T_tokens, d, E, k, ids, w, x, ns,
+                            reinterpret_cast<float*>(scratch + gate_t_bytes(d, E, sizeof(T))),
+                            reinterpret_cast<uint16_t*>(scratch), stream);
   }
   T* WgT = reinterpret_cast<T*>(scratch);
   float* partial = reinterpret_cast<float*>(scratch + gate_t_bytes(d, E, sizeof(T)));
@@ -649,6 +777,10 @@ size_t router_scratch_bytes(int T_tokens, int d, int E, int dtype) {
   const int nsplit = (d + split_len - 1) / split_len;
   size_t b = gate_t_bytes(d, E, esize);
   if (nsplit > 1) b += static_cast<size_t>(nsplit) * T_tokens * E * sizeof(float);
+  // the split LDS router's partial logits in fragment order (16 x 16*NT per
+  // tile and slice; it never splits for few tokens)
+  if (const int ns = lds_router_slices(dtype, T_tokens, d, E); ns > 1)
+    b += static_cast<size_t>(ns) * ((T_tokens + 15) / 16) * 16 * ((E + 15) / 16 * 16) * sizeof(float);
   return b;
 }
 

@@ -122,14 +122,17 @@ def test_route_exact_ties_go_to_lower_id(T, d, E, k, dt):
 
 
 @pytest.mark.parametrize("T,d,E,k", [(12000, 256, 16, 2), (40000, 128, 8, 2), (9000, 128, 40, 3), (5000, 256, 5, 2),
-                                     (20000, 2048, 32, 2), (17000, 2048, 64, 2), (16400, 1536, 50, 3)],
+                                     (20000, 2048, 32, 2), (17000, 2048, 64, 2), (16400, 1536, 50, 3),
+                                     (16389, 4096, 64, 2), (5000, 4096, 24, 3)],
                          ids=["t12000_rows4", "t40000_two_passes", "e40_nt3", "e5_gathered_gate", "t20000_d2048",
-                              "gate_in_l2_64tok_blocks", "gate_in_l2_e50_k3"])
+                              "gate_in_l2_64tok_blocks", "gate_in_l2_e50_k3", "gate_slices4_d4096_ragged",
+                              "gate_slices2_e24"])
 def test_route_many_tokens(T, d, E, k):
     """Router shapes where one block per CU covers 48-128 tokens per pass
     (and a second pass past 32768 tokens), with gates whose expert count is
-    or is not a multiple of 8; and gates too large for LDS with enough
-    tokens for 64-token blocks (ragged last block)."""
+    or is not a multiple of 8; and gates too large for LDS whole, which the
+    router cuts into K slices of at most 64K gate elements (2 or 4 slices,
+    ragged last block)."""
     inp = workloads.random_case(71 + T, T, d, E, k, 64, "bf16", -1, 0.7, w_scale=0.05)
     cfg = moe.config(T, d, 64, E, k, -1, "bf16")
     X, Wg = to_dev(inp.X, "bf16"), to_dev(inp.Wg, "bf16")
@@ -191,8 +194,9 @@ def test_route_stats(case, tau):
         assert np.array_equal(ids0.cpu().numpy(), ids) and np.array_equal(tw0.cpu().numpy(), tw)
 
 
-@pytest.mark.parametrize("T,d,E,k", [(12000, 256, 16, 2), (40000, 128, 8, 2), (9000, 128, 40, 3)],
-                         ids=["t12000_rows4", "t40000_two_passes", "e40_nt3"])
+@pytest.mark.parametrize("T,d,E,k", [(12000, 256, 16, 2), (40000, 128, 8, 2), (9000, 128, 40, 3),
+                                     (16389, 4096, 64, 2)],
+                         ids=["t12000_rows4", "t40000_two_passes", "e40_nt3", "gate_slices4_d4096"])
 def test_route_stats_many_tokens(T, d, E, k):
     inp = workloads.random_case(171 + T, T, d, E, k, 64, "bf16", -1, 0.7, w_scale=0.05)
     _check_route_stats(inp, moe.config(T, d, 64, E, k, -1, "bf16"), 0.7)

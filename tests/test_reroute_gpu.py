@@ -289,3 +289,28 @@ def test_nan_token_keeps_routing_total(T, d, E, k, cap):
     assert np.array_equal(o[others], order0.cpu().numpy()[others])
     got = _dispatch_reroute(cfg, ids_np, o, Xn, T, E, k, d)
     _check_exact(got, oracle.dispatch(ids_np, E, cap, o), T * k)
+
+
+@pytest.mark.parametrize("T,d,E,k", [(5000, 4096, 64, 2), (4200, 2048, 64, 4)], ids=["slices4", "slices2"])
+def test_route_ranked_gate_slices(T, d, E, k):
+    """The router that cuts a gate too large for LDS into K slices: the
+    preference order is the oracle's (near-ties aside) and its first k
+    entries are moe_route's ids, bit for bit."""
+    inp = workloads.random_case(5 + T, T, d, E, k, 64, "bf16", -1, 0.7, w_scale=0.05)
+    cfg = moe.config(T, d, 64, E, k, -1, "bf16")
+    X, Wg, bias = to_dev(inp.X, "bf16"), to_dev(inp.Wg, "bf16"), to_dev(inp.bias, "f32")
+    ids, tw, order = _route_ranked(cfg, X, Wg, bias, T, E, k)
+    ids0 = torch.empty_like(ids)
+    tw0 = torch.empty_like(tw)
+    rws = torch.empty(max(1, moe.moe_workspace_size(cfg, moe.MOE_OP_ROUTE)), dtype=torch.uint8, device="cuda")
+    moe.moe_route(cfg, X, Wg, bias, ids0, tw0, rws)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids0) and torch.equal(tw, tw0)
+    o = order.cpu().numpy().astype(np.int64)
+    assert (np.sort(o, axis=1) == np.arange(E)).all()
+    assert (o[:, :k] == ids.cpu().numpy()).all()
+    r = oracle.route(oracle.as_f64(inp.X, "bf16"), oracle.as_f64(inp.Wg, "bf16"), inp.bias, k)
+    check_routing(ids.cpu().numpy(), tw.cpu().numpy(), r)
+    ref, margin = oracle.expert_ranking(r.probs)
+    bad = (o != ref).any(axis=1) & (margin >= TIE_MARGIN)
+    assert not bad.any(), f"order differs on {int(bad.sum())} tokens without a near-tie"
