@@ -41,16 +41,16 @@ METRIC = "MoE-layer tokens/sec at 1 GPU; % bf16 MFMA peak (FFN) / % HBM peak (re
 # WRITE_SIZE (KiB per dispatch), scaled by what the same counters read for a
 # plain 1 GiB device copy (FETCH_SIZE x2.0, WRITE_SIZE x1.0); valid only for
 # the GEMM source they were taken on (sha1 prefix), else reported as null.
-TRAFFIC_SOURCE_SHA1 = "99bae6925e6f"
+TRAFFIC_SOURCE_SHA1 = "49884abe60af"
 TRAFFIC_BYTES = {  # (workload, stage) -> (fetch KiB, write KiB) per dispatch, raw counter values
-    ("prefill", "expert_up"): (476088.9, 180226.3),
-    ("prefill", "expert_down"): (802335.4, 65536.2),
-    ("capacity", "expert_up"): (830483.9, 285269.4),
-    ("capacity", "expert_down"): (717762.6, 415605.1),
-    ("skewed", "expert_up"): (7229923.1, 918933.6),
-    ("skewed", "expert_down"): (6423522.8, 262171.6),
-    ("decode", "expert_up"): (122723.7, 80.0),
-    ("decode", "expert_down"): (122812.6, 112.0),
+    ("skewed", "expert_up"): (7083529.3, 918354.6),
+    ("skewed", "expert_down"): (6339288.4, 264606.5),
+    ("prefill", "expert_up"): (470459.9, 180281.5),
+    ("prefill", "expert_down"): (518061.6, 65539.5),
+    ("capacity", "expert_up"): (776892.0, 285357.8),
+    ("capacity", "expert_down"): (592510.5, 417092.1),
+    ("decode", "expert_up"): (122263.0, 80.0),
+    ("decode", "expert_down"): (122352.2, 112.0),
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 
