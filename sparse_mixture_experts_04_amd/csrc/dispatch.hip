@@ -17,7 +17,9 @@
 // a wave ballot that matches expert ids bit by bit (7 ballots per slot).
 // No global atomics, so the result is deterministic.
 //
-// Kernels (dropless): count -> scan -> scatter.
+// Kernels (dropless): count -> scatter with the scan folded in (each block
+// sums the chunk histograms it needs), or count -> scan -> scatter when the
+// histograms are too large for every block to sum.
 // Kernels (capacity): count per (slot, expert) -> scan (priority bases and
 // offsets) -> keep -> scan of kept counts -> scatter.
 #include <type_traits>
@@ -138,24 +140,32 @@ __device__ __forceinline__ void load_keep(const int8_t* __restrict__ keep, int t
   }
 }
 
-// Histogram of one chunk: cols = E (dropless, col = e) or k*E (capacity, col = s*E + e).
+// Histogram of one chunk: cols = E (dropless, col = e) or k*E (capacity,
+// col = s*E + e), stored as row blockIdx.x of hist with row stride `stride`
+// (>= cols, at most 64 when dropless; the columns past cols get zero).  One
+// wave, a token per lane; for each slot lane e counts the lanes holding
+// expert e from the expert-id-bit ballots, so no cell takes atomics (a
+// skewed routing would serialise them on its few hot experts).
 __global__ __launch_bounds__(kWave) void dispatch_count_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
-                                                               bool per_slot, int32_t* __restrict__ hist) {
-  extern __shared__ int s_hist[];
-  const int cols = per_slot ? k * E : E;
-  for (int c = threadIdx.x; c < cols; c += kWave) s_hist[c] = 0;
-  __syncthreads();
-  const int t = blockIdx.x * kDispatchChunk + threadIdx.x;
+                                                               bool per_slot, int stride,
+                                                               int32_t* __restrict__ hist) {
+  const int lane = threadIdx.x;
+  const int t = blockIdx.x * kDispatchChunk + lane;
+  int32_t* out = hist + static_cast<int64_t>(blockIdx.x) * stride;
+  int cnt = 0;
   for (int s0 = 0; s0 < k; s0 += 8) {
     int e[8];
     load_ids(ids, t, T, k, E, s0, e);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (e[j] != kNone) atomicAdd(&s_hist[per_slot ? (s0 + j) * E + e[j] : e[j]], 1);
+    for (int j = 0; j < 8; ++j) {
+      if (s0 + j < k) {
+        const int c = __popcll(match(ballots_of(e[j]), lane));
+        if (!per_slot) cnt += c;
+        else if (lane < E) out[(s0 + j) * E + lane] = c;
+      }
+    }
   }
-  __syncthreads();
-  int32_t* out = hist + static_cast<int64_t>(blockIdx.x) * cols;
-  for (int c = threadIdx.x; c < cols; c += kWave) out[c] = s_hist[c];
+  if (!per_slot && lane < stride) out[lane] = cnt;
 }
 
 enum ScanMode { kScanDropless = 0, kScanCapacity1 = 1, kScanCapacity2 = 2, kScanOffsets = 3 };
@@ -596,6 +606,142 @@ __global__ __launch_bounds__(kScatterThreads) void dispatch_scatter_kernel(
   copy_rows<kScatterThreads>(X, Xp, d, k, tok0, min(kScatterTok, T_tok - tok0), &s_row[0][0], KMAX);
 }
 
+// Dropless rows with the scan folded into the scatter, so the dispatch is
+// two launches (count, then this).  Every block sums the count kernel's
+// per-chunk histograms H[c][e] (row stride Ep = E rounded up to 4, padded
+// with zeros) for itself: tot[e] over all chunks and pre[e] over the chunks
+// before its own; offsets = exclusive scan of tot, and its pairs' rows
+// follow as in dispatch_scatter_kernel with offsets[e] + pre[e] as the
+// chunk's base.  The sums are integer, so every block holds the bits one
+// scan would give.  A block covers ntb = 64 tokens (one chunk) when it only
+// writes indices, or 16 (a quarter chunk, four blocks summing the same
+// histograms) when it also copies rows, for more blocks on the copy.  The
+// reads cost nblocks * nchunks * Ep * 4 bytes of L2, so the launcher takes
+// this path only while nchunks * Ep <= kScanScatterMaxCells.  Block 0 writes
+// counts and offsets; all blocks share the -1 tail of perm.
+constexpr int kScanScatterMaxCells = 16384;  // 64 KB of histograms per block
+constexpr int kScanScatterBatch = 16;        // 16-byte loads in flight per thread
+
+template <typename T, int KMAX>
+__global__ __launch_bounds__(kScatterThreads) void dispatch_scan_scatter_kernel(
+    const int32_t* __restrict__ ids, const T* __restrict__ X, int T_tok, int d, int E, int k, int ntb,
+    const int32_t* __restrict__ H, int Ep, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm, T* __restrict__ Xp) {
+  __shared__ u32x4_t s_tot[kScatterThreads];
+  __shared__ u32x4_t s_pre[kScatterThreads];
+  __shared__ int s_base[kMaxExperts];
+  __shared__ int s_N;
+  __shared__ int s_row[kDispatchChunk][KMAX];
+  const int tid = threadIdx.x;
+  const int tok0 = blockIdx.x * ntb;
+  const int chunk = tok0 / kDispatchChunk;
+  const int nchunks = (T_tok + kDispatchChunk - 1) / kDispatchChunk;
+  const int total_pairs = T_tok * k;
+  // Thread (cg, g) sums columns 4cg .. 4cg+3 over rows g, g + G, ...
+  const int ncg = Ep / 4;
+  const int G = kScatterThreads / ncg;
+  const int cg = tid % ncg;
+  const int g = tid / ncg;
+  // Wave 0's id loads go out first, to overlap the histogram reads.
+  const int lane = tid % kWave;
+  const int t = chunk * kDispatchChunk + lane;
+  int e[KMAX];
+  if (tid < kWave) load_ids(ids, t, T_tok, k, E, 0, e);
+  u32x4_t tot = {0u, 0u, 0u, 0u};
+  u32x4_t pre = {0u, 0u, 0u, 0u};
+  if (g < G) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(H), 0, nchunks * Ep * 4, 0x00020000);
+    for (int r0 = g; r0 < nchunks; r0 += G * kScanScatterBatch) {
+      u32x4_t v[kScanScatterBatch];
+#pragma unroll
+      for (int q = 0; q < kScanScatterBatch; ++q) {
+        const int row = r0 + q * G;
+        const int off = row < nchunks ? (row * Ep + cg * 4) * 4 : static_cast<int>(0x80000000u);
+        v[q] = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < kScanScatterBatch; ++q) {
+        tot += v[q];
+        if (r0 + q * G < chunk) pre += v[q];
+      }
+    }
+  }
+  s_tot[tid] = tot;
+  s_pre[tid] = pre;
+  __syncthreads();
+  if (tid < kWave) {
+    // Lane e: expert e's total and prefix, then the exclusive scan over e.
+    int te = 0;
+    int pe = 0;
+    if (lane < E) {
+      const int* st = reinterpret_cast<const int*>(s_tot);
+      const int* sp = reinterpret_cast<const int*>(s_pre);
+      for (int q = 0; q < G; ++q) {
+        te += st[q * Ep + lane];
+        pe += sp[q * Ep + lane];
+      }
+    }
+    int incl = te;
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) {
+      const int o = __shfl_up(incl, m);
+      if (lane >= m) incl += o;
+    }
+    const int excl = incl - te;
+    const int N = __shfl(incl, kWave - 1);
+    if (lane < E) s_base[lane] = excl + pe;
+    if (lane == 0) s_N = N;
+    if (blockIdx.x == 0) {
+      if (lane < E) {
+        counts[lane] = te;
+        offsets[lane] = excl;
+      }
+      if (lane == 0) offsets[E] = N;
+    }
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    // Ranks within the chunk, as in dispatch_scatter_kernel.
+    const uint64_t below = (1ull << lane) - 1ull;
+    int cnt[KMAX];
+#pragma unroll
+    for (int s = 0; s < KMAX; ++s) cnt[s] = 0;
+#pragma unroll
+    for (int s2 = 0; s2 < KMAX; ++s2) {
+      if (s2 < k) {
+        const Ballots B = ballots_of(e[s2]);
+#pragma unroll
+        for (int s = 0; s < KMAX; ++s)
+          if (s < k) cnt[s] += __popcll(match(B, e[s]) & below);
+      }
+    }
+    const bool mine = t >= tok0 && t < tok0 + ntb;
+#pragma unroll
+    for (int s = 0; s < KMAX; ++s) {
+      if (s < k && mine) {
+        int row = -1;
+        if (e[s] != kNone) {
+          int same = 0;
+#pragma unroll
+          for (int s2 = 0; s2 < KMAX; ++s2)
+            if (s2 < s && e[s2] == e[s]) ++same;
+          row = s_base[e[s]] + cnt[s] + same;
+          if (row < 0 || row >= total_pairs) row = -1;  // unreachable for consistent histograms; keeps stores in bounds
+          if (t < T_tok && row >= 0) perm[row] = t * k + s;
+        }
+        if (t < T_tok) inv_perm[static_cast<int64_t>(t) * k + s] = row;
+        s_row[t - tok0][s] = (t < T_tok) ? row : -1;
+      }
+    }
+  }
+  for (int q = s_N + blockIdx.x * kScatterThreads + tid; q < total_pairs; q += gridDim.x * kScatterThreads)
+    perm[q] = -1;
+  if (Xp == nullptr) return;
+  __syncthreads();
+  copy_rows<kScatterThreads>(X, Xp, d, k, tok0, min(ntb, T_tok - tok0), &s_row[0][0], KMAX);
+}
+
 // Small T (<= 256 tokens, k <= 8): the whole dispatch in one block of 4
 // waves, one 64-token chunk per wave -- histogram, scans, capacity cut,
 // ranks, perm/inv_perm and the row copy -- so decode pays one launch.
@@ -798,13 +944,39 @@ hipError_t launch_scatter(bool cap, int nblocks, const int32_t* ids, const T* X,
   return launch_scatter_k<T, kMaxExperts>(cap, nblocks, ids, X, T_tok, d, E, k, cb, offsets, keep, perm, inv_perm, Xp, stream);
 }
 
+template <typename T, int KMAX>
+hipError_t launch_scan_scatter_k(int nblocks, int ntb, const int32_t* ids, const T* X, int T_tok, int d, int E, int k,
+                                 const int32_t* H, int Ep, int32_t* counts, int32_t* offsets, int32_t* perm,
+                                 int32_t* inv_perm, T* Xp, hipStream_t stream) {
+  hipLaunchKernelGGL((dispatch_scan_scatter_kernel<T, KMAX>), dim3(nblocks), dim3(kScatterThreads), 0, stream, ids, X,
+                     T_tok, d, E, k, ntb, H, Ep, counts, offsets, perm, inv_perm, Xp);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_scan_scatter(int nblocks, int ntb, const int32_t* ids, const T* X, int T_tok, int d, int E, int k,
+                               const int32_t* H, int Ep, int32_t* counts, int32_t* offsets, int32_t* perm,
+                               int32_t* inv_perm, T* Xp, hipStream_t stream) {
+  if (k <= 2)
+    return launch_scan_scatter_k<T, 2>(nblocks, ntb, ids, X, T_tok, d, E, k, H, Ep, counts, offsets, perm, inv_perm,
+                                       Xp, stream);
+  if (k <= 4)
+    return launch_scan_scatter_k<T, 4>(nblocks, ntb, ids, X, T_tok, d, E, k, H, Ep, counts, offsets, perm, inv_perm,
+                                       Xp, stream);
+  if (k <= 8)
+    return launch_scan_scatter_k<T, 8>(nblocks, ntb, ids, X, T_tok, d, E, k, H, Ep, counts, offsets, perm, inv_perm,
+                                       Xp, stream);
+  return launch_scan_scatter_k<T, kMaxExperts>(nblocks, ntb, ids, X, T_tok, d, E, k, H, Ep, counts, offsets, perm,
+                                               inv_perm, Xp, stream);
+}
+
 size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
 }  // namespace
 
 size_t dispatch_scratch_bytes(int T, int E, int k, bool capacity, bool reroute) {
   const size_t nchunks = (static_cast<size_t>(T) + kDispatchChunk - 1) / kDispatchChunk;
-  size_t b = align256(nchunks * (capacity ? k * E : E) * sizeof(int32_t));
+  size_t b = align256(nchunks * (capacity ? k * E : (E + 3) & ~3) * sizeof(int32_t));
   if (capacity) {
     b += align256(nchunks * E * sizeof(int32_t));
     b += align256(static_cast<size_t>(k) * E * sizeof(int32_t));
@@ -828,7 +1000,7 @@ DispatchScratch carve_dispatch_scratch(void* ws, int T, int E, int k, bool capac
   unsigned char* p = static_cast<unsigned char*>(ws);
   DispatchScratch s{};
   s.chunk_base = reinterpret_cast<int32_t*>(p);
-  p += align256(nchunks * (capacity ? k * E : E) * sizeof(int32_t));
+  p += align256(nchunks * (capacity ? k * E : (E + 3) & ~3) * sizeof(int32_t));
   if (capacity) {
     s.chunk_kept = reinterpret_cast<int32_t*>(p);
     p += align256(nchunks * E * sizeof(int32_t));
@@ -934,8 +1106,23 @@ hipError_t launch_dispatch(int dtype, const int32_t* ids, const void* X, int T, 
     return hipGetLastError();
   }
   const int cols = cap ? k * E : E;
-  hipLaunchKernelGGL(dispatch_count_kernel, dim3(nchunks), dim3(kWave), cols * sizeof(int), stream, ids, T, E, k, cap,
-                     sc.chunk_base);
+  const int Ep = (E + 3) & ~3;
+  if (!cap && static_cast<int64_t>(nchunks) * Ep <= kScanScatterMaxCells) {
+    // Dropless, histograms small enough for every block to sum: two launches.
+    hipLaunchKernelGGL(dispatch_count_kernel, dim3(nchunks), dim3(kWave), 0, stream, ids, T, E, k,
+                       false, Ep, sc.chunk_base);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    const int ntb = Xp != nullptr ? kScatterTok : kDispatchChunk;
+    const int nblocks = (T + ntb - 1) / ntb;
+    if (dtype == kDtypeBF16)
+      return launch_scan_scatter<uint16_t>(nblocks, ntb, ids, static_cast<const uint16_t*>(X), T, d, E, k,
+                                           sc.chunk_base, Ep, counts, offsets, perm, inv_perm,
+                                           static_cast<uint16_t*>(Xp), stream);
+    return launch_scan_scatter<float>(nblocks, ntb, ids, static_cast<const float*>(X), T, d, E, k, sc.chunk_base, Ep,
+                                      counts, offsets, perm, inv_perm, static_cast<float*>(Xp), stream);
+  }
+  hipLaunchKernelGGL(dispatch_count_kernel, dim3(nchunks), dim3(kWave), 0, stream, ids, T, E, k, cap,
+                     cols, sc.chunk_base);
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, sc.chunk_base, nchunks, cols,
                      static_cast<int>(cap ? kScanCapacity1 : kScanDropless), E, k, capacity, counts, offsets,
                      sc.slot_base, perm, total_pairs);
@@ -968,8 +1155,8 @@ hipError_t launch_dispatch_reroute(int dtype, const int32_t* ids, const uint8_t*
   const int nchunks = (T + kDispatchChunk - 1) / kDispatchChunk;
   const int total_pairs = T * k;
   const int cols = k * E;
-  hipLaunchKernelGGL(dispatch_count_kernel, dim3(nchunks), dim3(kWave), cols * sizeof(int), stream, ids, T, E, k, true,
-                     sc.chunk_base);
+  hipLaunchKernelGGL(dispatch_count_kernel, dim3(nchunks), dim3(kWave), 0, stream, ids, T, E, k, true,
+                     cols, sc.chunk_base);
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, sc.chunk_base, nchunks, cols,
                      static_cast<int>(kScanCapacity1), E, k, capacity, counts, offsets, sc.slot_base, perm,
                      total_pairs);

@@ -16,7 +16,7 @@ constexpr int kMaxExpertsAbi = 64;  // expert ids fit one wave (64 lanes)
 
 // Scratch of the dispatcher, carved from the caller's workspace.
 struct DispatchScratch {
-  int32_t* chunk_base;   // [nchunks][cols]: per-chunk histogram, then its chunk-exclusive prefix
+  int32_t* chunk_base;   // [nchunks][cols] (dropless: cols rounded up to 4): per-chunk histogram, then (three-launch path) its chunk-exclusive prefix
   int32_t* chunk_kept;   // [nchunks][E]:  kept pairs per chunk, then prefix (capacity only)
   int32_t* slot_base;    // [k][E]: pairs of expert e in slots < s (capacity only)
   int8_t* keep;          // [T*k]: keep flag per pair (capacity only)

@@ -353,6 +353,42 @@ def test_expert_up_gather_bad_perm_entries(T, d, F, E, k, bad, offsets):
     assert_close(got[good], ref[good], "bf16", "H")
 
 
+@pytest.mark.parametrize("T,E,k,skew,copy", [
+    (16384, 64, 2, 1.2, False),   # chunk histograms exactly at the two-launch limit (256 chunks x 64 experts)
+    (16385, 64, 2, 1.2, False),   # one chunk past it: count, scan, scatter
+    (16384, 64, 2, 1.2, True),    # the two-launch path with the row copy (quarter-chunk blocks)
+    (100000, 5, 2, 0.0, True),    # experts padded from 5 to 8 columns
+    (150000, 5, 3, 0.5, False),   # past the limit with padding
+    (20000, 40, 3, 0.8, True),
+    (4097, 33, 1, 0.0, False),    # one token past a chunk boundary
+], ids=["at_limit", "past_limit", "at_limit_copy", "e5_padded_copy", "e5_past_limit", "e40_k3_copy", "e33_k1"])
+def test_dispatch_ids_many_tokens(T, E, k, skew, copy):
+    """moe_dispatch on given ids (Zipf-weighted, repeated ids within a token
+    allowed) equals the oracle's counting sort, on both sides of the size
+    where the scan moves out of the scatter into a launch of its own."""
+    rng = np.random.default_rng(900 + T + E + k)
+    p = 1.0 / (np.arange(E) + 1.0) ** skew
+    ids_np = rng.choice(E, size=(T, k), p=p / p.sum()).astype(np.int32)
+    disp = oracle.dispatch(ids_np, E, -1)
+    d = 64
+    Tk = T * k
+    cfg = moe.config(T, d, 64, E, k, -1, "bf16")
+    X = (torch.randn(T, d, generator=torch.Generator().manual_seed(T)) * 0.5).to(torch.bfloat16).cuda()
+    ids = torch.from_numpy(ids_np).cuda()
+    counts = torch.full((E,), -7, dtype=torch.int32, device="cuda")
+    offsets = torch.full((E + 1,), -7, dtype=torch.int32, device="cuda")
+    perm = torch.full((Tk,), -7, dtype=torch.int32, device="cuda")
+    inv = torch.full((Tk,), -7, dtype=torch.int32, device="cuda")
+    Xp = torch.zeros((Tk, d), dtype=torch.bfloat16, device="cuda") if copy else None
+    ws = torch.empty(max(1, moe.moe_workspace_size(cfg, moe.MOE_OP_DISPATCH)), dtype=torch.uint8, device="cuda")
+    moe.moe_dispatch(cfg, ids, X, counts, offsets, perm, inv, Xp, ws)
+    torch.cuda.synchronize()
+    check_dispatch_exact(counts.cpu().numpy(), offsets.cpu().numpy(), perm.cpu().numpy(), inv.cpu().numpy(), disp, Tk)
+    if copy:
+        src = torch.from_numpy((disp.perm // k).astype(np.int64)).cuda()
+        assert torch.equal(Xp, X[src]), "gathered rows differ"
+
+
 @pytest.mark.parametrize("case", GATHER_CASES, ids=[c[0] for c in GATHER_CASES])
 def test_dispatch_indices_only(case):
     """moe_dispatch with Xp = NULL writes the same indices."""
