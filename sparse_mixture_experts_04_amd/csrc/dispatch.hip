@@ -195,13 +195,15 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(int32_t* __
     const int L = (nrows + P - 1) / P;
     const int r0 = p * L;
     const int r1 = min(nrows, r0 + L);
-    // Rows go in batches of kScanBatch independent loads, so a thread's
-    // L rows cost ceil(L / kScanBatch) memory round trips per pass.  The
+    // Up to kScanRegRows rows per thread are loaded once, all together;
+    // beyond that rows go in batches of kScanBatch independent loads, so a
+    // thread's L rows cost ceil(L / kScanBatch) memory round trips per pass.  The
     // loads go through a buffer resource over M: a row past the thread's
     // range takes an offset beyond the resource and reads zero, so no load
     // sits behind a branch (which would serialise them).  M beyond 2^31
     // bytes (past 8 M tokens at k*E = 4096 columns) uses plain loads.
     constexpr int kScanBatch = 16;
+    constexpr int kScanRegRows = 64;  // rows per thread held in registers when they all fit
     const __amdgpu_buffer_rsrc_t mrsrc =
         __builtin_amdgcn_make_buffer_rsrc(M, 0, nrows * ncols * 4, 0x00020000);
     auto scan_col = [&](auto buffered_c) {
@@ -214,6 +216,34 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(int32_t* __
           return static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(mrsrc, off, 0, 0));
         }
       };
+      // All of the thread's rows in registers (16, 32 or 64 loads, the fewest
+      // that cover them; past 32 only the thread's L, which keeps the
+      // registers within the kernel's budget): one round of loads serves
+      // both passes.
+      auto reg_rows = [&](auto n_c) {
+        constexpr int kN = decltype(n_c)::value;
+        int v[kN];
+#pragma unroll
+        for (int j = 0; j < kN; ++j) v[j] = kN <= 32 || j < L ? load_row(r0 + j) : 0;  // rows past r1 read zero
+        int sum = 0;
+#pragma unroll
+        for (int j = 0; j < kN; ++j) sum += v[j];
+        s_part[tid] = sum;
+        __syncthreads();
+        if (p < P) {
+          int base = 0;
+          for (int q = 0; q < p; ++q) base += s_part[q * gcols + ci];
+          if (p == P - 1) s_tot[col0 + ci] = base + sum;
+#pragma unroll
+          for (int j = 0; j < kN; ++j) {
+            if (r0 + j < r1) M[static_cast<int64_t>(r0 + j) * ncols + col0 + ci] = base;
+            base += v[j];
+          }
+        }
+      };
+      if (kBuf && L <= 16) return reg_rows(std::integral_constant<int, 16>{});
+      if (kBuf && L <= 32) return reg_rows(std::integral_constant<int, 32>{});
+      if (kBuf && L <= kScanRegRows) return reg_rows(std::integral_constant<int, kScanRegRows>{});
       int sum = 0;
       if (p < P)
         for (int rb = r0; rb < r1; rb += kScanBatch) {
@@ -245,39 +275,41 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(int32_t* __
     else scan_col(std::false_type{});
     __syncthreads();
   }
-  if (tid == 0) {
-    if (mode == kScanDropless) {
-      int acc = 0;
-      for (int e = 0; e < E; ++e) {
+  if (tid < kWave) {
+    // Lane e: expert e's total (and, capacity1, its slot bases), then the
+    // offsets as an exclusive scan over the lanes.
+    const int e = tid;
+    int add = 0;  // what expert e adds to the offsets
+    if (e < E) {
+      if (mode == kScanDropless) {
         counts[e] = s_tot[e];
-        offsets[e] = acc;
-        acc += s_tot[e];
-      }
-      offsets[E] = acc;
-      s_N = acc;
-    } else if (mode == kScanCapacity1) {
-      int acc = 0;
-      for (int e = 0; e < E; ++e) {
+        add = s_tot[e];
+      } else if (mode == kScanCapacity1) {
         int n = 0;
         for (int s = 0; s < k; ++s) {
           slot_base[s * E + e] = n;
           n += s_tot[s * E + e];
         }
         counts[e] = n;
-        offsets[e] = acc;
-        acc += min(n, capacity);
+        add = min(n, capacity);
+      } else if (mode == kScanOffsets) {
+        add = s_tot[e];
       }
-      offsets[E] = acc;
-      s_N = acc;
-    } else if (mode == kScanOffsets) {
-      int acc = 0;
-      for (int e = 0; e < E; ++e) {
-        offsets[e] = acc;
-        acc += s_tot[e];
+    }
+    if (mode != kScanCapacity2) {
+      int incl = add;
+#pragma unroll
+      for (int m = 1; m < kWave; m <<= 1) {
+        const int o = __shfl_up(incl, m);
+        if (e >= m) incl += o;
       }
-      offsets[E] = acc;
-      s_N = acc;
-    } else {
+      if (e < E) offsets[e] = incl - add;
+      const int total = __shfl(incl, kWave - 1);
+      if (e == 0) {
+        offsets[E] = total;
+        s_N = total;
+      }
+    } else if (e == 0) {
       s_N = offsets[E];
     }
   }
