@@ -361,7 +361,11 @@ def test_expert_up_gather_bad_perm_entries(T, d, F, E, k, bad, offsets):
     (150000, 5, 3, 0.5, False),   # past the limit with padding
     (20000, 40, 3, 0.8, True),
     (4097, 33, 1, 0.0, False),    # one token past a chunk boundary
-], ids=["at_limit", "past_limit", "at_limit_copy", "e5_padded_copy", "e5_past_limit", "e40_k3_copy", "e33_k1"])
+    (16381, 64, 2, 1.2, True),    # ragged: the last quarter-chunk block copies 13 tokens
+    (3001, 16, 6, 0.3, True),     # 5..8 slots per token
+    (2999, 24, 12, 0.3, False),   # more than 8 slots per token
+], ids=["at_limit", "past_limit", "at_limit_copy", "e5_padded_copy", "e5_past_limit", "e40_k3_copy", "e33_k1",
+        "ragged_copy", "k6_copy", "k12"])
 def test_dispatch_ids_many_tokens(T, E, k, skew, copy):
     """moe_dispatch on given ids (Zipf-weighted, repeated ids within a token
     allowed) equals the oracle's counting sort, on both sides of the size
@@ -369,6 +373,8 @@ def test_dispatch_ids_many_tokens(T, E, k, skew, copy):
     rng = np.random.default_rng(900 + T + E + k)
     p = 1.0 / (np.arange(E) + 1.0) ** skew
     ids_np = rng.choice(E, size=(T, k), p=p / p.sum()).astype(np.int32)
+    if k > 2:  # also repeated ids within a token at other slot pairs
+        ids_np[::7, k - 1] = ids_np[::7, 0]
     disp = oracle.dispatch(ids_np, E, -1)
     d = 64
     Tk = T * k
