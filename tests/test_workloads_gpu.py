@@ -48,6 +48,13 @@ def run_and_check(inp, X_np=None, report=None, sample="all"):
     out = layer.forward(Xd)
     torch.cuda.synchronize()
     b = layer.buf
+    # at full size too the layer is deterministic: a second forward gives the same bits, indices included
+    first = [t.clone() for t in (out, b.topk_ids, b.topk_w, b.expert_offsets, b.perm, b.inv_perm)]
+    layer.forward(Xd)
+    torch.cuda.synchronize()
+    for f, t in zip(first, (b.out, b.topk_ids, b.topk_w, b.expert_offsets, b.perm, b.inv_perm)):
+        assert torch.equal(f, t), "a second forward differs"
+    out = b.out
     ids_g = b.topk_ids.cpu().numpy()
     r = oracle.route(oracle.as_f64(X_np, w.dtype), oracle.as_f64(inp.Wg, w.dtype), inp.bias, w.k)
     disp = oracle.dispatch(r.ids, w.E, inp.expert_capacity)
