@@ -141,11 +141,12 @@ __device__ __forceinline__ void load_keep(const int8_t* __restrict__ keep, int t
 }
 
 // Histogram of one chunk: cols = E (dropless, col = e) or k*E (capacity,
-// col = s*E + e), stored as row blockIdx.x of hist with row stride `stride`
-// (>= cols, at most 64 when dropless; the columns past cols get zero).  One
-// wave, a token per lane; for each slot lane e counts the lanes holding
-// expert e from the expert-id-bit ballots, so no cell takes atomics (a
-// skewed routing would serialise them on its few hot experts).
+// col = s*E + e), stored as row blockIdx.x of hist with row stride `stride`.
+// Dropless rows may be padded (cols <= stride <= 64; the padding gets
+// zeros); capacity rows are not (stride = cols).  One wave, a token per lane;
+// for each slot lane e counts the lanes holding expert e from the
+// expert-id-bit ballots, so no cell takes atomics (a skewed routing would
+// serialise them on its few hot experts).
 __global__ __launch_bounds__(kWave) void dispatch_count_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
                                                                bool per_slot, int stride,
                                                                int32_t* __restrict__ hist) {
