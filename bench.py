@@ -43,14 +43,14 @@ METRIC = "MoE-layer tokens/sec at 1 GPU; % bf16 MFMA peak (FFN) / % HBM peak (re
 # the GEMM source they were taken on (sha1 prefix), else reported as null.
 TRAFFIC_SOURCE_SHA1 = "49884abe60af"
 TRAFFIC_BYTES = {  # (workload, stage) -> (fetch KiB, write KiB) per dispatch, raw counter values
-    ("skewed", "expert_up"): (7141491.3, 918310.3),
-    ("skewed", "expert_down"): (6334009.3, 264790.5),
-    ("prefill", "expert_up"): (467831.5, 180274.2),
-    ("prefill", "expert_down"): (518057.1, 65539.1),
-    ("capacity", "expert_up"): (770128.1, 285360.1),
-    ("capacity", "expert_down"): (596026.4, 417098.5),
-    ("decode", "expert_up"): (122262.9, 80.1),
-    ("decode", "expert_down"): (122352.3, 112.0),
+    ("skewed", "expert_up"): (7085544.3, 918318.1),
+    ("skewed", "expert_down"): (6365159.4, 264594.1),
+    ("prefill", "expert_up"): (468093.1, 180276.5),
+    ("prefill", "expert_down"): (518114.5, 65538.9),
+    ("capacity", "expert_up"): (755286.8, 285339.6),
+    ("capacity", "expert_down"): (590147.0, 417323.2),
+    ("decode", "expert_up"): (122263.0, 80.0),
+    ("decode", "expert_down"): (122352.2, 112.0),
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 
