@@ -14,7 +14,10 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("T,d,E,k,F,cap,reroute", [(300, 256, 8, 2, 384, -1, False), (8, 1024, 64, 2, 256, -1, False),
                                                    (500, 256, 16, 4, 256, 100, False),
-                                                   (2500, 256, 16, 4, 256, 500, True)])
+                                                   (2500, 256, 16, 4, 256, 500, True),
+                                                   # the skewed layer's kernels: K-sliced router (gate too large
+                                                   # for LDS), two-launch dispatch, gathered up-projection
+                                                   (4100, 4096, 64, 2, 128, -1, False)])
 def test_graph_replay_matches_eager(T, d, E, k, F, cap, reroute):
     inp = workloads.random_case(3, T, d, E, k, F, "bf16", cap, 0.3, w_scale=0.05)
     cfg = moe.config(T, d, F, E, k, cap, "bf16")
