@@ -41,16 +41,16 @@ METRIC = "MoE-layer tokens/sec at 1 GPU; % bf16 MFMA peak (FFN) / % HBM peak (re
 # WRITE_SIZE (KiB per dispatch), scaled by what the same counters read for a
 # plain 1 GiB device copy (FETCH_SIZE x2.0, WRITE_SIZE x1.0); valid only for
 # the GEMM source they were taken on (sha1 prefix), else reported as null.
-TRAFFIC_SOURCE_SHA1 = "49884abe60af"
+TRAFFIC_SOURCE_SHA1 = "d133c3efde78"
 TRAFFIC_BYTES = {  # (workload, stage) -> (fetch KiB, write KiB) per dispatch, raw counter values
-    ("skewed", "expert_up"): (7085544.3, 918318.1),
-    ("skewed", "expert_down"): (6365159.4, 264594.1),
-    ("prefill", "expert_up"): (468093.1, 180276.5),
-    ("prefill", "expert_down"): (518114.5, 65538.9),
-    ("capacity", "expert_up"): (755286.8, 285339.6),
-    ("capacity", "expert_down"): (590147.0, 417323.2),
-    ("decode", "expert_up"): (122263.0, 80.0),
-    ("decode", "expert_down"): (122352.2, 112.0),
+    ("skewed", "expert_up"): (7088717.0, 919066.7),
+    ("skewed", "expert_down"): (6337415.2, 267010.2),
+    ("prefill", "expert_up"): (468861.6, 180401.2),
+    ("prefill", "expert_down"): (518034.1, 65568.1),
+    ("capacity", "expert_up"): (741792.0, 285475.1),
+    ("capacity", "expert_down"): (590179.2, 417427.1),
+    ("decode", "expert_up"): (122264.0, 80.1),
+    ("decode", "expert_down"): (122352.3, 112.0),
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 

@@ -605,7 +605,10 @@ __global__ __launch_bounds__(kWaves * kWave) void grouped_gemm_bf16_256(const ui
   // 2*kLd loads, may still be in flight).
   wait_vmcnt<2 * kLd>();
   barrier();
-  bool after_epilogue = false;
+  // Stores of the last epilogue: issued after the next stage's data, so the
+  // stage-end wait may leave them in flight (vector memory operations
+  // retire in issue order: loads and stores count down vmcnt in one order).
+  int pending_st = 0;
 
   // One tile: all K stages with nj token fragments per wave, then its
   // epilogue.  k-step 0 of the tile's first stage is read here (the previous
@@ -634,12 +637,18 @@ __global__ __launch_bounds__(kWaves * kWave) void grouped_gemm_bf16_256(const ui
       block(nj_c, acc, wf1, xf1, 2, wf0, xf0, nullptr, nullptr);
       block(nj_c, acc, wf0, xf0, 3, wf1, xf1, nullptr, nullptr);
       // The next stage must have landed; the weight unit issued above may stay
-      // in flight (right after an epilogue its stores are outstanding too:
-      // drain).  lgkmcnt(0): this wave's reads of this stage are complete, so
-      // after the barrier its two units are free.
-      wait_vmcnt_lgkm0<kLd>();
-      if (after_epilogue) wait_vmcnt<0>();
-      after_epilogue = false;
+      // in flight, and right after an epilogue so may its stores (2 per
+      // accumulator group, issued between the next stage's token unit and
+      // that weight unit).  lgkmcnt(0): this wave's reads of this stage are
+      // complete, so after the barrier its two units are free.
+      switch (pending_st) {
+        case 0: wait_vmcnt_lgkm0<kLd>(); break;
+        case 4: wait_vmcnt_lgkm0<kLd + 4>(); break;
+        case 8: wait_vmcnt_lgkm0<kLd + 8>(); break;
+        case 12: wait_vmcnt_lgkm0<kLd + 12>(); break;
+        default: wait_vmcnt_lgkm0<kLd + 16>(); break;  // 16 (more with 4 waves: a lower count only waits longer)
+      }
+      pending_st = 0;
       barrier();
       __builtin_amdgcn_sched_barrier(0);
       c_wslot = c_wslot + 2 >= kSlots ? c_wslot + 2 - kSlots : c_wslot + 2;
@@ -650,7 +659,7 @@ __global__ __launch_bounds__(kWaves * kWave) void grouped_gemm_bf16_256(const ui
       block(nj_c, acc, wf1, xf1, 0, wf0, xf0, &xs, vx);
       advance_x(xs, gn);
     }
-    after_epilogue = true;
+    pending_st = 2 * kWF * NJ;
 
     // acc[i][j][q]: token row m0 + (2j + wm)*32 + frow, column n0 + wn*kWF*32 + i*32 + 16*fhalf + q.
     // Stores go through a buffer resource over the tile's rows of C; a
