@@ -387,7 +387,7 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": src.numel() * 4, "copies": 5}))
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus N>1 is not supported",
+        print(json.dumps({"error": "the library runs the layer on one GPU holding all experts; --gpus N>1 is not supported",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
