@@ -512,11 +512,13 @@ __global__ __launch_bounds__(kRouterThreads, 1) void router_lds_kernel(
   }
 }
 
-// Sum the K-split partial logits in split order, then top-k.  A block of 1024
-// threads owns 16 tokens: one thread per (token, expert) entry sums the splits
-// with 8 loads in flight, the sums meet in LDS, and wave 0 selects.
+// Sum the K-split partial logits in split order, then top-k.  A block of 512
+// threads owns 16 tokens: each thread sums the splits of two (token, expert)
+// entries with 8 loads in flight, the sums meet in LDS, and wave 0 selects
+// (512 threads leave the selection the registers it needs).
+constexpr int kTopkThreads = 512;
 template <int NT>
-__global__ __launch_bounds__(1024) void router_topk_kernel(const float* __restrict__ partial, int nsplit,
+__global__ __launch_bounds__(kTopkThreads) void router_topk_kernel(const float* __restrict__ partial, int nsplit,
                                                            const float* __restrict__ bias, int T_tokens, int E, int k,
                                                            int32_t* __restrict__ topk_ids,
                                                            float* __restrict__ topk_w, float inv_tau,
@@ -525,8 +527,8 @@ __global__ __launch_bounds__(1024) void router_topk_kernel(const float* __restri
   __shared__ float logit[16][kMaxExperts];
   __shared__ float sel_val[16 * kMaxExperts];
   __shared__ int sel_id[16 * kMaxExperts];
-  topk_from_partials<NT>(partial, nsplit, bias, T_tokens, E, k, blockIdx.x * 16, logit, sel_val, sel_id, topk_ids,
-                         topk_w, inv_tau, prob_sum, order);
+  topk_from_partials<NT, kTopkThreads>(partial, nsplit, bias, T_tokens, E, k, blockIdx.x * 16, logit, sel_val,
+                                       sel_id, topk_ids, topk_w, inv_tau, prob_sum, order);
 }
 
 // Sum the K-slice partial logits of router_lds_kernel<..., true> (fragment
@@ -752,8 +754,8 @@ hipError_t launch_nt(const T* X, const T* Wg, const float* bias, int T_tokens, i
                        T_tokens, d, E, k, split_len, nullptr, ids, w, x.inv_tau, x.prob_sum, x.order);
   }
   if (nsplit > 1 && select)
-    hipLaunchKernelGGL((router_topk_kernel<NT>), dim3((T_tokens + 15) / 16), dim3(1024), 0, stream, partial, nsplit,
-                       bias, T_tokens, E, k, ids, w, x.inv_tau, x.prob_sum, x.order);
+    hipLaunchKernelGGL((router_topk_kernel<NT>), dim3((T_tokens + 15) / 16), dim3(kTopkThreads), 0, stream, partial,
+                       nsplit, bias, T_tokens, E, k, ids, w, x.inv_tau, x.prob_sum, x.order);
   return hipGetLastError();
 }
 

@@ -17,17 +17,37 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
-// One step of a 16-lane arg-max: take the (value, id) of the lane that DPP
-// control kCtrl names in this lane's row of 16, keep the better.  DPP moves
-// are plain VALU operations (no LDS round trip, unlike a lane shuffle).
+// A (logit, expert) pair as a 64-bit key whose unsigned order is better()'s:
+// the high word is the logit's bit pattern mapped so that unsigned order is
+// float order (negative zero taken as positive zero, which better() treats
+// as equal), the low word is 63 - expert, so the lower id wins a tie.  Valid
+// for every non-NaN logit, infinities included, and expert ids below 64.
+__device__ __forceinline__ uint32_t ordered_bits(float v) {
+  uint32_t u = __builtin_bit_cast(uint32_t, v);
+  u = u == 0x80000000u ? 0u : u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ uint64_t pair_key(uint32_t ordered, int e) {
+  return (static_cast<uint64_t>(ordered) << 32) | static_cast<uint32_t>(63 - e);
+}
+__device__ __forceinline__ float key_value(uint64_t key) {
+  const uint32_t o = static_cast<uint32_t>(key >> 32);
+  return __builtin_bit_cast(float, (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+__device__ __forceinline__ int key_expert(uint64_t key) { return 63 - static_cast<int>(static_cast<uint32_t>(key)); }
+
+// One step of a 16-lane arg-max over four keys at once: take the keys of the
+// lane that DPP control kCtrl names in this lane's row of 16, keep the larger.
+// DPP moves are plain VALU operations (no LDS round trip, unlike a lane
+// shuffle), and the four independent chains hide each other's latency.
 template <int kCtrl>
-__device__ __forceinline__ void argmax_dpp_step(float& bv, int& bi) {
-  const float ov = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, bv), kCtrl, 0xF,
-                                                                         0xF, false));
-  const int oi = __builtin_amdgcn_update_dpp(0, bi, kCtrl, 0xF, 0xF, false);
-  if (better(ov, oi, bv, bi)) {
-    bv = ov;
-    bi = oi;
+__device__ __forceinline__ void argmax_dpp_step(uint64_t (&b)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = __builtin_amdgcn_update_dpp(0, static_cast<uint32_t>(b[i]), kCtrl, 0xF, 0xF, false);
+    const uint32_t hi = __builtin_amdgcn_update_dpp(0, static_cast<uint32_t>(b[i] >> 32), kCtrl, 0xF, 0xF, false);
+    const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+    b[i] = o > b[i] ? o : b[i];
   }
 }
 
@@ -56,13 +76,13 @@ __device__ __forceinline__ float max16(float v) {
 // Arg-max over each row of 16 lanes, left in every lane of the row: pairs
 // (quad_perm 1,0,3,2), quads (quad_perm 2,3,0,1), then the two quads of each
 // half-row (row_half_mirror: lane i with 7-i) and the two halves
-// (row_mirror: lane i with 15-i).  better() is a total order, so the result
+// (row_mirror: lane i with 15-i).  The key order is total, so the result
 // does not depend on the pairing.
-__device__ __forceinline__ void argmax16(float& bv, int& bi) {
-  argmax_dpp_step<0xB1>(bv, bi);
-  argmax_dpp_step<0x4E>(bv, bi);
-  argmax_dpp_step<0x141>(bv, bi);
-  argmax_dpp_step<0x140>(bv, bi);
+__device__ __forceinline__ void argmax16(uint64_t (&b)[4]) {
+  argmax_dpp_step<0xB1>(b);
+  argmax_dpp_step<0x4E>(b);
+  argmax_dpp_step<0x141>(b);
+  argmax_dpp_step<0x140>(b);
 }
 
 // Step R of the places in a 16-lane row: compare this lane's NT values with
@@ -170,29 +190,47 @@ __device__ __forceinline__ void topk_tile(f32x4_t (&acc)[NT], const float* __res
       }
     }
   }
+  // k rounds on the pair keys: each round takes every row's best remaining
+  // expert and gives it the key of a -inf logit (what the padding lanes
+  // hold), so the next round finds the next one.  k <= E live experts, so a
+  // round never takes a padding lane.  Only the high words are kept: the low
+  // word of lane n's entry t is 63 - (16t + n) in every row.
+  uint32_t hw[NT][4];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hw[t][i] = ordered_bits(acc[t][i]);
+  const uint32_t taken_hw = ordered_bits(-INFINITY);
+#pragma unroll 1
   for (int s = 0; s < k; ++s) {
+    uint64_t best[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float bv = acc[0][i];
-      int bi = n;
+      // The lane's own best: the largest high word, the lowest t on a tie.
+      uint32_t bh = hw[0][i];
+      int be = n;
 #pragma unroll
-      for (int t = 1; t < NT; ++t)
-        if (better(acc[t][i], t * 16 + n, bv, bi)) { bv = acc[t][i]; bi = t * 16 + n; }
-      argmax16(bv, bi);
+      for (int t = 1; t < NT; ++t) {
+        const bool gt = hw[t][i] > bh;
+        bh = gt ? hw[t][i] : bh;
+        be = gt ? t * 16 + n : be;
+      }
+      best[i] = pair_key(bh, be);
+    }
+    argmax16(best);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int bi = key_expert(best[i]);
       const bool live = tok0 + grp * 4 + i < T_tokens;
-      if ((bi & 15) == n) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-          if (t == (bi >> 4)) {
-            acc[t][i] = -INFINITY;
-            if (live && s < k) cnt[t] += 1.f;
-          }
+      for (int t = 0; t < NT; ++t) {
+        const bool taken = t * 16 + n == bi;
+        hw[t][i] = taken ? taken_hw : hw[t][i];
+        cnt[t] += live && taken ? 1.f : 0.f;
       }
       if (n == 0) {
-        if (s < k) {
-          sel_val[(grp * 4 + i) * kMaxExperts + s] = bv;
-          sel_id[(grp * 4 + i) * kMaxExperts + s] = bi;
-        }
+        sel_val[(grp * 4 + i) * kMaxExperts + s] = key_value(best[i]);
+        sel_id[(grp * 4 + i) * kMaxExperts + s] = bi;
       }
     }
   }
@@ -232,9 +270,10 @@ __device__ __forceinline__ void topk_tile(f32x4_t (&acc)[NT], const float* __res
 
 // Sum the K-split partial logits of tokens tok0 .. tok0+15 in split order into
 // logit[16][kMaxExperts] (LDS), then select with wave 0.  Called by a whole
-// block of 1024 threads (one (token, expert) entry per thread, 8 loads in
+// block of kThreads threads (a multiple of 64: each thread sums the entries
+// (token, expert) of its expert for every kThreads/64-th token, 8 loads in
 // flight); the caller synchronises the block before and after.
-template <int NT>
+template <int NT, int kThreads = 1024>
 __device__ __forceinline__ void topk_from_partials(const float* __restrict__ partial, int nsplit,
                                                    const float* __restrict__ bias, int T_tokens, int E, int k,
                                                    int tok0, float (*logit)[kMaxExperts], float* sel_val,
@@ -242,9 +281,9 @@ __device__ __forceinline__ void topk_from_partials(const float* __restrict__ par
                                                    float* __restrict__ topk_w, float inv_tau = 1.f,
                                                    float* __restrict__ prob_sum = nullptr,
                                                    uint8_t* __restrict__ order = nullptr) {
-  {
-    const int r = threadIdx.x / kMaxExperts;
-    const int e = threadIdx.x % kMaxExperts;
+  static_assert(kThreads % kMaxExperts == 0 && kThreads <= 16 * kMaxExperts, "whole rows of (token, expert) entries");
+  const int e = threadIdx.x % kMaxExperts;
+  for (int r = threadIdx.x / kMaxExperts; r < 16; r += kThreads / kMaxExperts) {
     const int tok = tok0 + r;
     float v = 0.f;
     if (tok < T_tokens && e < E) {
