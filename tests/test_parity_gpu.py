@@ -121,6 +121,52 @@ def test_route_exact_ties_go_to_lower_id(T, d, E, k, dt):
     check_routing(got, tw.cpu().numpy(), r)
 
 
+@pytest.mark.parametrize("T,d,E,k,dt", [(500, 256, 16, 6, "bf16"), (8, 1024, 64, 6, "bf16"), (200, 128, 40, 6, "f32"),
+                                        (5000, 2048, 64, 6, "bf16")],
+                         ids=["lds_router", "splitk", "f32", "gate_slices"])
+def test_route_extreme_logits(T, d, E, k, dt):
+    """Gate biases across the whole float range (+3e38, +2.5e37, -3e38,
+    -2.5e37, -1e-30, the subnormal -1e-40, +0 and -0; the other experts'
+    negative) and two tokens whose hidden state is zero, so their logits are
+    the biases alone.  The selection must follow the float64 logits (the
+    oracle's probabilities underflow to equal zeros here, so its own top-k
+    cannot decide): +-3e38 and +-2.5e37 in their places, and on the zero
+    tokens +0 and -0 tied (lower id first) ahead of -1e-40 and -1e-30.  The
+    weights are exactly 1 for the +3e38 expert and 0 for the others."""
+    inp = workloads.random_case(31 + T, T, d, E, k, 64, dt, -1, 0.5, w_scale=0.05)
+    bias = -(np.abs(np.array(inp.bias, copy=True)) + np.float32(0.1))
+    pool = [3.0e38, 2.5e37, -3.0e38, -2.5e37, -1e-30, -1e-40, 0.0, -0.0]
+    at = [(7 * j + 3) % E for j in range(len(pool))]
+    for e, v in zip(at, pool):
+        bias[e] = np.float32(v)
+    X = np.array(inp.X, copy=True)
+    X[0] = 0
+    X[T - 1] = 0
+    cfg = moe.config(T, d, 64, E, k, -1, dt)
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    tw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    rws = torch.empty(max(1, moe.moe_workspace_size(cfg, moe.MOE_OP_ROUTE)), dtype=torch.uint8, device="cuda")
+    moe.moe_route(cfg, to_dev(X, dt), to_dev(inp.Wg, dt), to_dev(bias, "f32"), ids, tw, rws)
+    torch.cuda.synchronize()
+    got, w = ids.cpu().numpy(), tw.cpu().numpy()
+    logits = oracle.router_logits(oracle.as_f64(X, dt), oracle.as_f64(inp.Wg, dt), bias)
+    assert (got[:, :2] == at[:2]).all(), "the +3e38 and +2.5e37 experts lead every token"
+    assert not np.isin(got, at[2:4]).any(), "the -3e38 and -2.5e37 experts are never taken"
+    zero_row = at[:2] + sorted(at[6:8]) + [at[5], at[4]]
+    for t in (0, T - 1):
+        assert list(got[t]) == zero_row, (t, got[t], zero_row)
+    compared = 0
+    for t in range(T):
+        order = sorted(range(E), key=lambda e: (-logits[t, e], e))
+        gaps = -np.diff(logits[t, order[:k + 1]])
+        if t in (0, T - 1) or gaps.min() < 1e-3:  # zero tokens checked above; near-ties between fp32 and fp64
+            continue
+        compared += 1
+        assert list(got[t]) == order[:k], (t, got[t], order[:k])
+    assert compared >= (T - 2) // 2, compared
+    assert (w[:, 0] == 1).all() and (w[:, 1:] == 0).all()
+
+
 @pytest.mark.parametrize("T,d,E,k", [(12000, 256, 16, 2), (40000, 128, 8, 2), (9000, 128, 40, 3), (5000, 256, 5, 2),
                                      (20000, 2048, 32, 2), (17000, 2048, 64, 2), (16400, 1536, 50, 3),
                                      (16389, 4096, 64, 2), (5000, 4096, 24, 3)],
