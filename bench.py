@@ -41,16 +41,16 @@ METRIC = "MoE-layer tokens/sec at 1 GPU; % bf16 MFMA peak (FFN) / % HBM peak (re
 # WRITE_SIZE (KiB per dispatch), scaled by what the same counters read for a
 # plain 1 GiB device copy (FETCH_SIZE x2.0, WRITE_SIZE x1.0); valid only for
 # the GEMM source they were taken on (sha1 prefix), else reported as null.
-TRAFFIC_SOURCE_SHA1 = "d133c3efde78"
+TRAFFIC_SOURCE_SHA1 = "9cc7615b85f3"
 TRAFFIC_BYTES = {  # (workload, stage) -> (fetch KiB, write KiB) per dispatch, raw counter values
-    ("skewed", "expert_up"): (7088717.0, 919066.7),
-    ("skewed", "expert_down"): (6337415.2, 267010.2),
-    ("prefill", "expert_up"): (468861.6, 180401.2),
-    ("prefill", "expert_down"): (518034.1, 65568.1),
-    ("capacity", "expert_up"): (741792.0, 285475.1),
-    ("capacity", "expert_down"): (590179.2, 417427.1),
-    ("decode", "expert_up"): (122264.0, 80.1),
-    ("decode", "expert_down"): (122352.3, 112.0),
+    ("skewed", "expert_up"): (7128509.4, 918925.5),
+    ("skewed", "expert_down"): (6364913.2, 266475.8),
+    ("prefill", "expert_up"): (470517.6, 180374.7),
+    ("prefill", "expert_down"): (518015.0, 65568.3),
+    ("capacity", "expert_up"): (787941.8, 285440.3),
+    ("capacity", "expert_down"): (598937.3, 416700.0),
+    ("decode", "expert_up"): (122263.0, 160.0),
+    ("decode", "expert_down"): (122351.2, 224.0),
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 
