@@ -177,8 +177,8 @@ moe_status moe_expert_up_gather(const moe_config* cfg, const void* X, const int3
 
 /* Host only: *supported = 1 if moe_expert_up_gather runs for cfg, else 0:
  * bf16, T*d*2 < 2^31 bytes, and either more than 64 pairs per expert possible
- * (min(T, C) > 64) or at most 16 (decode-sized batches) with d a multiple of
- * 128 and F a multiple of 8.  moe_forward then gathers too and leaves the Xp
+ * (min(T, C) > 64) or at most 64 with d a multiple of 128 and F a multiple
+ * of 8.  moe_forward then gathers too and leaves the Xp
  * part of its workspace unwritten. */
 moe_status moe_expert_up_gather_supported(const moe_config* cfg, int32_t* supported);
 

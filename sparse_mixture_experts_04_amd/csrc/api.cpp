@@ -84,7 +84,7 @@ int rows_per_expert_bound(const moe_config* c) {
 // decode kernel runs, and X fits 32-bit buffer offsets).
 bool gathers(const moe_config* c) {
   return moe::grouped_gemm_gathers(c->dtype, c->hidden_size, c->intermediate_size, rows_per_expert_bound(c),
-                                   c->num_tokens);
+                                   c->num_tokens, static_cast<int>(pairs_of(c)), c->num_experts);
 }
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }

@@ -735,8 +735,9 @@ hipError_t launch_big(const uint16_t* A, const uint16_t* B, uint16_t* C, const i
 }
 
 // ---------------------------------------------------------------------------
-// Skinny variant for few rows per expert (decode: a handful of tokens), where
-// the layer is bound by streaming each active expert's weights once.  A
+// Skinny variant for few rows per expert where the decode variant below does
+// not run (K not a multiple of 128 or N not of 8): the layer is bound by
+// streaming each active expert's weights once.  A
 // one-wave block owns 16 weight rows (one 16-row MFMA A tile) over the whole
 // K and up to 64 of the expert's token rows (up to four 16-column B tiles),
 // so every weight byte is loaded exactly once, with 8 k-steps of loads in
@@ -870,7 +871,7 @@ __global__ __launch_bounds__(kWave) void grouped_gemm_bf16_skinny(const uint16_t
 }
 
 // ---------------------------------------------------------------------------
-// Decode variant (at most 16 token rows per expert): weight streaming with
+// Decode variant (at most 64 token rows per expert possible): weight streaming with
 // whole-line loads.  One 16x16x32 MFMA takes as its A operand 4 weight rows x
 // 4 K-slices of 32 (each lane's 16 bytes; the 16 lanes of a row cover 256
 // contiguous bytes of it) and as its B operand 4 token rows x the same 4
@@ -892,7 +893,9 @@ __global__ __launch_bounds__(kWave) void grouped_gemm_bf16_skinny(const uint16_t
 constexpr int kGvGroups = 2;        // 4-row weight groups per wave
 constexpr int kGvWaves = 1;
 constexpr int kGvRows = kGvWaves * kGvGroups * 4;  // weight rows per block
-constexpr int kGvMaxTok = 16;       // token rows per expert this kernel handles
+// Largest bound on the rows per expert (from the batch and capacity; the real
+// counts are on the device) for which this kernel runs; see gemv_runs.
+constexpr int kGvMaxTok = 64;
 
 template <bool kGelu, int kTG, bool kGather>
 __global__ __launch_bounds__(kGvWaves * kWave) void grouped_gemm_bf16_gemv(const uint16_t* __restrict__ A,
@@ -1097,6 +1100,21 @@ hipError_t launch_cfg(bool gelu, const T* A, const T* B, T* C, const int32_t* of
   return hipGetLastError();
 }
 
+// The decode kernel runs for this shape: whole 128-element K chunks, 8-row
+// weight groups, and few rows per expert.  A pass of it holds 16 rows, so a
+// bound above 16 costs an expert that gets more than 16 rows extra passes
+// over its weights; up to a bound of 64 it still runs when the batch averages
+// at most 16 rows per expert (rows <= 16 E), where most experts need one pass
+// and it streams at about 6 TB/s against 3.8 TB/s for the skinny kernel at 64
+// tokens and 5.1 at 32 (d = 3584, F = 2560, E = 64, k = 2).  A batch that can
+// fill its experts to 64 rows runs the skinny kernel, which reads each weight
+// once.
+bool gemv_runs(int K, int N, int max_tokens_per_expert, int rows, int E) {
+  if (K % 128 != 0 || N % (kGvGroups * 4) != 0) return false;
+  return max_tokens_per_expert <= 16 ||
+         (max_tokens_per_expert <= kGvMaxTok && static_cast<int64_t>(rows) <= int64_t{16} * E);
+}
+
 }  // namespace
 
 hipError_t launch_grouped_gemm(int dtype, bool gelu, const void* A, const void* B, void* C, const int32_t* offsets,
@@ -1106,16 +1124,16 @@ hipError_t launch_grouped_gemm(int dtype, bool gelu, const void* A, const void* 
     const uint16_t* a = static_cast<const uint16_t*>(A);
     const uint16_t* b = static_cast<const uint16_t*>(B);
     uint16_t* c = static_cast<uint16_t*>(C);
-    const bool gemv_ok = K % 128 == 0 && N % (kGvGroups * 4) == 0;
-    if (gemv_ok && max_tokens_per_expert <= 4)
-      return gelu ? launch_gemv<true, 1>(a, b, c, offsets, E, N, K, max_rows, stream)
-                  : launch_gemv<false, 1>(a, b, c, offsets, E, N, K, max_rows, stream);
-    if (gemv_ok && max_tokens_per_expert <= 8)
-      return gelu ? launch_gemv<true, 2>(a, b, c, offsets, E, N, K, max_rows, stream)
-                  : launch_gemv<false, 2>(a, b, c, offsets, E, N, K, max_rows, stream);
-    if (gemv_ok && max_tokens_per_expert <= kGvMaxTok)
+    if (gemv_runs(K, N, max_tokens_per_expert, max_rows, E)) {
+      if (max_tokens_per_expert <= 4)
+        return gelu ? launch_gemv<true, 1>(a, b, c, offsets, E, N, K, max_rows, stream)
+                    : launch_gemv<false, 1>(a, b, c, offsets, E, N, K, max_rows, stream);
+      if (max_tokens_per_expert <= 8)
+        return gelu ? launch_gemv<true, 2>(a, b, c, offsets, E, N, K, max_rows, stream)
+                    : launch_gemv<false, 2>(a, b, c, offsets, E, N, K, max_rows, stream);
       return gelu ? launch_gemv<true, 4>(a, b, c, offsets, E, N, K, max_rows, stream)
                   : launch_gemv<false, 4>(a, b, c, offsets, E, N, K, max_rows, stream);
+    }
     if (max_tokens_per_expert <= 16)
       return gelu ? launch_skinny<true, 1>(a, b, c, offsets, E, N, K, max_rows, stream)
                   : launch_skinny<false, 1>(a, b, c, offsets, E, N, K, max_rows, stream);
@@ -1132,15 +1150,9 @@ hipError_t launch_grouped_gemm(int dtype, bool gelu, const void* A, const void* 
                                          static_cast<float*>(C), offsets, E, N, K, max_rows, stream);
 }
 
-namespace {
-// The decode kernel runs (launch_grouped_gemm's rule) for this shape.
-bool gemv_runs(int K, int N, int max_tokens_per_expert) {
-  return K % 128 == 0 && N % (kGvGroups * 4) == 0 && max_tokens_per_expert <= kGvMaxTok;
-}
-}  // namespace
-
-bool grouped_gemm_gathers(int dtype, int K, int N, int max_tokens_per_expert, int src_rows) {
-  return dtype == kDtypeBF16 && (max_tokens_per_expert > kSkinnyMaxTok || gemv_runs(K, N, max_tokens_per_expert)) &&
+bool grouped_gemm_gathers(int dtype, int K, int N, int max_tokens_per_expert, int src_rows, int rows, int E) {
+  return dtype == kDtypeBF16 &&
+         (max_tokens_per_expert > kSkinnyMaxTok || gemv_runs(K, N, max_tokens_per_expert, rows, E)) &&
          static_cast<int64_t>(src_rows) * K * 2 < (int64_t{1} << 31);
 }
 
@@ -1151,7 +1163,7 @@ hipError_t launch_grouped_gemm_gather(bool gelu, const void* X, int src_rows, co
   const uint16_t* a = static_cast<const uint16_t*>(X);
   const uint16_t* b = static_cast<const uint16_t*>(B);
   uint16_t* c = static_cast<uint16_t*>(C);
-  if (gemv_runs(K, N, max_tokens_per_expert)) {
+  if (gemv_runs(K, N, max_tokens_per_expert, max_rows, E)) {
     if (max_tokens_per_expert <= 4)
       return gelu ? launch_gemv<true, 1, true>(a, b, c, offsets, E, N, K, max_rows, stream, gidx, gdiv, src_rows)
                   : launch_gemv<false, 1, true>(a, b, c, offsets, E, N, K, max_rows, stream, gidx, gdiv, src_rows);

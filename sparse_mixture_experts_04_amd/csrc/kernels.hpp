@@ -97,8 +97,9 @@ hipError_t launch_grouped_gemm(int dtype, bool gelu, const void* A, const void* 
 // permutation and gdiv = k read each pair's token row).  Only where
 // grouped_gemm_gathers() holds, i.e. where launch_grouped_gemm runs its
 // 256x256 kernel or its decode (few-rows, whole-line) kernel and X fits
-// 32-bit buffer offsets; max_tokens_per_expert picks the kernel as there.
-bool grouped_gemm_gathers(int dtype, int K, int N, int max_tokens_per_expert, int src_rows);
+// 32-bit buffer offsets; max_tokens_per_expert, rows (the pairs the operand
+// can hold, max_rows of the launch) and E pick the kernel as there.
+bool grouped_gemm_gathers(int dtype, int K, int N, int max_tokens_per_expert, int src_rows, int rows, int E);
 hipError_t launch_grouped_gemm_gather(bool gelu, const void* X, int src_rows, const int32_t* gidx, int gdiv,
                                       const void* B, void* C, const int32_t* offsets, int E, int N, int K,
                                       int max_rows, int max_tokens_per_expert, hipStream_t stream);

@@ -147,13 +147,16 @@ def test_gathered_up_projection_support():
     assert moe.moe_expert_up_gather_supported(moe.config(8192, 2048, 5632, 32, 2, -1, "bf16"))
     assert moe.moe_expert_up_gather_supported(moe.config(65, 128, 128, 8, 2, -1, "bf16"))
     assert moe.moe_expert_up_gather_supported(moe.config(32768, 2048, 1408, 32, 4, 4096, "bf16"))
-    assert not moe.moe_expert_up_gather_supported(moe.config(64, 128, 128, 8, 2, -1, "bf16"))
     assert not moe.moe_expert_up_gather_supported(moe.config(8192, 2048, 5632, 32, 2, 64, "bf16"))
     assert not moe.moe_expert_up_gather_supported(moe.config(8192, 2048, 5632, 32, 2, -1, "f32"))
-    # decode-sized batches (at most 16 pairs per expert) gather too, where the decode kernel runs
+    # decode-sized batches gather too, where the decode kernel runs: at most 16 pairs per expert, or at
+    # most 64 with at most 16 pairs per expert on average (T * k <= 16 E)
     assert moe.moe_expert_up_gather_supported(moe.config(8, 3584, 2560, 64, 2, -1, "bf16"))
     assert moe.moe_expert_up_gather_supported(moe.config(300, 1024, 256, 16, 2, 16, "bf16"))
-    assert not moe.moe_expert_up_gather_supported(moe.config(300, 1024, 256, 16, 2, 17, "bf16"))  # 17-64: no
+    assert moe.moe_expert_up_gather_supported(moe.config(64, 128, 128, 8, 2, -1, "bf16"))  # 128 pairs = 16 E
+    assert moe.moe_expert_up_gather_supported(moe.config(64, 3584, 2560, 64, 2, -1, "bf16"))
+    assert not moe.moe_expert_up_gather_supported(moe.config(64, 128, 128, 4, 2, -1, "bf16"))  # 128 pairs > 16 E
+    assert not moe.moe_expert_up_gather_supported(moe.config(300, 1024, 256, 16, 2, 17, "bf16"))  # 600 > 16 E
     assert not moe.moe_expert_up_gather_supported(moe.config(8, 3520, 2560, 64, 2, -1, "bf16"))  # d % 128 != 0
     assert not moe.moe_expert_up_gather_supported(moe.config(8, 3584, 2560, 64, 2, -1, "f32"))
     # X must fit 32-bit buffer offsets: T * d * 2 < 2^31
@@ -170,7 +173,7 @@ def test_gathered_up_projection_rejects_before_launch():
         with pytest.raises(moe.MoeError) as ei:
             moe.moe_expert_up_gather(cfg, *args, stream=0)
         assert ei.value.status == moe.MOE_ERR_INVALID_ARG
-    for unsupported in (moe.config(64, 128, 128, 8, 2, -1, "bf16"), moe.config(300, 128, 128, 8, 2, -1, "f32")):
+    for unsupported in (moe.config(64, 128, 128, 4, 2, -1, "bf16"), moe.config(300, 128, 128, 8, 2, -1, "f32")):
         with pytest.raises(moe.MoeError) as ei:
             moe.moe_expert_up_gather(unsupported, 1, 1, 1, 1, 1, stream=0)
         assert ei.value.status == moe.MOE_ERR_UNSUPPORTED

@@ -34,6 +34,8 @@ CASES = [
     ("skinny_cap", 60, 128, 8, 3, 128, "bf16", 9, 0.5),
     ("splitk_cap_k3", 48, 1024, 16, 3, 256, "bf16", 7, 0.5),
     ("splitk_t200_e64", 200, 512, 64, 2, 256, "bf16", -1, 0.3),
+    # up to 48 rows per expert possible but 6 on average: the decode kernel, with extra passes
+    ("gemv_bound48", 48, 256, 16, 2, 384, "bf16", -1, 0.8),
     # 256x256-tile GEMM at its edges: K = 64 (one LDS stage per tile), N = 64
     # (an n-tile of 64 valid weight rows), experts of a few hundred rows
     ("big_d64_f64", 700, 64, 4, 2, 64, "bf16", -1, 0.0),
@@ -534,13 +536,14 @@ def test_expert_gemm_tile_heights(rows):
     assert_close(dev_to_f64(H), H_ref, "bf16", "H")
 
 
-@pytest.mark.parametrize("d,F,cap", [(256, 384, 4), (256, 384, 8), (256, 384, 16), (192, 320, 16)],
-                         ids=["gemv_tok4", "gemv_tok8", "gemv_tok16", "skinny_tok16"])
+@pytest.mark.parametrize("d,F,cap", [(256, 384, 4), (256, 384, 8), (256, 384, 16), (256, 384, -1), (192, 320, 16)],
+                         ids=["gemv_tok4", "gemv_tok8", "gemv_tok16", "gemv_bound30", "skinny_tok16"])
 def test_expert_rows_beyond_the_bound(d, F, cap):
     """The few-rows expert kernels are chosen by a bound on rows per expert
     (here the capacity in the config); offsets that give some experts more
     rows than that must still be computed in full (extra passes), not
-    clipped.  d = 192 (not a multiple of 128) takes the 16-row-tile kernel."""
+    clipped.  d = 192 (not a multiple of 128) takes the 16-row-tile kernel; with
+    no capacity the bound is T = 30 (60 rows over 8 experts: the decode kernel)."""
     E, k, T = 8, 2, 30
     counts = np.array([25, 0, 3, 17, 1, 6, 0, 8])
     Tk = T * k
