@@ -16,8 +16,10 @@ HIP graph and replayed.  Each stage entry point is then timed on its own: K
 back-to-back launches between two HIP events on the stream the kernels run
 on, which gives the kernels' average duration without host gaps.  Prints one
 JSON line: tokens/s of the whole layer, the roofline fraction of the dominant
-kernel, per-stage times, and the CPU oracle timed on a bounded sample of the
-same workload (a baseline, not the target).
+kernel (of the published peak, and of the peak a plain copy and a large
+vendor-library GEMM reach on the same GPU, "achievable"), per-stage times,
+and the CPU oracle timed on a bounded sample of the same workload (a
+baseline, not the target).
 """
 from __future__ import annotations
 
@@ -375,6 +377,58 @@ def measure(torch, moe, workloads, name, steps, warmup, eager=False, reroute=Fal
     return res
 
 
+def achievable_peaks(torch):
+    """Peaks measured on this GPU beside the published ones: HBM from a plain
+    1 GiB device-to-device copy (read plus write bytes) and a read-only sum
+    over 2 GiB (the better of the two), and MFMA from a square
+    8192 x 8192 x 8192 bf16 matrix product through torch (the vendor GEMM
+    library), each timed with HIP events over back-to-back launches."""
+    stream = torch.cuda.current_stream()
+
+    def per_launch_ms(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    copy_ms = per_launch_ms(lambda: dst.copy_(src), 10)
+    copy_gbs = 2 * src.numel() * 4 / copy_ms / 1e6
+    del dst
+    big = torch.ones(1 << 29, dtype=torch.float32, device="cuda")  # 2 GiB, read only
+    acc = torch.empty((), dtype=torch.float32, device="cuda")
+    read_ms = per_launch_ms(lambda: torch.sum(big, dim=0, out=acc), 10)
+    read_gbs = big.numel() * 4 / read_ms / 1e6
+    del src, big, acc
+    n = 8192
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    a = torch.randn((n, n), device="cuda", generator=g).to(torch.bfloat16)
+    b = torch.randn((n, n), device="cuda", generator=g).to(torch.bfloat16)
+    c = torch.empty((n, n), device="cuda", dtype=torch.bfloat16)
+    mm_ms = per_launch_ms(lambda: torch.mm(a, b, out=c), 20)
+    tflops = 2.0 * n ** 3 / mm_ms / 1e9
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"hbm_gbs": round(max(copy_gbs, read_gbs), 1), "hbm_copy_gbs": round(copy_gbs, 1),
+            "hbm_read_gbs": round(read_gbs, 1), "bf16_gemm_tflops": round(tflops, 1),
+            "method": "HBM: the better of a 1 GiB fp32 device copy (2 GiB moved) and a sum over 2 GiB of fp32, "
+                      "10 launches each; MFMA: torch.mm bf16 8192^3, 20 launches; HIP events"}
+
+
+def add_achievable(roof, ach):
+    """The roofline's achieved rate as a fraction of the measured peak of its bound."""
+    ref = ach["hbm_gbs"] if roof["bound"] == "hbm" else ach["bf16_gemm_tflops"]
+    if roof["unit"] in ("GB/s", "TFLOP/s") and ref > 0 and (roof["bound"] == "hbm" or roof["peak"] == PEAK_BF16_TFLOPS):
+        roof["frac_of_achievable"] = round(roof["achieved"] / ref, 4)
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -410,6 +464,12 @@ def main():
             print(f"[bench] {name}: {r['value']:.1f} tokens/s, {r['roofline']['kernel']} at "
                   f"{r['roofline']['frac']:.4f} of peak", file=sys.stderr, flush=True)
 
+    ach = achievable_peaks(torch)
+    for r in [head] + list(others.values()):
+        add_achievable(r["roofline"], ach)
+        for st in r["stages"].values():
+            st["frac_of_achievable_hbm"] = round(st["gbs"] / ach["hbm_gbs"], 4)
+
     line = {
         "metric": METRIC,
         "value": head["value"],
@@ -428,6 +488,7 @@ def main():
         "config": head["config"],
         "roofline": head["roofline"],
         "cpu_baseline": head["cpu_baseline"],
+        "achievable": ach,
         "stages": head["stages"],
         "stage_input_sets": head["stage_input_sets"],
         "kept_pairs": head["kept_pairs"],
