@@ -919,6 +919,98 @@ __device__ __forceinline__ void dispatch_small_block(const int32_t* __restrict__
   if (Xp != nullptr) copy_rows<kThreads>(X, Xp, d, k, 0, T_tok, &s_row[0][0], kSmallMaxK);
 }
 
+// At most 64 tokens: the whole dispatch in one wave with no block barrier,
+// token t on lane t (its ids in e[], kNone for slots >= k, tokens >= T and
+// ids outside [0, E)).  Lane ex also stands for expert ex: per-expert counts
+// come from expert-id-bit ballots, the offsets from one wave scan, and a
+// pair's expert-indexed values (slot base, offset) from a lane shuffle.  The
+// results are those of dispatch_small_block: capacity by (slot, token)
+// priority, rows stable by (expert, token, slot).  row_of (LDS, [64][k_stride])
+// receives each pair's row for the row copy.  Called by one whole wave.
+template <bool kCap>
+__device__ __forceinline__ void dispatch_one_wave(int (&e)[kSmallMaxK], int T_tok, int E, int k, int capacity,
+                                                  int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                  int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
+                                                  int* row_of, int k_stride) {
+  const int lane = threadIdx.x % kWave;
+  const uint64_t below = (1ull << lane) - 1ull;
+  // routed pairs of expert `lane`, and (capacity) its pairs in slots < s
+  int routed = 0;
+  int slot_base[kSmallMaxK];
+#pragma unroll
+  for (int s = 0; s < kSmallMaxK; ++s) {
+    slot_base[s] = routed;
+    if (s < k) routed += __popcll(match(ballots_of(e[s]), lane));
+  }
+  int kept = routed;
+  if (kCap) {
+    // a pair is kept if fewer than C pairs of its expert come before it in
+    // (slot, token) order; dropped pairs become kNone
+#pragma unroll
+    for (int s = 0; s < kSmallMaxK; ++s) {
+      if (s < k) {
+        const Ballots B = ballots_of(e[s]);
+        const int base = __shfl(slot_base[s], e[s] & (kWave - 1));
+        if (e[s] != kNone && base + __popcll(match(B, e[s]) & below) >= capacity) e[s] = kNone;
+      }
+    }
+    kept = 0;
+#pragma unroll
+    for (int s = 0; s < kSmallMaxK; ++s)
+      if (s < k) kept += __popcll(match(ballots_of(e[s]), lane));
+  }
+  if (lane >= E) routed = kept = 0;  // no id names expert >= E
+  int incl = kept;
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) {
+    const int o = __shfl_up(incl, m);
+    if (lane >= m) incl += o;
+  }
+  const int off = incl - kept;
+  const int total = __shfl(incl, kWave - 1);
+  if (lane < E) {
+    counts[lane] = routed;
+    offsets[lane] = off;
+  }
+  if (lane == 0) offsets[E] = total;
+  // rank of each pair among its expert's kept pairs of earlier tokens (any
+  // slot) and earlier slots of its own token
+  int cnt[kSmallMaxK];
+#pragma unroll
+  for (int s = 0; s < kSmallMaxK; ++s) cnt[s] = 0;
+#pragma unroll
+  for (int s2 = 0; s2 < kSmallMaxK; ++s2) {
+    if (s2 < k) {
+      const Ballots B = ballots_of(e[s2]);
+#pragma unroll
+      for (int s = 0; s < kSmallMaxK; ++s)
+        if (s < k) cnt[s] += __popcll(match(B, e[s]) & below);
+    }
+  }
+  const int Tk = T_tok * k;
+#pragma unroll
+  for (int s = 0; s < kSmallMaxK; ++s) {
+    if (s < k) {
+      const int base = __shfl(off, e[s] & (kWave - 1));
+      if (lane < T_tok) {
+        int row = -1;
+        if (e[s] != kNone) {
+          int same = 0;
+#pragma unroll
+          for (int s2 = 0; s2 < kSmallMaxK; ++s2)
+            if (s2 < s && e[s2] == e[s]) ++same;
+          row = base + cnt[s] + same;
+          if (row < 0 || row >= Tk) row = -1;  // unreachable for consistent counts; keeps stores in bounds
+          if (row >= 0) perm[row] = lane * k + s;
+        }
+        inv_perm[lane * k + s] = row;
+        if (row_of != nullptr) row_of[lane * k_stride + s] = row;
+      }
+    }
+  }
+  for (int r = total + lane; r < Tk; r += kWave) perm[r] = -1;
+}
+
 template <typename T, bool kCap>
 __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __restrict__ ids, const T* __restrict__ X,
                                                              int T_tok, int d, int E, int k, int capacity,
@@ -926,6 +1018,18 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t* __re
                                                              int32_t* __restrict__ offsets,
                                                              int32_t* __restrict__ perm,
                                                              int32_t* __restrict__ inv_perm, T* __restrict__ Xp) {
+  if (T_tok <= kWave) {
+    __shared__ int s_row1[kWave][kSmallMaxK];
+    if (threadIdx.x < kWave) {
+      int e[kSmallMaxK];
+      load_ids(ids, threadIdx.x, T_tok, k, E, 0, e);
+      dispatch_one_wave<kCap>(e, T_tok, E, k, capacity, counts, offsets, perm, inv_perm, &s_row1[0][0], kSmallMaxK);
+    }
+    if (Xp == nullptr) return;
+    __syncthreads();
+    copy_rows<256>(X, Xp, d, k, 0, T_tok, &s_row1[0][0], kSmallMaxK);
+    return;
+  }
   dispatch_small_block<256, T, kCap>(ids, X, T_tok, d, E, k, capacity, counts, offsets, perm, inv_perm, Xp);
 }
 
@@ -947,11 +1051,35 @@ __global__ __launch_bounds__(1024) void topk_dispatch_small_kernel(const float* 
   __shared__ float logit[16][kMaxExperts];
   __shared__ float sel_val[16 * kMaxExperts];
   __shared__ int sel_id[16 * kMaxExperts];
+  __shared__ int s_ids[kWave][kSmallMaxK];  // T <= 64: each pass's selected ids, kept for the one-wave dispatch
+  __shared__ int s_row1[kWave][kSmallMaxK];
+  const bool one_wave = T_tok <= kWave;
   for (int tok0 = 0; tok0 < T_tok; tok0 += 16) {
     topk_from_partials<NT>(partial, nsplit, bias, T_tok, E, k, tok0, logit, sel_val, sel_id, ids, w);
     __syncthreads();
+    if (one_wave && threadIdx.x < 16 * kSmallMaxK) {
+      const int r = threadIdx.x / kSmallMaxK, s = threadIdx.x % kSmallMaxK;
+      if (tok0 + r < T_tok) s_ids[tok0 + r][s] = sel_id[r * kMaxExperts + s];  // slots >= k are not read
+    }
   }
-  dispatch_small_block<1024, T, kCap>(ids, X, T_tok, d, E, k, capacity, counts, offsets, perm, inv_perm, Xp);
+  if (!one_wave) {
+    dispatch_small_block<1024, T, kCap>(ids, X, T_tok, d, E, k, capacity, counts, offsets, perm, inv_perm, Xp);
+    return;
+  }
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    const int t = threadIdx.x;
+    int e[kSmallMaxK];
+#pragma unroll
+    for (int s = 0; s < kSmallMaxK; ++s) {
+      const int v = (s < k && t < T_tok) ? s_ids[t][s] : -1;
+      e[s] = (v >= 0 && v < E) ? v : kNone;
+    }
+    dispatch_one_wave<kCap>(e, T_tok, E, k, capacity, counts, offsets, perm, inv_perm, &s_row1[0][0], kSmallMaxK);
+  }
+  if (Xp == nullptr) return;
+  __syncthreads();
+  copy_rows<1024>(X, Xp, d, k, 0, T_tok, &s_row1[0][0], kSmallMaxK);
 }
 
 template <typename T, int KMAX>
