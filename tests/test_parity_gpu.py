@@ -368,6 +368,43 @@ def test_expert_up_gather(case):
         assert_close(dev_to_f64(H[:N]), H_ref, w.dtype, "H")
 
 
+def test_expert_up_gather_at_offset_limit():
+    """The gathered up-projection at the largest X it takes: T * d * 2 bytes
+    just under 2^31 (its buffer offsets are 32-bit), T = 262143 tokens of
+    d = 4096.  Sampled tokens (the first, middle and last rows of X among
+    them) hold random hidden states and every other row is zero; the output
+    rows of sampled tokens match the oracle, and the rows of zero tokens are
+    exactly 0 (GELU(0) = 0)."""
+    d, F, E, k = 4096, 128, 8, 2
+    T = (1 << 31) // (2 * d) - 1
+    cfg = moe.config(T, d, F, E, k, -1, "bf16")
+    assert moe.moe_expert_up_gather_supported(cfg)
+    assert not moe.moe_expert_up_gather_supported(moe.config(T + 1, d, F, E, k, -1, "bf16"))
+    rng = np.random.default_rng(2026)
+    Tk = T * k
+    sampled = np.unique(np.concatenate([[0, 1, T // 2, T - 2, T - 1], rng.choice(T, 59, replace=False)]))
+    Xs = round_to(rng.standard_normal((len(sampled), d)), "bf16")
+    W1_64 = round_to(rng.standard_normal((E, F, d)) * 0.05, "bf16")
+    X = torch.zeros((T, d), dtype=torch.bfloat16, device="cuda")
+    X[torch.from_numpy(sampled).cuda()] = torch.from_numpy(Xs).to(torch.bfloat16).cuda()
+    W1 = torch.from_numpy(W1_64).to(torch.bfloat16).cuda()
+    perm_np = rng.permutation(Tk).astype(np.int32)
+    offsets_np = np.linspace(0, Tk, E + 1).astype(np.int64).astype(np.int32)  # near-equal expert segments
+    H = torch.full((Tk, F), 3.0, dtype=torch.bfloat16, device="cuda")
+    print(f"gathered up-projection at the offset limit: T={T} d={d} X bytes={T * d * 2}", flush=True)
+    moe.moe_expert_up_gather(cfg, X, torch.from_numpy(perm_np).cuda(), torch.from_numpy(offsets_np).cuda(), W1, H)
+    torch.cuda.synchronize()
+    tok_of_row = perm_np // k
+    expert_of_row = np.searchsorted(offsets_np, np.arange(Tk), side="right") - 1
+    is_sampled = np.isin(tok_of_row, sampled)
+    rows = np.nonzero(is_sampled)[0]
+    assert {T - 1, T - 2, 0} <= set(tok_of_row[rows].tolist())
+    src = np.searchsorted(sampled, tok_of_row[rows])
+    ref = np.stack([oracle.gelu_tanh(W1_64[expert_of_row[r]] @ Xs[i]) for r, i in zip(rows, src)])
+    assert_close(dev_to_f64(H[torch.from_numpy(rows).cuda()]), ref, "bf16", "H (sampled tokens)")
+    assert bool((H[torch.from_numpy(np.nonzero(~is_sampled)[0]).cuda()] == 0).all()), "rows of zero tokens"
+
+
 @pytest.mark.parametrize("T,d,F,E,k,bad,offsets", [
     (130, 128, 192, 2, 2, [0, 5, 100, 200, 259], [0, 150, 260]),      # 256x256 kernel
     (8, 256, 128, 4, 2, [0, 6, 9, 15, 12], [0, 5, 9, 16, 16]),         # decode kernel (<= 16 rows per expert)
