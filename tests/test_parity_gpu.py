@@ -480,6 +480,48 @@ def test_dispatch_ids_many_tokens(T, E, k, skew, copy):
         assert torch.equal(Xp, X[src]), "gathered rows differ"
 
 
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 200])
+@pytest.mark.parametrize("E,k,cap,copy", [(5, 1, -1, True), (64, 3, -1, False), (16, 8, 7, False), (32, 2, 3, True)],
+                         ids=["e5_k1_copy", "e64_k3", "e16_k8_cap7", "e32_k2_cap3_copy"])
+def test_dispatch_small_batches_given_ids(T, E, k, cap, copy):
+    """The single-block dispatch on given ids (Zipf-weighted, repeated ids
+    inside a token at other slot pairs) on both sides of 64 tokens, where one
+    wave does all of it, dropless and under a capacity: the oracle's counting
+    sort and (slot, token) capacity cut, bit for bit."""
+    rng = np.random.default_rng(77 + 131 * T + E + k)
+    p = 1.0 / (np.arange(E) + 1.0) ** 1.1
+    ids_np = rng.choice(E, size=(T, k), p=p / p.sum()).astype(np.int32)
+    if k > 2:
+        ids_np[::5, k - 1] = ids_np[::5, 0]
+    disp = oracle.dispatch(ids_np, E, cap)
+    d = 64
+    Tk = T * k
+    cfg = moe.config(T, d, 64, E, k, cap, "bf16")
+    X = (torch.randn(T, d, generator=torch.Generator().manual_seed(T)) * 0.5).to(torch.bfloat16).cuda()
+    counts = torch.full((E,), -7, dtype=torch.int32, device="cuda")
+    offsets = torch.full((E + 1,), -7, dtype=torch.int32, device="cuda")
+    perm = torch.full((Tk,), -7, dtype=torch.int32, device="cuda")
+    inv = torch.full((Tk,), -7, dtype=torch.int32, device="cuda")
+    Xp = torch.zeros((Tk, d), dtype=torch.bfloat16, device="cuda") if copy else None
+    ws = torch.empty(max(1, moe.moe_workspace_size(cfg, moe.MOE_OP_DISPATCH)), dtype=torch.uint8, device="cuda")
+    moe.moe_dispatch(cfg, torch.from_numpy(ids_np).cuda(), X, counts, offsets, perm, inv, Xp, ws)
+    torch.cuda.synchronize()
+    check_dispatch_exact(counts.cpu().numpy(), offsets.cpu().numpy(), perm.cpu().numpy(), inv.cpu().numpy(), disp, Tk)
+    N = int(disp.offsets[-1])
+    if copy and N:
+        src = torch.from_numpy((disp.perm // k).astype(np.int64)).cuda()
+        assert torch.equal(Xp[:N], X[src]), "gathered rows differ"
+
+
+@pytest.mark.parametrize("T", [63, 64, 65])
+@pytest.mark.parametrize("cap", [-1, 5])
+def test_forward_small_batch_boundary(T, cap):
+    """The forward's fused top-k + dispatch (K-split router, d = 1024) on both
+    sides of 64 tokens (the one-wave dispatch, then the four-wave one),
+    dropless and under a capacity: everything test_forward checks."""
+    test_forward((f"fwd_t{T}_c{cap}", T, 1024, 16, 2, 256, "bf16", cap, 0.5))
+
+
 @pytest.mark.parametrize("case", GATHER_CASES, ids=[c[0] for c in GATHER_CASES])
 def test_dispatch_indices_only(case):
     """moe_dispatch with Xp = NULL writes the same indices."""
