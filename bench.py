@@ -13,8 +13,9 @@ the CPU baseline) and reported under "other_workloads".  --reroute times moe_for
 instead: pairs over the expert capacity move to their token's next-best
 expert with room rather than being dropped.  The headline times K steps captured in one
 HIP graph and replayed.  Each stage entry point is then timed on its own: K
-back-to-back launches between two HIP events on the stream the kernels run
-on, which gives the kernels' average duration without host gaps.  Prints one
+back-to-back launches, captured in a HIP graph and replayed between two HIP
+events on the stream the kernels run on, which gives the kernels' average
+duration without host gaps.  Prints one
 JSON line: tokens/s of the whole layer, the roofline fraction of the dominant
 kernel (of the published peak, and of the peak a plain copy and a large
 vendor-library GEMM reach on the same GPU, "achievable"), per-stage times,
@@ -265,8 +266,9 @@ def measure(torch, moe, workloads, name, steps, warmup, eager=False, reroute=Fal
     ms_step, wall = (eager_ms, eager_wall) if graph_ms is None else (graph_ms, graph_wall)
 
     # ---- per-stage kernel times: each stage entry point is launched K times
-    # back to back between two HIP events on the launch stream, so the queue
-    # stays full and the interval is the kernels' own time (no host gaps).
+    # back to back (one graph replay) between two HIP events on the launch
+    # stream, so the queue stays full and the interval is the kernels' own
+    # time (no host gaps).
     # The launches rotate over several input sets prepared by forwards of the
     # benchmark's own batches (decode: consecutive steps, so the expert
     # weights streamed change from launch to launch; prefill-like: the
@@ -307,12 +309,25 @@ def measure(torch, moe, workloads, name, steps, warmup, eager=False, reroute=Fal
         stage_fn["dispatch"] = lambda q: moe.moe_dispatch_reroute(
             cfg, q["ids"], q["order"], q["X"], b.expert_counts, b.expert_offsets, b.perm, b.inv_perm,
             None if gathers else Xp_ws, dws, dbytes)
+    # The K launches of a stage are captured in one HIP graph and replayed
+    # (eager launches with --eager): a stage of microsecond kernels (decode)
+    # would otherwise time the host's per-call overhead, not the kernels.
     stage_ms = {}
     nst = max(steps, nsets)
     for n in names:
         fn = stage_fn[n]
         fn(sets[0])  # untimed
-        stage_ms[n], _ = timed(lambda: [fn(sets[i % nsets]) for i in range(nst)], nst)
+        run_all = lambda: [fn(sets[i % nsets]) for i in range(nst)]  # noqa: E731
+        if eager:
+            stage_ms[n], _ = timed(run_all, nst)
+        else:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run_all()
+            g.replay()  # untimed replay
+            torch.cuda.synchronize()
+            stage_ms[n], _ = timed(g.replay, nst)
+            del g
 
     N = float(np.mean(per_step_N))
     active = float(np.mean(per_step_active))
