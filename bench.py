@@ -80,12 +80,13 @@ def gemm_kernel_name(w, capacity, stage, gathers):
     if w.dtype != "bf16":
         return f"grouped_gemm_kernel<float, 64, 64, 2, 2, {gelu}>"
     bound = w.T if capacity < 0 else min(w.T, capacity)
-    if K % 128 == 0 and N % 8 == 0 and bound <= 16:
+    few = bound <= 16 or (bound <= 64 and w.T * w.k <= 16 * w.E)  # at most 16 rows per expert on average
+    if K % 128 == 0 and N % 8 == 0 and few:
         g = 1 if bound <= 4 else 2 if bound <= 8 else 4
         return f"grouped_gemm_bf16_gemv<{gelu}, {g}, {'true' if gathers and stage == 'expert_up' else 'false'}>"
     if bound <= 64:
         return f"grouped_gemm_bf16_skinny<{gelu}, {1 if bound <= 16 else 2 if bound <= 32 else 4}>"
-    return f"grouped_gemm_bf16_256<{gelu}, {'true' if gathers and stage == 'expert_up' else 'false'}>"
+    return f"grouped_gemm_bf16_256<{gelu}, {'true' if gathers and stage == 'expert_up' else 'false'}, 8>"
 
 
 def parse():
