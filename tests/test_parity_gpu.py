@@ -1,6 +1,7 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle on small
 seeded cases that still span several tiles and ragged tails: each stage fed
 with the oracle's own intermediates, and the whole layer."""
+import dataclasses
 import math
 
 import numpy as np
@@ -690,6 +691,10 @@ def test_combine(case):
 @pytest.mark.parametrize("case", CASES, ids=IDS)
 def test_forward(case):
     inp, cfg = make(case)
+    _check_forward(inp, cfg)
+
+
+def _check_forward(inp, cfg):
     w = inp.workload
     out_ref, r, disp = oracle_all(inp)
     X, Wg = to_dev(inp.X, w.dtype), to_dev(inp.Wg, w.dtype)
@@ -718,6 +723,23 @@ def test_forward(case):
     layer.forward(X)
     torch.cuda.synchronize()
     assert torch.equal(first, layer.buf.out)
+
+
+@pytest.mark.parametrize("T,d,E,k,F,cap", [
+    (3000, 256, 8, 1, 384, -1),    # every pair in one expert: 12 m-tiles of it, 7 experts empty
+    (3000, 256, 8, 2, 384, -1),    # every token's first slot in one expert
+    (3000, 256, 8, 2, 384, 500),   # ... and cut to a capacity of 500
+    (40, 1024, 16, 2, 256, -1),    # decode-sized (K-split router, few-rows kernel): 40 rows in one expert
+], ids=["k1_all_one_expert", "k2_first_slot", "k2_capacity", "decode_sized"])
+def test_layer_every_token_to_one_expert(T, d, E, k, F, cap):
+    """A gate bias of +10 on expert 3 sends every token's first slot there:
+    one expert holds T rows and most of the others few or none.  The layer
+    matches the oracle (the capacity cut included) and is deterministic."""
+    inp = workloads.random_case(555 + T + k, T, d, E, k, F, "bf16", cap, 0.0, w_scale=0.05)
+    bias = np.zeros(E, dtype=np.float32)
+    bias[3] = 10.0
+    inp = dataclasses.replace(inp, bias=bias)
+    _check_forward(inp, moe.config(T, d, F, E, k, cap, "bf16"))
 
 
 @pytest.mark.parametrize("T,d,E,k,F", [(300, 128, 8, 2, 128), (8, 1024, 16, 2, 256)], ids=["tiles256", "decode"])
