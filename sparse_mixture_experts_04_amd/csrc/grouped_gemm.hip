@@ -736,10 +736,11 @@ hipError_t launch_big(const uint16_t* A, const uint16_t* B, uint16_t* C, const i
 
 // ---------------------------------------------------------------------------
 // Skinny variant for few rows per expert where the decode variant below does
-// not run (K not a multiple of 128 or N not of 8): the layer is bound by
-// streaming each active expert's weights once.  A
-// one-wave block owns 16 weight rows (one 16-row MFMA A tile) over the whole
-// K and up to 64 of the expert's token rows (up to four 16-column B tiles),
+// not run (K not a multiple of 128 or N not of 8, or up to 64 rows per expert
+// on a batch averaging more than 16): the layer is bound by streaming each
+// active expert's weights once.  A one-wave block owns 16 weight rows (one
+// 16-row MFMA A tile) over the whole K and up to 64 of the expert's token
+// rows (up to four 16-column B tiles),
 // so every weight byte is loaded exactly once, with 8 k-steps of loads in
 // flight per lane.  Small blocks keep the per-CU work even when the number of
 // (expert, row tile) pairs is not a multiple of the CU count.  The result tile

@@ -82,3 +82,13 @@ def test_fractions_of_the_measured_peaks():
     assert mfma["frac_of_achievable"] == pytest.approx(1000.0 / 1200.0, abs=1e-4)
     assert hbm["frac_of_achievable"] == pytest.approx(1.2)
     assert "frac_of_achievable" not in f32  # the fp32 layer has no measured fp32 reference
+
+
+def test_gemm_code_hash_ignores_comments(tmp_path):
+    a = tmp_path / "a.hip"
+    b = tmp_path / "b.hip"
+    c = tmp_path / "c.hip"
+    a.write_text("int f(int x) {\n  return x + 1;  // one\n}\n")
+    b.write_text("// a comment line\nint f(int x) {\n\n  return x + 1;   // another comment\n}\n")
+    c.write_text("int f(int x) {\n  return x + 2;\n}\n")
+    assert bench.gemm_code_sha1(a) == bench.gemm_code_sha1(b) != bench.gemm_code_sha1(c)
